@@ -1,0 +1,398 @@
+/*
+ * oracle.c - plain CPU oracle of the NVFP4 SwiGLU producer and block-scaled GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path calls, links or loads
+ * this file; only the tests, the package's smoke check and the benchmark's CPU
+ * baseline do. It shares no code, header, table or constant generator with the
+ * HIP library.
+ *
+ * What it computes (the pages: "FC2 NVFP4 Scheduling Results", section
+ * "Canonical Operation": E2M1 data with vector-16 UE4M3 block scales, FP32
+ * scalars and accumulation, BF16 output, rows padded 37,810 -> 37,824; the
+ * component-2 NSYS summary, keys "swiglu_silu_total_ms" /
+ * "swiglu_multiply_total_ms" for the silu-then-multiply chain, and
+ * "native_pack_validation.fix" for the 128-row by 4-scale-column tiled scale
+ * offset). The pages print no formula; where they are silent the readings
+ * below are the plainest ones consistent with them:
+ *
+ *   O1 silu_bf16(x)   correctly rounded bf16 of x / (1 + e^-x)
+ *   O2 y              RN_bf16(silu_bf16(gate) * up) - one rounding of the
+ *                     exact product; plain quantization takes y = x
+ *   O3 amax           max |y| over the logical rows
+ *   O4 g              amax / 2688 rounded toward +inf to fp32 (2688 = 6 * 448)
+ *   O5 S[r,b]         smallest UE4M3 byte e with v(e) * 6 * g >= max_{16} |y|
+ *   O6 code           nearest E2M1 magnitude of |y| / (v(S) g), ties to the
+ *                     even code, sign bit kept (also on zero)
+ *   O7 pack           byte j of a row = code[2j] | code[2j+1] << 4; padding
+ *                     rows [m, m_pad) are zero
+ *   O8 swizzle        off(r,c) = ((r>>7)*(C'/4) + (c>>2))*512 + (r&31)*16
+ *                                + ((r>>5)&3)*4 + (c&3); uncovered bytes zero
+ *   O10 GEMM          RN_bf16(g_a g_w sum_b v(SA) v(SW) sum_k e2m1 e2m1),
+ *                     evaluated exactly in integers
+ *
+ * Pins (tests/test_oracle_*.py): O1 against 50-digit decimal arithmetic for
+ * all 65,536 inputs; O2 against torch's CPU bf16 multiply; O4-O6 against exact
+ * rationals; O7 by an independent unpacker; O10 against fp64
+ * dequantize-then-matmul and one-hot / all-ones reductions. O8: the tile
+ * structure (each 128-row x 4-column tile is one contiguous 512-byte run, tiles
+ * row-tile-major) and bijectivity are pinned; the order inside a tile is a
+ * reading the pages do not fix - parity unpinned for that order.
+ *
+ * All floating-point decisions are taken exactly: every product compared below
+ * has at most 31 significant bits and is exact in double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL -1
+#define OR_ENOMEM -2
+#define OR_ENONFINITE -3
+
+/* ---------- bf16 helpers ---------------------------------------------------- */
+
+static double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static int bf16_is_finite(uint16_t b) { return (b & 0x7F80u) != 0x7F80u; }
+
+/*
+ * Round hi + lo to the nearest bf16, ties to even, where t = hi + lo is the
+ * long-double sum and err its exact rounding error (TwoSum). When t itself sits
+ * exactly on a bf16 rounding boundary, err decides the side.
+ */
+static uint16_t rn_bf16_pair(long double hi, long double lo) {
+  long double t = (lo == 0.0L) ? hi : hi + lo; /* keep the sign of a zero hi */
+  long double bb = t - hi;
+  long double err = (hi - (t - bb)) + (lo - bb); /* TwoSum: hi + lo == t + err exactly */
+  if (t == 0.0L) return signbit(t) ? 0x8000u : 0x0000u;
+  uint16_t sign = signbit(t) ? 0x8000u : 0u;
+  long double a = fabsl(t);
+  long double e_dir = signbit(t) ? -err : err; /* err measured along |t| */
+  int e;
+  frexpl(a, &e);           /* a = f * 2^e, f in [0.5, 1): leading bit at 2^(e-1) */
+  int lead = e - 1;
+  if (lead < -126) lead = -126; /* bf16 subnormal quantum is 2^-133 */
+  long double q = ldexpl(1.0L, lead - 7);
+  long double r = a / q; /* exact: division by a power of two */
+  long double fl = floorl(r);
+  long double fr = r - fl;
+  long double n;
+  if (fr > 0.5L) n = fl + 1.0L;
+  else if (fr < 0.5L) n = fl;
+  else if (e_dir > 0.0L) n = fl + 1.0L;
+  else if (e_dir < 0.0L) n = fl;
+  else n = (fmodl(fl, 2.0L) == 0.0L) ? fl : fl + 1.0L;
+  long double rr = n * q;
+  if (rr >= 0x1p128L) return sign | 0x7F80u;
+  float f = (float)rr; /* exact: rr has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return sign | (uint16_t)(u >> 16);
+}
+
+static uint16_t rn_bf16_ld(long double v) { return rn_bf16_pair(v, 0.0L); }
+
+uint16_t oracle_rn_bf16(double v) { return rn_bf16_ld((long double)v); }
+
+/*
+ * O1: silu correctly rounded to bf16. For |x| < 1/16 the value is formed as
+ * x/2 + (x/2) tanh(x/2) (the same function, since x sigma(x) = x/2 (1 + tanh(x/2))):
+ * x/2 is exact and may itself be a bf16 rounding boundary when x is tiny, and the
+ * small second term then decides the rounding, so it must not be absorbed.
+ */
+uint16_t oracle_silu_bf16(uint16_t xb) {
+  long double x = (long double)bf16_to_double(xb);
+  if (x == 0.0L) return xb; /* silu(+-0) = +-0 */
+  if (fabsl(x) < 0.0625L) {
+    long double h = x * 0.5L;
+    return rn_bf16_pair(h, h * tanhl(h));
+  }
+  return rn_bf16_ld(x / (1.0L + expl(-x)));
+}
+
+void oracle_silu_table(uint16_t* tab) {
+  for (uint32_t i = 0; i < 65536u; ++i) tab[i] = oracle_silu_bf16((uint16_t)i);
+}
+
+/* O2 */
+uint16_t oracle_swiglu_bf16(uint16_t gate, uint16_t up, const uint16_t* silu_tab) {
+  uint16_t s = silu_tab ? silu_tab[gate] : oracle_silu_bf16(gate);
+  double p = bf16_to_double(s) * bf16_to_double(up); /* exact: 8 x 8 significant bits */
+  return oracle_rn_bf16(p);
+}
+
+/* ---------- UE4M3 / E2M1 ---------------------------------------------------- */
+
+/* UE4M3 byte -> value: E = b>>3, m = b&7; E == 0: m * 2^-9, else (1 + m/8) * 2^(E-7). */
+double oracle_ue4m3_value(uint8_t b) {
+  int E = b >> 3, m = b & 7;
+  if (E == 0) return ldexp((double)m, -9);
+  return ldexp(1.0 + m / 8.0, E - 7);
+}
+
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double oracle_e2m1_value(uint8_t code) {
+  double v = E2M1_MAG[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+/* O4: the smallest fp32 g with 2688 * g >= amax (products with 2688 = 21 * 2^7
+ * are exact in double). */
+float oracle_global_scale(double amax) {
+  if (!(amax > 0.0)) return 0.0f;
+  float g = (float)(amax / 2688.0);
+  while ((double)g * 2688.0 < amax) g = nextafterf(g, INFINITY);
+  for (;;) {
+    float p = nextafterf(g, 0.0f);
+    if (p > 0.0f && (double)p * 2688.0 >= amax) g = p;
+    else break;
+  }
+  return g;
+}
+
+/* O5: smallest UE4M3 byte e in [0, 126] with v(e) * 6 * g >= bmax (exact). */
+uint8_t oracle_block_scale(double bmax, float g) {
+  for (int e = 0; e <= 126; ++e) {
+    if (oracle_ue4m3_value((uint8_t)e) * 6.0 * (double)g >= bmax) return (uint8_t)e;
+  }
+  return 0xFF; /* unreachable when g comes from O4 */
+}
+
+/* O6: E2M1 code of y in a block with scale byte s and global scale g. */
+uint8_t oracle_e2m1_code(double y, uint8_t s, float g) {
+  uint8_t sign = signbit(y) ? 8u : 0u;
+  if (s == 0) return sign;
+  double a = fabs(y);
+  double unit = oracle_ue4m3_value(s) * (double)g; /* exact */
+  int idx = 0;
+  for (int j = 0; j < 7; ++j) {
+    double mid = (E2M1_MAG[j] + E2M1_MAG[j + 1]) * 0.5 * unit; /* exact */
+    int up_is_even = ((j + 1) % 2) == 0;
+    if (a > mid || (a == mid && up_is_even)) idx = j + 1;
+    else break;
+  }
+  return sign | (uint8_t)idx;
+}
+
+/* ---------- layout ----------------------------------------------------------- */
+
+int64_t oracle_padded_rows(int64_t rows) { return (rows + 15) / 16 * 16; }
+int64_t oracle_scale_rows(int64_t rows) { return (oracle_padded_rows(rows) + 127) / 128 * 128; }
+int64_t oracle_scale_cols(int64_t k) { return ((k / 16) + 3) / 4 * 4; }
+
+/* O8 */
+int64_t oracle_scale_offset(int64_t r, int64_t c, int64_t cpad) {
+  return ((r >> 7) * (cpad / 4) + (c >> 2)) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (c & 3);
+}
+
+/* ---------- producer --------------------------------------------------------- */
+
+/*
+ * Quantize y = swiglu(gate, up) (up != NULL) or y = x (up == NULL) of logical
+ * shape [m, k] (row strides ldx, ldu in elements) into
+ *   qdata  [m_pad, k/2] bytes, m_pad = roundup(m, 16)
+ *   scales [roundup(m_pad,128) * roundup(k/16,4)] bytes, swizzled (O8)
+ *   *g_out the fp32 global scale
+ * y_out (optional, [m, k] bf16 bits) receives y for inspection.
+ */
+int oracle_quantize(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t ldu, int64_t m,
+                    int64_t k, uint8_t* qdata, uint8_t* scales, float* g_out, uint16_t* y_out,
+                    int nthreads) {
+  if (!x || !qdata || !scales || !g_out || m < 0 || k <= 0 || k % 16 != 0 || ldx < k ||
+      (up && ldu < k))
+    return OR_EINVAL;
+  if (nthreads <= 0) nthreads = 1;
+  const int64_t m_pad = oracle_padded_rows(m);
+  const int64_t nb = k / 16;
+  const int64_t cpad = oracle_scale_cols(k);
+  const int64_t rpad = oracle_scale_rows(m);
+
+  uint16_t* y = (uint16_t*)malloc((size_t)(m > 0 ? m : 1) * (size_t)k * sizeof(uint16_t));
+  uint16_t* tab = (uint16_t*)malloc(65536 * sizeof(uint16_t));
+  if (!y || !tab) {
+    free(y);
+    free(tab);
+    return OR_ENOMEM;
+  }
+  if (up) oracle_silu_table(tab);
+
+  /* O1-O2 */
+  int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(| : bad)
+  for (int64_t r = 0; r < m; ++r) {
+    for (int64_t c = 0; c < k; ++c) {
+      uint16_t xv = x[r * ldx + c];
+      uint16_t yv;
+      if (up) {
+        uint16_t uv = up[r * ldu + c];
+        if (!bf16_is_finite(xv) || !bf16_is_finite(uv)) bad = 1;
+        yv = oracle_swiglu_bf16(xv, uv, tab);
+      } else {
+        yv = xv;
+      }
+      if (!bf16_is_finite(yv)) bad = 1;
+      y[r * k + c] = yv;
+    }
+  }
+  free(tab);
+  if (bad) {
+    free(y);
+    return OR_ENONFINITE;
+  }
+
+  /* O3 */
+  double amax = 0.0;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(max : amax)
+  for (int64_t i = 0; i < m * k; ++i) {
+    double a = fabs(bf16_to_double(y[i]));
+    if (a > amax) amax = a;
+  }
+  /* O4 */
+  const float g = oracle_global_scale(amax);
+
+  /* O5-O8 */
+  memset(scales, 0, (size_t)(rpad * cpad));
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+  for (int64_t r = 0; r < m_pad; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      double yv[16];
+      double bmax = 0.0;
+      for (int t = 0; t < 16; ++t) {
+        yv[t] = (r < m) ? bf16_to_double(y[r * k + b * 16 + t]) : 0.0;
+        if (fabs(yv[t]) > bmax) bmax = fabs(yv[t]);
+      }
+      uint8_t s = oracle_block_scale(bmax, g);
+      scales[oracle_scale_offset(r, b, cpad)] = s;
+      for (int t = 0; t < 16; t += 2) {
+        uint8_t lo = oracle_e2m1_code(yv[t], s, g);
+        uint8_t hi = oracle_e2m1_code(yv[t + 1], s, g);
+        qdata[r * (k / 2) + (b * 16 + t) / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+  if (y_out) memcpy(y_out, y, (size_t)m * (size_t)k * sizeof(uint16_t));
+  free(y);
+  *g_out = g;
+  return OR_OK;
+}
+
+/* ---------- GEMM ------------------------------------------------------------- */
+
+/* 2 * e2m1 value: an integer in [-12, 12] */
+static int q2_of_code(uint8_t code) {
+  static const int MAG2[8] = {0, 1, 2, 3, 4, 6, 8, 12};
+  int v = MAG2[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+/* 2^9 * v(s): an integer in [0, 229376] */
+static int64_t s9_of_byte(uint8_t b) {
+  int E = b >> 3, m = b & 7;
+  if (E == 0) return m;
+  return (int64_t)(8 + m) << (E - 1);
+}
+
+/* Round sign * P * 2^E (exact, P < 2^127) to the nearest bf16, ties to even. */
+static uint16_t rn_bf16_exact(int negative, unsigned __int128 P, int E) {
+  if (P == 0) return 0x0000u; /* an exact zero sum is +0 */
+  int L = 0;
+  for (unsigned __int128 t = P; t; t >>= 1) ++L;
+  int lead = L - 1 + E;
+  int shift = (lead >= -126) ? (L - 8) : (-133 - E);
+  unsigned __int128 q;
+  if (shift > 0) {
+    q = P >> shift;
+    unsigned __int128 rem = P - (q << shift);
+    unsigned __int128 half = (unsigned __int128)1 << (shift - 1);
+    if (rem > half || (rem == half && (q & 1))) q += 1;
+  } else {
+    q = P << (-shift);
+  }
+  double mag = ldexp((double)(uint64_t)q, E + shift); /* q <= 256: exact */
+  uint16_t sign = negative ? 0x8000u : 0u;
+  if (mag >= 0x1p128) return sign | 0x7F80u;
+  float f = (float)mag;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return sign | (uint16_t)(u >> 16);
+}
+
+/*
+ * D[i, j] for i < nrows (activation row rows[i]) and j < n:
+ *   RN_bf16(g_a g_w sum_b v(SA[rows[i],b]) v(SW[j,b]) sum_{k in b} e2m1(A) e2m1(W))
+ * computed exactly. a_rows_total / w_rows_total are the logical row counts the
+ * scale buffers were sized for (their padded forms give the swizzle geometry).
+ */
+int oracle_gemm_rows(const uint8_t* aq, const uint8_t* as, int64_t a_rows_total, float ga,
+                     const uint8_t* wq, const uint8_t* ws, int64_t n, float gw, int64_t k,
+                     const int64_t* rows, int64_t nrows, uint16_t* out, int nthreads) {
+  if (!aq || !as || !wq || !ws || !rows || !out || n <= 0 || k <= 0 || k % 16 != 0 ||
+      !(ga >= 0.0f) || !(gw >= 0.0f))
+    return OR_EINVAL;
+  if (nthreads <= 0) nthreads = 1;
+  const int64_t nb = k / 16, cpad = oracle_scale_cols(k), kb = k / 2;
+  const int64_t a_pad = oracle_padded_rows(a_rows_total);
+  for (int64_t i = 0; i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= a_pad) return OR_EINVAL;
+
+  int8_t* A = (int8_t*)malloc((size_t)(nrows ? nrows : 1) * (size_t)k);
+  int8_t* W = (int8_t*)malloc((size_t)n * (size_t)k);
+  int64_t* SA = (int64_t*)malloc((size_t)(nrows ? nrows : 1) * (size_t)nb * sizeof(int64_t));
+  int64_t* SW = (int64_t*)malloc((size_t)n * (size_t)nb * sizeof(int64_t));
+  if (!A || !W || !SA || !SW) {
+    free(A); free(W); free(SA); free(SW);
+    return OR_ENOMEM;
+  }
+  for (int64_t i = 0; i < nrows; ++i) {
+    int64_t r = rows[i];
+    for (int64_t c = 0; c < k; ++c) {
+      uint8_t byte = aq[r * kb + c / 2];
+      A[i * k + c] = (int8_t)q2_of_code((c & 1) ? (byte >> 4) : (byte & 15));
+    }
+    for (int64_t b = 0; b < nb; ++b) SA[i * nb + b] = s9_of_byte(as[oracle_scale_offset(r, b, cpad)]);
+  }
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+  for (int64_t j = 0; j < n; ++j) {
+    for (int64_t c = 0; c < k; ++c) {
+      uint8_t byte = wq[j * kb + c / 2];
+      W[j * k + c] = (int8_t)q2_of_code((c & 1) ? (byte >> 4) : (byte & 15));
+    }
+    for (int64_t b = 0; b < nb; ++b) SW[j * nb + b] = s9_of_byte(ws[oracle_scale_offset(j, b, cpad)]);
+  }
+
+  /* g_a = Ga * 2^ea, g_w = Gw * 2^ew with integer mantissas */
+  int ea, ew;
+  float fa = frexpf(ga, &ea), fw = frexpf(gw, &ew);
+  uint64_t Ga = (uint64_t)ldexp((double)fa, 24), Gw = (uint64_t)ldexp((double)fw, 24);
+  const int Ebase = (ea - 24) + (ew - 24) - 20; /* 2^-20: (1/2)^2 from q2, (2^-9)^2 from s9 */
+
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int8_t* a = A + i * k;
+    const int64_t* sa = SA + i * nb;
+    for (int64_t j = 0; j < n; ++j) {
+      const int8_t* w = W + j * k;
+      const int64_t* sw = SW + j * nb;
+      int64_t total = 0;
+      for (int64_t b = 0; b < nb; ++b) {
+        int32_t dot = 0;
+        for (int t = 0; t < 16; ++t) dot += (int32_t)a[b * 16 + t] * (int32_t)w[b * 16 + t];
+        total += (int64_t)dot * (sa[b] * sw[b]);
+      }
+      int neg = total < 0;
+      unsigned __int128 P = (unsigned __int128)(neg ? -total : total);
+      P *= (unsigned __int128)Ga * Gw;
+      out[i * n + j] = rn_bf16_exact(neg, P, Ebase);
+    }
+  }
+  free(A); free(W); free(SA); free(SW);
+  return OR_OK;
+}

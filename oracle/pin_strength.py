@@ -1,0 +1,50 @@
+"""Pin-strength check for the CPU oracle (test infrastructure; run by hand, not by pytest).
+
+Plants one plausible mistake at a time into a copy of oracle.c (a sign, a tie rule,
+a rounding direction, a nibble or swizzle order, a dropped scale, a transposed
+operand, ...), builds it, and runs the oracle pin tests against that build through
+NVFP4_ORACLE_LIB. Every planted mistake that changes a result must make a pin fail.
+
+    python oracle/pin_strength.py [mutation ...]
+"""
+import os, subprocess, sys, tempfile, re
+ROOT=os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+src=open(os.path.join(ROOT, 'oracle', 'oracle.c')).read()
+M = {
+ 'silu_sign': ('x / (1.0L + expl(-x))', 'x / (1.0L + expl(x))'),
+ 'silu_tiny_split_lost': ('return rn_bf16_pair(h, h * tanhl(h));', 'return rn_bf16_ld(x / (1.0L + expl(-x)));'),
+ 'ties_odd': ('int up_is_even = ((j + 1) % 2) == 0;', 'int up_is_even = ((j + 1) % 2) == 1;'),
+ 'ties_up': ('if (a > mid || (a == mid && up_is_even)) idx = j + 1;', 'if (a >= mid) idx = j + 1;'),
+ 'gscale_rn': ('while ((double)g * 2688.0 < amax) g = nextafterf(g, INFINITY);', ''),
+ 'bscale_strict': ('* 6.0 * (double)g >= bmax) return', '* 6.0 * (double)g > bmax) return'),
+ 'bscale_from1': ('for (int e = 0; e <= 126; ++e)', 'for (int e = 1; e <= 126; ++e)'),
+ 'nibble_swap': ('(uint8_t)(lo | (hi << 4))', '(uint8_t)(hi | (lo << 4))'),
+ 'swizzle_swap': ('(r & 31) * 16 + ((r >> 5) & 3) * 4', '(r & 31) * 4 + ((r >> 5) & 3) * 16'),
+ 'ue4m3_sub': ('if (E == 0) return ldexp((double)m, -9);', 'if (E == 0) return ldexp((double)m, -10);'),
+ 'amax_noabs': ('double a = fabs(bf16_to_double(y[i]));', 'double a = bf16_to_double(y[i]);'),
+ 'y_trunc': ('double p = bf16_to_double(s) * bf16_to_double(up); /* exact: 8 x 8 significant bits */\n  return oracle_rn_bf16(p);',
+             'double p = bf16_to_double(s) * bf16_to_double(up);\n  float pf=(float)p; uint32_t uu; memcpy(&uu,&pf,4); return (uint16_t)(uu>>16);'),
+ 'code_nosign_zero': ('uint8_t sign = signbit(y) ? 8u : 0u;\n  if (s == 0) return sign;', 'uint8_t sign = signbit(y) ? 8u : 0u;\n  if (s == 0) return 0;'),
+ 'gemm_drop_sw': ('total += (int64_t)dot * (sa[b] * sw[b]);', 'total += (int64_t)dot * (sa[b]);'),
+ 'gemm_transpose': ('const int8_t* w = W + j * k;', 'const int8_t* w = W + ((j * 7) % n) * k;'),
+ 'gemm_trunc': ('if (rem > half || (rem == half && (q & 1))) q += 1;', ''),
+ 'gemm_ties_away': ('if (rem > half || (rem == half && (q & 1))) q += 1;', 'if (rem >= half) q += 1;'),
+ 'gemm_scale_wrong_block': ('total += (int64_t)dot * (sa[b] * sw[b]);', 'total += (int64_t)dot * (sa[b] * sw[(b+1)%nb]);'),
+ 'gemm_code_table': ('static const int MAG2[8] = {0, 1, 2, 3, 4, 6, 8, 12};', 'static const int MAG2[8] = {0, 1, 2, 3, 4, 5, 8, 12};'),
+ 'gemm_nibble': ('A[i * k + c] = (int8_t)q2_of_code((c & 1) ? (byte >> 4) : (byte & 15));', 'A[i * k + c] = (int8_t)q2_of_code((c & 1) ? (byte & 15) : (byte >> 4));'),
+}
+tmpd=tempfile.mkdtemp()
+res={}
+only=sys.argv[1:] 
+for name,(a,b) in M.items():
+    if only and name not in only: continue
+    assert src.count(a)>=1, name
+    msrc=src.replace(a,b)
+    cpath=os.path.join(tmpd,name+'.c'); lib=os.path.join(tmpd,name+'.so')
+    open(cpath,'w').write(msrc)
+    subprocess.run(['gcc','-O2','-fopenmp','-fPIC','-shared','-std=gnu11',cpath,'-o',lib,'-lm'],check=True)
+    env=dict(os.environ, NVFP4_ORACLE_LIB=lib)
+    r=subprocess.run([sys.executable,'-m','pytest','-x','-q','tests/test_oracle_silu.py','tests/test_oracle_quant.py','tests/test_oracle_layout.py','tests/test_oracle_gemm.py','-k','not exhaustive_against_decimal or silu'],cwd=ROOT,env=env,capture_output=True,text=True,timeout=900)
+    caught = r.returncode!=0
+    last=[l for l in r.stdout.splitlines() if 'FAILED' in l or 'passed' in l or 'failed' in l]
+    print(f'{name:25s} caught={caught} {last[:1]}',flush=True)

@@ -1,0 +1,227 @@
+"""Benchmark of the NVFP4 FC2 hot path on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input: the fused SwiGLU ->
+NVFP4 producer on gate/up [M, K] followed by the block-scaled GEMM against the
+pre-quantized weight (weights are quantized once, as in inference; that launch is
+timed separately and reported, not inside the step). Inputs are resident in HBM
+before the timed region. Per-kernel durations come from HIP events recorded on
+the stream the kernels run on (torch's current stream, which the binding passes to
+the C ABI).
+
+Prints one JSON line. `value` is the FC2 GEMM throughput, 2 * M * N * K / t_gemm with
+the logical M = 37,810 (the pages count FC2 TFLOP/s this way: 5.828e12 FLOP at
+15.636 ms = 372.74 TFLOP/s, "FC2 NVFP4 Scheduling Results", "Timing").
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fc2_canonical]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FC2 NVFP4 GEMM TFLOP/s (% BF16 MFMA peak) + producer GB/s @M=37810"
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
+
+
+def producer_bytes(m: int, k: int, swiglu: bool) -> int:
+    """Algorithmic HBM bytes of the two-pass producer: inputs read twice (absmax pass,
+    pack pass), QDATA and the 128-row-padded scale buffer written once."""
+    m_pad = (m + 15) // 16 * 16
+    s_rows = (m_pad + 127) // 128 * 128
+    n_in = 2 if swiglu else 1
+    return 2 * n_in * m * k * 2 + m_pad * k // 2 + s_rows * (k // 16)
+
+
+def gemm_bytes(m: int, n: int, k: int) -> int:
+    """Distinct data of the GEMM: packed A and W with their scales, the padded bf16 output."""
+    m_pad = (m + 15) // 16 * 16
+    a = m_pad * k // 2 + (m_pad + 127) // 128 * 128 * (k // 16)
+    w = n * k // 2 + (n + 127) // 128 * 128 * (k // 16)
+    return a + w + m_pad * n * 2
+
+
+def cpu_baseline(w, threads: int) -> dict:
+    """The CPU oracle timed on a bounded sample of the same workload: the exact GEMM on
+    sampled rows (all N columns, full K), scaled to TFLOP/s. The oracle is an
+    exact-arithmetic correctness reference, not a tuned CPU GEMM."""
+    import numpy as np
+    import oracle
+    import synth
+    rows = 1024
+    acts = w.activations(rows=rows, threads=threads)
+    aq, as_, ga = oracle.quantize(acts[0], acts[1] if w.swiglu else None, threads=threads)
+    W = w.weight(threads=threads)
+    wq, ws, gw = oracle.quantize(W, threads=threads)
+    t0 = time.perf_counter()
+    oracle.gemm_rows(aq, as_, rows, ga, wq, ws, w.n, gw, w.k, np.arange(rows), threads=threads)
+    t_gemm = time.perf_counter() - t0
+    prod_rows = 4096
+    acts = w.activations(rows=prod_rows, threads=threads)
+    t0 = time.perf_counter()
+    oracle.quantize(acts[0], acts[1] if w.swiglu else None, threads=threads)
+    t_prod = time.perf_counter() - t0
+    return {
+        "value": 2.0 * rows * w.n * w.k / t_gemm / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"exact int64 GEMM of {rows} sampled rows x {w.n} x {w.k} ({t_gemm:.2f} s); producer "
+                  f"over {prod_rows} rows x {w.k}: {producer_bytes(prod_rows, w.k, w.swiglu) / t_prod / 1e9:.3f} "
+                  f"GB/s ({t_prod:.2f} s)",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="fc2_canonical")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path is single-GPU; see DESIGN.md for how it "
+              f"would shard); got --gpus {args.gpus}", file=sys.stderr)
+        return 2
+
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    import synth
+    from tests import parity
+
+    w = synth.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nv.nvfp4_init()
+
+    t0 = time.perf_counter()
+    acts = w.activations()
+    W = w.weight()
+    x = parity.to_device_bf16(acts[0], dev)
+    u = parity.to_device_bf16(acts[1], dev) if w.swiglu else None
+    wt = parity.to_device_bf16(W, dev)
+    del acts, W
+    a = nv.empty_nvfp4(w.m, w.k, dev)
+    wq = nv.empty_nvfp4(w.n, w.k, dev)
+    d = torch.empty((w.m_pad, w.n), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+
+    stream = torch.cuda.current_stream()
+
+    # weight quantization: once, outside the step
+    ev_w0, ev_w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev_w0.record(stream)
+    nv.nvfp4_quantize(wt, out=wq)
+    ev_w1.record(stream)
+
+    def step():
+        if w.swiglu:
+            nv.nvfp4_quantize_swiglu(x, u, out=a)
+        else:
+            nv.nvfp4_quantize(x, out=a)
+        nv.nvfp4_gemm_bf16out(a, wq, out=d)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        if w.swiglu:
+            nv.nvfp4_quantize_swiglu(x, u, out=a)
+        else:
+            nv.nvfp4_quantize(x, out=a)
+        evs[i][1].record(stream)
+        nv.nvfp4_gemm_bf16out(a, wq, out=d)
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    prod_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    gemm_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    import statistics
+    t_prod = statistics.fmean(prod_ms)
+    t_gemm = statistics.fmean(gemm_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    tflops = w.gemm_flops / (t_gemm * 1e-3) / 1e12
+    pbytes = producer_bytes(w.m, w.k, w.swiglu)
+    prod_gbs = pbytes / (t_prod * 1e-3) / 1e9
+    finite = bool(torch.isfinite(d[: w.m].float()).all().item())
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: SwiGLU->NVFP4 producer + NVFP4 GEMM, M={w.m} (padded {w.m_pad}), "
+                        f"N={w.n}, K={w.k}, seed {w.seed}" if w.swiglu else
+                        f"{w.name}: NVFP4 quantize + NVFP4 GEMM, M={w.m}, N={w.n}, K={w.k}, seed {w.seed}",
+            "m": w.m, "m_padded": w.m_pad, "n": w.n, "k": w.k, "seed": w.seed,
+            "outlier_channels": w.n_outliers,
+            "operands": "E2M1 + vector-16 UE4M3 scales + fp32 global scale, dequantized exactly to fp16 "
+                        "for fp16 MFMA, fp32 accumulation, bf16 output",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "nvfp4::gemm_kernel",
+            "algorithmic_per_launch": f"{w.gemm_flops:.4e} FLOP (2*M*N*K, logical M)",
+            "avg_launch_ms": round(t_gemm, 4),
+        },
+        "roofline_producer": {
+            "bound": "hbm",
+            "achieved": round(prod_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(prod_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "nvfp4::producer_kernel<true>" if w.swiglu else "nvfp4::producer_kernel<false>",
+            "algorithmic_per_launch": f"{pbytes} B (inputs read twice, QDATA + padded scales written)",
+            "avg_launch_ms": round(t_prod, 4),
+        },
+        "producer_ms": round(t_prod, 4),
+        "gemm_ms": round(t_gemm, 4),
+        "step_tflops": round(w.gemm_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "weight_quantize_ms": round(ev_w0.elapsed_time(ev_w1), 4),
+        "gemm_distinct_bytes": gemm_bytes(w.m, w.n, w.k),
+        "output_finite": finite,
+        "setup_s": round(setup_s, 1),
+        "device": torch.cuda.get_device_name(dev),
+        "build": nv.nvfp4_build_info(),
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        try:
+            line["cpu_baseline"] = cpu_baseline(w, threads)
+        except Exception as e:  # the baseline is a report, not the product
+            line["cpu_baseline"] = {"error": repr(e)}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

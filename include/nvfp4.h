@@ -1,0 +1,171 @@
+/*
+ * nvfp4.h - C ABI of the MI355X (gfx950) NVFP4 SwiGLU producer and block-scaled GEMM.
+ *
+ * The library implements the NVFP4 MLP projection described on the pages
+ * "FC2 NVFP4 Scheduling Results" (section "Canonical Operation": E2M1 operands
+ * with vector-16 UE4M3 block scales, FP32 global scales and accumulation, BF16
+ * output; logical M = 37,810 padded to 37,824 rows, N = 5,376, K = 14,336) and
+ * "gb10-component2-nsys-summary" (the fused SwiGLU producer replacing separate
+ * silu, multiply, absmax, finalize, zero-fill and pack kernels; the 128-row by
+ * 4-scale-column tiled block-scale layout).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_dev are device pointers on the current HIP device; the
+ *    caller owns all memory. The library allocates nothing and keeps no
+ *    reference after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). All
+ *    work is enqueued on it asynchronously; no call synchronises with the host
+ *    except nvfp4_init (and the first call on a device, which runs it).
+ *  - Arguments are validated before anything is enqueued. On any error the call
+ *    returns a non-zero nvfp4_status, enqueues nothing and writes nothing;
+ *    nvfp4_last_error() then describes the failure (per host thread).
+ *  - Integer sizes are element counts unless named *_bytes.
+ *
+ * Data formats (shared by producer output and GEMM input):
+ *  - QDATA: E2M1 codes, bit 3 = sign, bits 2..0 = magnitude index into
+ *    {0, 0.5, 1, 1.5, 2, 3, 4, 6}; two codes per byte, the even (first) element
+ *    in the low nibble. Row-major [padded_rows, k/2] bytes, rows padded to a
+ *    multiple of 16 with zero bytes.
+ *  - Block scales: one UE4M3 byte per 16 consecutive elements of a row
+ *    (value (1 + m/8) * 2^(E-7), or m * 2^-9 when E == 0; never above 0x7E),
+ *    stored in 512-byte tiles of 128 rows x 4 scale columns: byte (r, c) sits at
+ *      ((r >> 7) * (C / 4) + (c >> 2)) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (c & 3)
+ *    with C = roundup(k/16, 4); the buffer holds roundup(padded_rows, 128) * C
+ *    bytes and every byte outside real rows/columns is zero.
+ *  - Global scale: one FP32 on the device; element value = e2m1 * v(S) * g.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARG = 1,       /* null pointer, negative size, bad stride */
+  NVFP4_ERR_UNSUPPORTED_SHAPE = 2, /* k % 64 != 0, n % 16 != 0, m_padded % 16 != 0, too large */
+  NVFP4_ERR_MISALIGNED = 3,        /* a pointer or row stride breaks the 16-byte alignment rule */
+  NVFP4_ERR_WORKSPACE = 4,         /* workspace pointer missing */
+  NVFP4_ERR_NO_DEVICE = 5,         /* no HIP device, or the current device is not gfx950 */
+  NVFP4_ERR_LAUNCH = 6             /* the HIP runtime refused the launch (see nvfp4_last_error) */
+} nvfp4_status;
+
+/* ---- sizes (pure functions; no device access) ------------------------------------- */
+
+/* Rows after the producer's padding: roundup(rows, 16). 37,810 -> 37,824
+ * ("FC2 NVFP4 Scheduling Results", "Canonical Operation"). Returns -1 if rows < 0. */
+int64_t nvfp4_padded_rows(int64_t rows);
+
+/* Rows of the block-scale buffer: roundup(nvfp4_padded_rows(rows), 128). The
+ * component-2 summary's intermediate byte count (key
+ * intermediate_materialization_bytes_across_four_projections) decomposes exactly
+ * with scale buffers padded this way. */
+int64_t nvfp4_scale_rows(int64_t rows);
+
+/* Scale columns: roundup(k / 16, 4). */
+int64_t nvfp4_scale_cols(int64_t k);
+
+/* QDATA bytes: nvfp4_padded_rows(rows) * k / 2. */
+int64_t nvfp4_qdata_bytes(int64_t rows, int64_t k);
+
+/* Block-scale buffer bytes: nvfp4_scale_rows(rows) * nvfp4_scale_cols(k). */
+int64_t nvfp4_scale_bytes(int64_t rows, int64_t k);
+
+/* Bytes of the producer workspace (the absmax slot and grid-barrier counters).
+ * The caller allocates it on the device, zero-fills it once before the first
+ * call, and never touches it afterwards: every producer call leaves it zeroed
+ * again when it completes. Calls that may overlap in time (different streams)
+ * need distinct workspaces. */
+int64_t nvfp4_quantize_workspace_bytes(void);
+
+/* ---- set-up -------------------------------------------------------------------------- */
+
+/* One-time set-up of the current device: checks that it is gfx950, builds the
+ * producer's correctly rounded bf16 silu table in device memory and sizes the
+ * producer's persistent grid. Synchronous; safe to call repeatedly and from
+ * several threads. Called implicitly by the first producer call on a device;
+ * call it explicitly before capturing producer calls into a HIP graph. */
+int nvfp4_init(void);
+
+/* ---- stage P: producer ---------------------------------------------------------------- */
+
+/*
+ * Fused SwiGLU -> NVFP4 quantization of y = RN_bf16(silu_bf16(gate) * up), where
+ * silu_bf16 is x / (1 + e^-x) correctly rounded to bf16 (the component-2 summary's
+ * pre-fusion chain: a bf16 silu kernel, then a bf16 multiply kernel).
+ *
+ * gate_dev, up_dev : bf16 [m, k] row-major, row strides ld_gate, ld_up (elements,
+ *                    multiples of 8, >= k); 16-byte aligned. Read only.
+ * m, k             : logical rows (>= 0) and columns (k > 0, k % 64 == 0). With
+ *                    m == 0 only the global scale (0) is written and the input,
+ *                    qdata and scales pointers may be NULL.
+ * qdata_dev        : out, nvfp4_qdata_bytes(m, k) bytes, 16-byte aligned.
+ * scales_dev       : out, nvfp4_scale_bytes(m, k) bytes, 16-byte aligned.
+ * global_scale_dev : out, one float: g = amax / 2688 rounded up to FP32 (2688 =
+ *                    6 * 448), amax = max |y| over the m logical rows (0 if none).
+ * workspace_dev    : nvfp4_quantize_workspace_bytes() bytes (see there).
+ *
+ * Every byte of qdata and scales is written, padding included. Block scale S is
+ * the smallest UE4M3 byte with v(S) * 6 * g >= max |y| over its 16 elements; each
+ * code is the E2M1 value nearest to |y| / (v(S) * g), ties to the even code, with
+ * the sign of y (also on zero). One cooperative launch: absmax pass, grid-wide
+ * barrier, pack-and-swizzle pass. Inputs must be finite and keep every
+ * |silu(gate) * up| below 2^128.
+ */
+int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up,
+                          int64_t m, int64_t k, void* qdata_dev, void* scales_dev,
+                          float* global_scale_dev, void* workspace_dev, void* stream);
+
+/* Plain NVFP4 quantization of x (y = x): the same contract as
+ * nvfp4_quantize_swiglu with one bf16 [rows, k] input of row stride ld_x. Used for
+ * the QKV / attention-output / FC1 activations and for weights. */
+int nvfp4_quantize(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, void* qdata_dev,
+                   void* scales_dev, float* global_scale_dev, void* workspace_dev, void* stream);
+
+/* ---- stage G: GEMM ---------------------------------------------------------------------- */
+
+/*
+ * D = RN_bf16(g_a * g_w * sum_b v(SA[m,b]) v(SW[n,b]) sum_{k in b} e2m1(A[m,k]) e2m1(W[n,k]))
+ * for m < m_padded, n < n: the block-scaled NVFP4 GEMM with FP32 accumulation and
+ * BF16 output ("FC2 NVFP4 Scheduling Results": split-K 1, zero workspace, no
+ * global reduction, exactly one write of the padded BF16 output).
+ *
+ * a_qdata_dev, a_scales_dev : activation as written by the producer for
+ *                             nvfp4_padded_rows(m) == m_padded rows.
+ * a_global_dev, w_global_dev: device floats g_a, g_w (read on the device).
+ * w_qdata_dev, w_scales_dev : weight [n, k] as written by nvfp4_quantize(rows = n).
+ * d_dev                     : out, bf16 [m_padded, n] row-major, 16-byte aligned.
+ * m_padded % 16 == 0, n % 16 == 0, k % 64 == 0. Rows of D whose activation rows
+ * are zero padding come out +0. Takes no workspace.
+ */
+int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
+                       const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
+                       void* d_dev, int64_t m_padded, int64_t n, int64_t k, void* stream);
+
+/* ---- self-test hook ---------------------------------------------------------------------- */
+
+/* y[i] = silu_bf16(x[i]) for i < count, bf16 bit patterns, with the table the
+ * producer uses (so the producer's activation can be checked on all 65,536
+ * inputs). x_dev, y_dev: 2-byte aligned device arrays of count elements. */
+int nvfp4_silu_bf16(const void* x_dev, void* y_dev, int64_t count, void* stream);
+
+/* ---- diagnostics -------------------------------------------------------------------------- */
+
+/* Static text for a status code. */
+const char* nvfp4_status_string(int status);
+
+/* Detail of the last failing call on this host thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+/* Compile-time and run-time HIP versions, target architecture and the device
+ * the library last initialised, as one line of text. */
+const char* nvfp4_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

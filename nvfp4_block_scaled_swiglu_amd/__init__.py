@@ -1,0 +1,258 @@
+"""MI355X (gfx950) NVFP4 SwiGLU producer and block-scaled GEMM - Python binding.
+
+A thin ctypes layer over the C ABI in ``include/nvfp4.h`` (``libnvfp4.so``, built
+in-tree by ``build.py``). Every step of the computation runs in the library's HIP
+kernels; this module only marshals torch tensors (device memory) and the current
+torch stream into the C calls, and allocates outputs with torch when the caller
+does not pass them. There is no fallback path: if the library is missing or a
+call fails, an exception is raised.
+
+Functions carry the C names:
+
+* ``nvfp4_quantize_swiglu(gate, up)`` - fused SwiGLU -> NVFP4 producer
+* ``nvfp4_quantize(x)``               - plain NVFP4 quantization (activations, weights)
+* ``nvfp4_gemm_bf16out(a, w)``        - block-scaled GEMM, FP32 accumulation, BF16 out
+* ``nvfp4_silu_bf16(x)``              - the producer's bf16 silu, elementwise (self-test)
+* size helpers ``nvfp4_padded_rows``, ``nvfp4_qdata_bytes``, ``nvfp4_scale_bytes``, ...
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+from typing import Dict, Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4.so")
+
+NVFP4_OK = 0
+STATUS_NAMES = {
+    0: "NVFP4_OK",
+    1: "NVFP4_ERR_INVALID_ARG",
+    2: "NVFP4_ERR_UNSUPPORTED_SHAPE",
+    3: "NVFP4_ERR_MISALIGNED",
+    4: "NVFP4_ERR_WORKSPACE",
+    5: "NVFP4_ERR_NO_DEVICE",
+    6: "NVFP4_ERR_LAUNCH",
+}
+
+# Every symbol include/nvfp4.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+SIGNATURES = {
+    "nvfp4_padded_rows": (_I64, [_I64]),
+    "nvfp4_scale_rows": (_I64, [_I64]),
+    "nvfp4_scale_cols": (_I64, [_I64]),
+    "nvfp4_qdata_bytes": (_I64, [_I64, _I64]),
+    "nvfp4_scale_bytes": (_I64, [_I64, _I64]),
+    "nvfp4_quantize_workspace_bytes": (_I64, []),
+    "nvfp4_init": (_INT, []),
+    "nvfp4_quantize_swiglu": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "nvfp4_quantize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "nvfp4_gemm_bf16out": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "nvfp4_silu_bf16": (_INT, [_P, _P, _I64, _P]),
+    "nvfp4_status_string": (ctypes.c_char_p, [_INT]),
+    "nvfp4_last_error": (ctypes.c_char_p, []),
+    "nvfp4_build_info": (ctypes.c_char_p, []),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({detail})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                                  "g.build()'` or `python nvfp4_block_scaled_swiglu_amd/build.py`")
+            l = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(l, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = l
+    return _lib
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != NVFP4_OK:
+        detail = lib().nvfp4_last_error().decode(errors="replace")
+        raise Nvfp4Error(rc, where, detail)
+
+
+# ---- dispatch counters (attempts / successes / failures per entry point) ----------------
+COUNTERS: Dict[str, Dict[str, int]] = {}
+
+
+def _count(name: str, ok: bool) -> None:
+    c = COUNTERS.setdefault(name, {"attempts": 0, "successes": 0, "failures": 0})
+    c["attempts"] += 1
+    c["successes" if ok else "failures"] += 1
+
+
+def _call(name: str, *args) -> None:
+    rc = getattr(lib(), name)(*args)
+    _count(name, rc == NVFP4_OK)
+    _check(rc, name)
+
+
+# ---- sizes ---------------------------------------------------------------------------------
+
+def nvfp4_padded_rows(rows: int) -> int:
+    return int(lib().nvfp4_padded_rows(rows))
+
+
+def nvfp4_scale_rows(rows: int) -> int:
+    return int(lib().nvfp4_scale_rows(rows))
+
+
+def nvfp4_scale_cols(k: int) -> int:
+    return int(lib().nvfp4_scale_cols(k))
+
+
+def nvfp4_qdata_bytes(rows: int, k: int) -> int:
+    return int(lib().nvfp4_qdata_bytes(rows, k))
+
+
+def nvfp4_scale_bytes(rows: int, k: int) -> int:
+    return int(lib().nvfp4_scale_bytes(rows, k))
+
+
+def nvfp4_quantize_workspace_bytes() -> int:
+    return int(lib().nvfp4_quantize_workspace_bytes())
+
+
+def nvfp4_status_string(status: int) -> str:
+    return lib().nvfp4_status_string(status).decode()
+
+
+def nvfp4_build_info() -> str:
+    return lib().nvfp4_build_info().decode()
+
+
+def nvfp4_init() -> None:
+    _check(lib().nvfp4_init(), "nvfp4_init")
+
+
+# ---- tensors -------------------------------------------------------------------------------
+
+@dataclass
+class Nvfp4Tensor:
+    """A quantized [rows, k] tensor as the library lays it out in device memory."""
+    qdata: "torch.Tensor"         # uint8 [padded_rows, k/2]
+    scales: "torch.Tensor"        # uint8 [scale_rows * scale_cols], 128x4-tiled
+    global_scale: "torch.Tensor"  # float32 [1]
+    rows: int                     # logical rows
+    k: int
+
+    @property
+    def padded_rows(self) -> int:
+        return nvfp4_padded_rows(self.rows)
+
+
+def empty_nvfp4(rows: int, k: int, device) -> Nvfp4Tensor:
+    import torch
+    return Nvfp4Tensor(
+        qdata=torch.empty((nvfp4_padded_rows(rows), k // 2), dtype=torch.uint8, device=device),
+        scales=torch.empty((nvfp4_scale_bytes(rows, k),), dtype=torch.uint8, device=device),
+        global_scale=torch.empty((1,), dtype=torch.float32, device=device),
+        rows=rows, k=k)
+
+
+_workspaces: Dict[Tuple[int, int], "torch.Tensor"] = {}
+
+
+def _workspace(device, stream_handle: int):
+    """A zeroed producer workspace per (device, stream); the kernel leaves it zeroed."""
+    import torch
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = torch.zeros((nvfp4_quantize_workspace_bytes(),), dtype=torch.uint8, device=device)
+        torch.cuda.synchronize(device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _bf16_2d(t, name: str):
+    import torch
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_cuda:
+        raise ValueError(f"{name} must be a 2-D bfloat16 CUDA tensor")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t
+
+
+def nvfp4_quantize_swiglu(gate, up, out: Optional[Nvfp4Tensor] = None, m: Optional[int] = None,
+                          workspace=None, stream=None) -> Nvfp4Tensor:
+    """Fused y = RN_bf16(silu_bf16(gate) * up) -> NVFP4 (QDATA, 128x4-tiled scales, global scale)."""
+    _bf16_2d(gate, "gate")
+    _bf16_2d(up, "up")
+    m = gate.shape[0] if m is None else m
+    k = gate.shape[1]
+    if up.shape[1] != k or up.shape[0] < m or gate.shape[0] < m:
+        raise ValueError("gate/up shapes disagree")
+    out = empty_nvfp4(m, k, gate.device) if out is None else out
+    sh = _stream_handle(stream)
+    ws = _workspace(gate.device, sh) if workspace is None else workspace
+    _call("nvfp4_quantize_swiglu", gate.data_ptr(), gate.stride(0), up.data_ptr(), up.stride(0), m, k,
+          out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(), sh)
+    return out
+
+
+def nvfp4_quantize(x, out: Optional[Nvfp4Tensor] = None, rows: Optional[int] = None, workspace=None,
+                   stream=None) -> Nvfp4Tensor:
+    """Plain NVFP4 quantization of a bf16 [rows, k] tensor (y = x)."""
+    _bf16_2d(x, "x")
+    rows = x.shape[0] if rows is None else rows
+    k = x.shape[1]
+    out = empty_nvfp4(rows, k, x.device) if out is None else out
+    sh = _stream_handle(stream)
+    ws = _workspace(x.device, sh) if workspace is None else workspace
+    _call("nvfp4_quantize", x.data_ptr(), x.stride(0), rows, k, out.qdata.data_ptr(), out.scales.data_ptr(),
+          out.global_scale.data_ptr(), ws.data_ptr(), sh)
+    return out
+
+
+def nvfp4_gemm_bf16out(a: Nvfp4Tensor, w: Nvfp4Tensor, out=None, stream=None):
+    """D[m_padded, n] = RN_bf16(g_a g_w sum_k deq(A) deq(W)), FP32 accumulation."""
+    import torch
+    if a.k != w.k:
+        raise ValueError("k mismatch")
+    m_pad = a.padded_rows
+    n = w.rows
+    if out is None:
+        out = torch.empty((m_pad, n), dtype=torch.bfloat16, device=a.qdata.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (m_pad, n) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [m_padded, n] tensor")
+    _call("nvfp4_gemm_bf16out", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
+          w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), out.data_ptr(), m_pad, n, a.k,
+          _stream_handle(stream))
+    return out
+
+
+def nvfp4_silu_bf16(x, out=None, stream=None):
+    """The producer's correctly rounded bf16 silu applied elementwise (uint16/int16/bf16 bits)."""
+    import torch
+    out = torch.empty_like(x) if out is None else out
+    _call("nvfp4_silu_bf16", x.data_ptr(), out.data_ptr(), x.numel(), _stream_handle(stream))
+    return out

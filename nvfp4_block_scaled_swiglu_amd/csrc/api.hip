@@ -1,0 +1,268 @@
+// api.hip - the C ABI of the library (declared in include/nvfp4.h): argument
+// validation, one-time device set-up, launch of the producer and GEMM kernels.
+//
+// Every entry point validates all arguments before it enqueues anything; on an
+// error it returns a status, enqueues nothing and writes nothing, and records a
+// per-thread message for nvfp4_last_error().
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/nvfp4.h"
+#include "common.hpp"
+
+namespace nvfp4 {
+hipError_t silu_table_address(const uint16_t** p);
+hipError_t launch_silu_table_init(hipStream_t stream);
+hipError_t launch_silu_apply(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
+size_t producer_smem_bytes(bool swiglu);
+const void* producer_kernel_ptr(bool swiglu);
+int producer_block_threads();
+hipError_t launch_producer(bool swiglu, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
+                           int64_t m, int64_t k, uint8_t* qdata, uint8_t* scales, float* gout,
+                           void* workspace, const uint16_t* silu_table, int max_blocks, hipStream_t stream);
+size_t gemm_smem_bytes();
+const void* gemm_kernel_ptr();
+hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
+                       const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
+                       hipStream_t stream);
+}  // namespace nvfp4
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;  // 32-bit buffer offsets in the kernels
+
+struct DeviceState {
+  bool ready = false;
+  const uint16_t* silu_table = nullptr;
+  int producer_blocks_swiglu = 0;
+  int producer_blocks_plain = 0;
+  int cu_count = 0;
+  char arch[64] = {0};
+};
+
+DeviceState g_dev[kMaxDevices];
+std::mutex g_init_mutex;
+thread_local char t_last_error[512] = "";
+char g_build_info[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(t_last_error, sizeof(t_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  t_last_error[0] = '\0';
+  return NVFP4_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// One-time set-up of the current device (caller holds no lock).
+int ensure_device(DeviceState** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(NVFP4_ERR_NO_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
+  if (dev >= kMaxDevices) return fail(NVFP4_ERR_NO_DEVICE, "device index %d out of range", dev);
+  DeviceState& st = g_dev[dev];
+  if (st.ready) {
+    *out = &st;
+    return NVFP4_OK;
+  }
+  std::lock_guard<std::mutex> lock(g_init_mutex);
+  if (st.ready) {
+    *out = &st;
+    return NVFP4_OK;
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(NVFP4_ERR_NO_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(NVFP4_ERR_NO_DEVICE, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+  snprintf(st.arch, sizeof(st.arch), "%s", prop.gcnArchName);
+  st.cu_count = prop.multiProcessorCount;
+  if (!prop.cooperativeLaunch) return fail(NVFP4_ERR_NO_DEVICE, "device %d lacks cooperative launch", dev);
+
+  // kernels with more than 64 KiB of dynamic LDS must opt in
+  for (int sw = 0; sw < 2; ++sw) {
+    e = hipFuncSetAttribute(nvfp4::producer_kernel_ptr(sw != 0), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)nvfp4::producer_smem_bytes(sw != 0));
+    if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer LDS attribute: %s", hipGetErrorString(e));
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nvfp4::producer_kernel_ptr(sw != 0),
+                                                     nvfp4::producer_block_threads(),
+                                                     nvfp4::producer_smem_bytes(sw != 0));
+    if (e != hipSuccess || per_cu < 1)
+      return fail(NVFP4_ERR_LAUNCH, "producer occupancy query: %s (%d)", hipGetErrorString(e), per_cu);
+    (sw ? st.producer_blocks_swiglu : st.producer_blocks_plain) = per_cu * st.cu_count;
+  }
+  e = hipFuncSetAttribute(nvfp4::gemm_kernel_ptr(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)nvfp4::gemm_smem_bytes());
+  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "gemm LDS attribute: %s", hipGetErrorString(e));
+
+  e = nvfp4::silu_table_address(&st.silu_table);
+  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "silu table address: %s", hipGetErrorString(e));
+  hipStream_t s;
+  e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "stream create: %s", hipGetErrorString(e));
+  e = nvfp4::launch_silu_table_init(s);
+  hipError_t e2 = hipStreamSynchronize(s);
+  (void)hipStreamDestroy(s);
+  if (e != hipSuccess || e2 != hipSuccess)
+    return fail(NVFP4_ERR_LAUNCH, "silu table init: %s / %s", hipGetErrorString(e), hipGetErrorString(e2));
+  st.ready = true;
+  *out = &st;
+  return NVFP4_OK;
+}
+
+int check_quant_args(const void* x, int64_t ldx, const void* u, int64_t ldu, bool swiglu, int64_t m, int64_t k,
+                     const void* qdata, const void* scales, const float* g, const void* ws) {
+  if (!g) return fail(NVFP4_ERR_INVALID_ARG, "null global-scale pointer");
+  // with no rows nothing is read or written except the global scale
+  if (m != 0 && (!x || (swiglu && !u) || !qdata || !scales))
+    return fail(NVFP4_ERR_INVALID_ARG, "null input or output pointer");
+  if (!ws) return fail(NVFP4_ERR_WORKSPACE, "null workspace");
+  if (m < 0 || k <= 0) return fail(NVFP4_ERR_INVALID_ARG, "bad shape m=%lld k=%lld", (long long)m, (long long)k);
+  if (k % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k=%lld is not a multiple of 64", (long long)k);
+  if (ldx < k || (swiglu && ldu < k))
+    return fail(NVFP4_ERR_INVALID_ARG, "row stride below k (ld=%lld, %lld, k=%lld)", (long long)ldx,
+                (long long)ldu, (long long)k);
+  if (ldx % 8 != 0 || (swiglu && ldu % 8 != 0))
+    return fail(NVFP4_ERR_MISALIGNED, "row strides must be multiples of 8 elements");
+  if (!aligned16(x) || (swiglu && !aligned16(u)) || !aligned16(qdata) || !aligned16(scales) || ((uintptr_t)g & 3u) ||
+      !aligned16(ws))
+    return fail(NVFP4_ERR_MISALIGNED, "pointers must be 16-byte aligned (global scale 4-byte)");
+  const int64_t rows_pad = (m + 15) / 16 * 16;
+  const int64_t srows = (rows_pad + 127) / 128 * 128;
+  if (srows / 128 * ((k + 255) / 256) > (int64_t)1 << 30)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "tensor too large");
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t nvfp4_padded_rows(int64_t rows) { return rows < 0 ? -1 : (rows + 15) / 16 * 16; }
+int64_t nvfp4_scale_rows(int64_t rows) { return rows < 0 ? -1 : (nvfp4_padded_rows(rows) + 127) / 128 * 128; }
+int64_t nvfp4_scale_cols(int64_t k) { return k < 0 ? -1 : (k / 16 + 3) / 4 * 4; }
+int64_t nvfp4_qdata_bytes(int64_t rows, int64_t k) {
+  return (rows < 0 || k < 0) ? -1 : nvfp4_padded_rows(rows) * (k / 2);
+}
+int64_t nvfp4_scale_bytes(int64_t rows, int64_t k) {
+  return (rows < 0 || k < 0) ? -1 : nvfp4_scale_rows(rows) * nvfp4_scale_cols(k);
+}
+int64_t nvfp4_quantize_workspace_bytes(void) { return (int64_t)sizeof(nvfp4::ProducerWorkspace); }
+
+int nvfp4_init(void) {
+  DeviceState* st = nullptr;
+  int rc = ensure_device(&st);
+  return rc == NVFP4_OK ? ok() : rc;
+}
+
+static int quantize_common(bool swiglu, const void* x, int64_t ldx, const void* u, int64_t ldu, int64_t m, int64_t k,
+                           void* qdata, void* scales, float* g, void* ws, void* stream) {
+  int rc = check_quant_args(x, ldx, u, ldu, swiglu, m, k, qdata, scales, g, ws);
+  if (rc != NVFP4_OK) return rc;
+  DeviceState* st = nullptr;
+  rc = ensure_device(&st);
+  if (rc != NVFP4_OK) return rc;
+  hipError_t e = nvfp4::launch_producer(swiglu, (const uint16_t*)x, ldx, (const uint16_t*)u, ldu, m, k,
+                                        (uint8_t*)qdata, (uint8_t*)scales, g, ws, st->silu_table,
+                                        swiglu ? st->producer_blocks_swiglu : st->producer_blocks_plain,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up, int64_t m,
+                          int64_t k, void* qdata_dev, void* scales_dev, float* global_scale_dev, void* workspace_dev,
+                          void* stream) {
+  return quantize_common(true, gate_dev, ld_gate, up_dev, ld_up, m, k, qdata_dev, scales_dev, global_scale_dev,
+                         workspace_dev, stream);
+}
+
+int nvfp4_quantize(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, void* qdata_dev, void* scales_dev,
+                   float* global_scale_dev, void* workspace_dev, void* stream) {
+  return quantize_common(false, x_dev, ld_x, nullptr, 0, rows, k, qdata_dev, scales_dev, global_scale_dev,
+                         workspace_dev, stream);
+}
+
+int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
+                       const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev, void* d_dev,
+                       int64_t m_padded, int64_t n, int64_t k, void* stream) {
+  if (!a_qdata_dev || !a_scales_dev || !a_global_dev || !w_qdata_dev || !w_scales_dev || !w_global_dev || !d_dev)
+    return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (m_padded < 0 || n <= 0 || k <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "bad shape m_padded=%lld n=%lld k=%lld", (long long)m_padded, (long long)n,
+                (long long)k);
+  if (m_padded % 16 != 0 || n % 16 != 0 || k % 64 != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "need m_padded %% 16 == 0, n %% 16 == 0, k %% 64 == 0 (got %lld, %lld, %lld)",
+                (long long)m_padded, (long long)n, (long long)k);
+  if (!aligned16(a_qdata_dev) || !aligned16(a_scales_dev) || !aligned16(w_qdata_dev) || !aligned16(w_scales_dev) ||
+      !aligned16(d_dev) || ((uintptr_t)a_global_dev & 3u) || ((uintptr_t)w_global_dev & 3u))
+    return fail(NVFP4_ERR_MISALIGNED, "pointers must be 16-byte aligned (global scales 4-byte)");
+  const int64_t mt = (m_padded + 255) / 256 * 256, nt = (n + 255) / 256 * 256;
+  if (mt * (k / 2) >= kMaxBufferBytes || nt * (k / 2) >= kMaxBufferBytes ||
+      (mt + 128) * nvfp4_scale_cols(k) >= kMaxBufferBytes || (nt + 128) * nvfp4_scale_cols(k) >= kMaxBufferBytes ||
+      (mt / 256) * (nt / 256) >= ((int64_t)1 << 31))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "operands beyond 2 GiB are not supported");
+  DeviceState* st = nullptr;
+  int rc = ensure_device(&st);
+  if (rc != NVFP4_OK) return rc;
+  if (m_padded == 0) return ok();
+  hipError_t e = nvfp4::launch_gemm((const uint8_t*)a_qdata_dev, (const uint8_t*)a_scales_dev, a_global_dev,
+                                    (const uint8_t*)w_qdata_dev, (const uint8_t*)w_scales_dev, w_global_dev,
+                                    (uint16_t*)d_dev, m_padded, n, k, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int nvfp4_silu_bf16(const void* x_dev, void* y_dev, int64_t count, void* stream) {
+  if (count < 0) return fail(NVFP4_ERR_INVALID_ARG, "negative count");
+  if (count > 0 && (!x_dev || !y_dev)) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (((uintptr_t)x_dev & 1u) || ((uintptr_t)y_dev & 1u)) return fail(NVFP4_ERR_MISALIGNED, "2-byte alignment");
+  DeviceState* st = nullptr;
+  int rc = ensure_device(&st);
+  if (rc != NVFP4_OK) return rc;
+  hipError_t e = nvfp4::launch_silu_apply((const uint16_t*)x_dev, (uint16_t*)y_dev, count, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "silu launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARG: return "invalid argument";
+    case NVFP4_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case NVFP4_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing";
+    case NVFP4_ERR_NO_DEVICE: return "no usable gfx950 device";
+    case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* nvfp4_last_error(void) { return t_last_error; }
+
+const char* nvfp4_build_info(void) {
+  int rt = 0, drv = 0;
+  (void)hipRuntimeGetVersion(&rt);
+  (void)hipDriverGetVersion(&drv);
+  int dev = -1;
+  const char* arch = "";
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices && g_dev[dev].ready) arch = g_dev[dev].arch;
+  snprintf(g_build_info, sizeof(g_build_info),
+           "nvfp4 gfx950; HIP compile %d.%d.%d; HIP runtime %d; driver %d; device arch %s", HIP_VERSION_MAJOR,
+           HIP_VERSION_MINOR, HIP_VERSION_PATCH, rt, drv, arch[0] ? arch : "(not initialised)");
+  return g_build_info;
+}
+
+}  // extern "C"

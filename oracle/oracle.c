@@ -99,7 +99,23 @@ static uint16_t rn_bf16_pair(long double hi, long double lo) {
 
 static uint16_t rn_bf16_ld(long double v) { return rn_bf16_pair(v, 0.0L); }
 
-uint16_t oracle_rn_bf16(double v) { return rn_bf16_ld((long double)v); }
+/* Round a double to the nearest bf16 (ties to even), one rounding. */
+uint16_t oracle_rn_bf16(double v) {
+  if (v == 0.0) return signbit(v) ? 0x8000u : 0x0000u;
+  uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  double a = fabs(v);
+  int e;
+  frexp(a, &e);            /* a = f * 2^e, f in [0.5, 1): leading bit at 2^(e-1) */
+  int lead = e - 1;
+  if (lead < -126) lead = -126;
+  double q = ldexp(1.0, lead - 7);
+  double r = nearbyint(a / q) * q; /* a / q is exact; nearbyint rounds half to even */
+  if (r >= 0x1p128) return sign | 0x7F80u;
+  float f = (float)r;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return sign | (uint16_t)(u >> 16);
+}
 
 /*
  * O1: silu correctly rounded to bf16. For |x| < 1/16 the value is formed as
@@ -258,26 +274,44 @@ int oracle_quantize(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t 
   /* O4 */
   const float g = oracle_global_scale(amax);
 
-  /* O5-O8 */
+  /* O5-O8. The per-element decisions only depend on the bf16 input and the
+   * block's scale byte, so they are memoized: for each of the 65,536 bf16 bit
+   * patterns y and each scale byte s the code is oracle_e2m1_code(y, s, g), filled
+   * lazily; block scales come from oracle_block_scale directly. */
   memset(scales, 0, (size_t)(rpad * cpad));
+  uint8_t* code_memo = (uint8_t*)malloc((size_t)127 * 65536);
+  if (!code_memo) {
+    free(y);
+    return OR_ENOMEM;
+  }
+  memset(code_memo, 0xFF, (size_t)127 * 65536);
 #pragma omp parallel for schedule(static) num_threads(nthreads)
   for (int64_t r = 0; r < m_pad; ++r) {
     for (int64_t b = 0; b < nb; ++b) {
-      double yv[16];
+      uint16_t yb[16];
       double bmax = 0.0;
       for (int t = 0; t < 16; ++t) {
-        yv[t] = (r < m) ? bf16_to_double(y[r * k + b * 16 + t]) : 0.0;
-        if (fabs(yv[t]) > bmax) bmax = fabs(yv[t]);
+        yb[t] = (r < m) ? y[r * k + b * 16 + t] : 0;
+        double av = fabs(bf16_to_double(yb[t]));
+        if (av > bmax) bmax = av;
       }
       uint8_t s = oracle_block_scale(bmax, g);
       scales[oracle_scale_offset(r, b, cpad)] = s;
-      for (int t = 0; t < 16; t += 2) {
-        uint8_t lo = oracle_e2m1_code(yv[t], s, g);
-        uint8_t hi = oracle_e2m1_code(yv[t + 1], s, g);
-        qdata[r * (k / 2) + (b * 16 + t) / 2] = (uint8_t)(lo | (hi << 4));
+      uint8_t code[16];
+      for (int t = 0; t < 16; ++t) {
+        uint8_t* slot = &code_memo[(size_t)s * 65536 + yb[t]];
+        uint8_t c = __atomic_load_n(slot, __ATOMIC_RELAXED);
+        if (c == 0xFF) {
+          c = oracle_e2m1_code(bf16_to_double(yb[t]), s, g);
+          __atomic_store_n(slot, c, __ATOMIC_RELAXED);
+        }
+        code[t] = c;
       }
+      for (int t = 0; t < 16; t += 2)
+        qdata[r * (k / 2) + (b * 16 + t) / 2] = (uint8_t)(code[t] | (code[t + 1] << 4));
     }
   }
+  free(code_memo);
   if (y_out) memcpy(y_out, y, (size_t)m * (size_t)k * sizeof(uint16_t));
   free(y);
   *g_out = g;
@@ -323,6 +357,27 @@ static uint16_t rn_bf16_exact(int negative, unsigned __int128 P, int E) {
   uint32_t u;
   memcpy(&u, &f, 4);
   return sign | (uint16_t)(u >> 16);
+}
+
+/* One output row: exact integer sums per column, rounded once. */
+__attribute__((target_clones("avx2", "default")))
+static void gemm_row(const int8_t* a, const int64_t* sa, const int8_t* W, const int64_t* SW, int64_t n,
+                     int64_t nb, uint64_t Ga, uint64_t Gw, int Ebase, uint16_t* out) {
+  const int64_t k = nb * 16;
+  for (int64_t j = 0; j < n; ++j) {
+    const int8_t* w = W + j * k;
+    const int64_t* sw = SW + j * nb;
+    int64_t total = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+      int32_t dot = 0;
+      for (int t = 0; t < 16; ++t) dot += (int32_t)a[b * 16 + t] * (int32_t)w[b * 16 + t];
+      total += (int64_t)dot * (sa[b] * sw[b]);
+    }
+    int neg = total < 0;
+    unsigned __int128 P = (unsigned __int128)(neg ? -total : total);
+    P *= (unsigned __int128)Ga * Gw;
+    out[j] = rn_bf16_exact(neg, P, Ebase);
+  }
 }
 
 /*
@@ -375,24 +430,8 @@ int oracle_gemm_rows(const uint8_t* aq, const uint8_t* as, int64_t a_rows_total,
   const int Ebase = (ea - 24) + (ew - 24) - 20; /* 2^-20: (1/2)^2 from q2, (2^-9)^2 from s9 */
 
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
-  for (int64_t i = 0; i < nrows; ++i) {
-    const int8_t* a = A + i * k;
-    const int64_t* sa = SA + i * nb;
-    for (int64_t j = 0; j < n; ++j) {
-      const int8_t* w = W + j * k;
-      const int64_t* sw = SW + j * nb;
-      int64_t total = 0;
-      for (int64_t b = 0; b < nb; ++b) {
-        int32_t dot = 0;
-        for (int t = 0; t < 16; ++t) dot += (int32_t)a[b * 16 + t] * (int32_t)w[b * 16 + t];
-        total += (int64_t)dot * (sa[b] * sw[b]);
-      }
-      int neg = total < 0;
-      unsigned __int128 P = (unsigned __int128)(neg ? -total : total);
-      P *= (unsigned __int128)Ga * Gw;
-      out[i * n + j] = rn_bf16_exact(neg, P, Ebase);
-    }
-  }
+  for (int64_t i = 0; i < nrows; ++i)
+    gemm_row(A + i * k, SA + i * nb, W, SW, n, nb, Ga, Gw, Ebase, out + i * n);
   free(A); free(W); free(SA); free(SW);
   return OR_OK;
 }

@@ -1,0 +1,139 @@
+"""Host-side checks of the C-ABI boundary (no GPU needed): the shared library loads,
+exports every symbol include/nvfp4.h declares, its size functions agree with the
+oracle's geometry, and argument validation returns the documented status codes
+before anything touches a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import nvfp4_block_scaled_swiglu_amd as nv
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert "nvfp4_quantize_swiglu" in names and "nvfp4_gemm_bf16out" in names
+    lib = nv.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", nv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (nvfp4_[a-z0-9_]+)", out))
+    assert set(names) <= exported
+    # the binding declares exactly the header's functions
+    assert set(nv.SIGNATURES) == set(names)
+
+
+def test_library_is_gfx950_only():
+    """The embedded device code objects target gfx950 and nothing else."""
+    out = subprocess.run(["strings", nv.LIB_PATH], capture_output=True, text=True).stdout
+    targets = set(re.findall(r"amdgcn-amd-amdhsa--(gfx[0-9a-f]+)", out))
+    assert targets == {"gfx950"}, targets
+
+
+@pytest.mark.parametrize("rows,k", [(0, 64), (1, 64), (16, 1024), (37810, 14336), (37711, 14336), (5376, 14336),
+                                    (16128, 5376), (28672, 5376), (37810, 7168), (130, 192)])
+def test_sizes_match_oracle_geometry(rows, k):
+    assert nv.nvfp4_padded_rows(rows) == oracle.padded_rows(rows)
+    assert nv.nvfp4_qdata_bytes(rows, k) == oracle.qdata_bytes(rows, k)
+    assert nv.nvfp4_scale_bytes(rows, k) == oracle.scale_bytes(rows, k)
+    assert nv.nvfp4_scale_rows(rows) == oracle.scale_rows(rows)
+    assert nv.nvfp4_scale_cols(k) == oracle.scale_cols(k)
+
+
+def test_size_functions_reject_negative():
+    assert nv.nvfp4_padded_rows(-1) == -1
+    assert nv.nvfp4_qdata_bytes(-1, 64) == -1
+    assert nv.nvfp4_quantize_workspace_bytes() == 256
+
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced: validation fails first
+
+
+def call_quant(**kw):
+    args = dict(x=FAKE, ld=64, rows=16, k=64, q=FAKE, s=FAKE, g=FAKE, ws=FAKE)
+    args.update(kw)
+    return nv.lib().nvfp4_quantize(args["x"], args["ld"], args["rows"], args["k"], args["q"], args["s"],
+                                   args["g"], args["ws"], None)
+
+
+def call_swiglu(**kw):
+    args = dict(g_=FAKE, ldg=64, u=FAKE, ldu=64, m=16, k=64, q=FAKE, s=FAKE, g=FAKE, ws=FAKE)
+    args.update(kw)
+    return nv.lib().nvfp4_quantize_swiglu(args["g_"], args["ldg"], args["u"], args["ldu"], args["m"], args["k"],
+                                          args["q"], args["s"], args["g"], args["ws"], None)
+
+
+def call_gemm(**kw):
+    args = dict(aq=FAKE, as_=FAKE, ga=FAKE, wq=FAKE, ws=FAKE, gw=FAKE, d=FAKE, m=16, n=16, k=64)
+    args.update(kw)
+    return nv.lib().nvfp4_gemm_bf16out(args["aq"], args["as_"], args["ga"], args["wq"], args["ws"], args["gw"],
+                                       args["d"], args["m"], args["n"], args["k"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(q=None), 1), (dict(s=None), 1), (dict(g=None), 1),
+    (dict(ws=None), 4), (dict(rows=-1), 1), (dict(k=0), 1), (dict(k=96, ld=96), 2),
+    (dict(ld=32), 1), (dict(ld=68), 3), (dict(x=FAKE + 8), 3), (dict(q=FAKE + 4), 3),
+    (dict(g=FAKE + 2), 3),
+])
+def test_quantize_validation(kw, status):
+    assert call_quant(**kw) == status
+    assert nv.lib().nvfp4_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(u=None), 1), (dict(g_=None), 1), (dict(ldu=16), 1), (dict(ldg=68), 3), (dict(u=FAKE + 2), 3),
+    (dict(k=32, ldg=32, ldu=32), 2),
+])
+def test_swiglu_validation(kw, status):
+    assert call_swiglu(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(aq=None), 1), (dict(d=None), 1), (dict(ga=None), 1), (dict(n=0), 1), (dict(m=-16), 1),
+    (dict(m=8), 2), (dict(n=24), 2), (dict(k=96), 2), (dict(d=FAKE + 8), 3), (dict(gw=FAKE + 1), 3),
+    (dict(m=1 << 22, k=1 << 12), 2),
+])
+def test_gemm_validation(kw, status):
+    assert call_gemm(**kw) == status
+
+
+def test_silu_validation():
+    assert nv.lib().nvfp4_silu_bf16(None, None, -1, None) == 1
+    assert nv.lib().nvfp4_silu_bf16(None, FAKE, 4, None) == 1
+    assert nv.lib().nvfp4_silu_bf16(FAKE + 1, FAKE, 4, None) == 3
+
+
+def test_status_strings():
+    for s in range(7):
+        assert nv.nvfp4_status_string(s) not in ("", "unknown status")
+    assert nv.nvfp4_status_string(99) == "unknown status"
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(nv.Nvfp4Error) as ei:
+        nv._call("nvfp4_gemm_bf16out", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 64, None)
+    assert ei.value.status == 2
+    assert nv.COUNTERS["nvfp4_gemm_bf16out"]["failures"] >= 1
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    """With valid arguments and no visible GPU the call reaches the device check and
+    returns NVFP4_ERR_NO_DEVICE (nothing is launched)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert call_quant() == 5
+    assert "device" in nv.lib().nvfp4_last_error().decode().lower()

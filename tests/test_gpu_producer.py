@@ -1,0 +1,188 @@
+"""GPU parity of the producer (stage P) against the CPU oracle, through the C ABI.
+
+QDATA, scale buffer and global scale must be bit-exact, padding included, on every
+workload and edge case.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def check_quant(x_bits, up_bits, device, what, m=None):
+    _say(f"[producer] {what}: shape {x_bits.shape} m={m}")
+    _, qd, sc, g = parity.run_quantize(x_bits, up_bits, device, m=m)
+    rq, rs, rg = oracle.quantize(x_bits, up_bits, m=m)
+    assert np.float32(g).view(np.uint32) == np.float32(rg).view(np.uint32), f"{what}: g {g!r} != {rg!r}"
+    assert qd.shape == rq.shape and sc.shape == rs.shape
+    nq = int((qd != rq).sum())
+    ns = int((sc != rs).sum())
+    assert nq == 0 and ns == 0, f"{what}: {nq} QDATA bytes and {ns} scale bytes differ"
+    return qd, sc, g
+
+
+def test_silu_table_all_bf16_inputs(gpu):
+    """The producer's silu on all 65,536 bf16 bit patterns equals the oracle's
+    correctly rounded silu (finite inputs)."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    x = torch.arange(65536, dtype=torch.int32).to(torch.int16).to(gpu)
+    y = nv.nvfp4_silu_bf16(x).cpu().numpy().view(np.uint16)
+    want = oracle.silu_table()
+    finite = (np.arange(65536) & 0x7F80) != 0x7F80
+    bad = np.nonzero((y != want) & finite)[0]
+    assert bad.size == 0, [hex(b) for b in bad[:10]]
+
+
+def test_tiny_config(gpu):
+    w = synth.TINY
+    gate, up = w.activations()
+    check_quant(gate, up, gpu, "tiny swiglu")
+    check_quant(w.weight(), None, gpu, "tiny weight")
+
+
+@pytest.mark.parametrize("m,k", [(1, 64), (15, 64), (16, 128), (17, 192), (130, 320), (255, 1024), (300, 576)])
+def test_edge_shapes(gpu, m, k):
+    """Ragged rows (padding to 16 and to 128-row scale tiles) and widths that do not
+    fill a 256-column work item."""
+    gate = synth.normal_bf16(m, k, seed=m, tag=1, sigma=1.0)
+    up = synth.normal_bf16(m, k, seed=m, tag=2, sigma=1.0)
+    check_quant(gate, up, gpu, f"swiglu m={m} k={k}")
+    check_quant(gate, None, gpu, f"plain m={m} k={k}")
+
+
+def test_empty_rows(gpu):
+    """m = 0: no QDATA or scale bytes, g = 0."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    x = torch.zeros((16, 64), dtype=torch.bfloat16, device=gpu)
+    t = nv.nvfp4_quantize(x, rows=0)
+    t2 = nv.nvfp4_quantize_swiglu(x, x, m=0)
+    torch.cuda.synchronize()
+    assert t.qdata.numel() == 0 and t.scales.numel() == 0
+    assert float(t.global_scale.item()) == 0.0 and float(t2.global_scale.item()) == 0.0
+
+
+def test_strided_inputs(gpu):
+    """Row strides larger than k, different for gate and up."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    m, k = 200, 384
+    gate_full = synth.normal_bf16(m, k + 64, seed=5, tag=1, sigma=1.0)
+    up_full = synth.normal_bf16(m, k + 128, seed=5, tag=2, sigma=1.0)
+    g_t = parity.to_device_bf16(gate_full, gpu)[:, :k]
+    u_t = parity.to_device_bf16(up_full, gpu)[:, :k]
+    t = nv.nvfp4_quantize_swiglu(g_t, u_t)
+    torch.cuda.synchronize()
+    rq, rs, rg = oracle.quantize(np.ascontiguousarray(gate_full[:, :k]), np.ascontiguousarray(up_full[:, :k]))
+    assert (t.qdata.cpu().numpy() == rq).all() and (t.scales.cpu().numpy() == rs).all()
+    assert float(t.global_scale.item()) == rg
+
+
+def test_zero_and_signed_zero(gpu):
+    x = np.zeros((32, 128), dtype=np.uint16)
+    x[3, 5] = 0x8000
+    x[7, 100] = 0x8000
+    qd, sc, g = check_quant(x, None, gpu, "zeros")
+    assert g == 0.0 and (sc == 0).all()
+
+
+def test_exact_ties(gpu):
+    """Blocks whose elements sit exactly on E2M1 rounding midpoints: amax = 2.625 gives
+    g = 2^-10, the amax block gets S = 448 and unit 0.4375; every other element is
+    mid * 0.4375 for a midpoint mid (all representable in bf16)."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    rows, k = 64, 256
+    x = np.zeros((rows, k), dtype=np.float32)
+    rng = np.random.default_rng(0)
+    for r in range(rows):
+        for b in range(k // 16):
+            blk = [6.0 * 0.4375] + [mids[int(i)] * 0.4375 for i in rng.integers(0, 7, 15)]
+            blk = np.array(blk) * np.where(rng.random(16) < 0.5, -1.0, 1.0)
+            x[r, b * 16:(b + 1) * 16] = blk
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    assert ((bits.astype(np.uint32) << 16).view(np.float32) == x).all()
+    qd, sc, g = check_quant(bits, None, gpu, "exact ties")
+    assert g == 2.0 ** -10
+
+
+def test_subnormal_products_and_tiny_tensor(gpu):
+    """silu(gate) * up below 2^-126 (rounded once from the exact product), inside a
+    normal tensor and in a tensor whose absmax itself is subnormal."""
+    m, k = 64, 256
+    rng = np.random.default_rng(1)
+    gate = synth.normal_bf16(m, k, seed=9, tag=1, sigma=1.0)
+    up = synth.normal_bf16(m, k, seed=9, tag=2, sigma=1.0)
+    # silu(-90) ~ -7.4e-38; times small up values gives fp32 subnormal products
+    sel = rng.random((m, k)) < 0.3
+    gate[sel] = 0xC2B4  # -90
+    up[sel] = (rng.integers(0x3A00, 0x3C80, size=sel.sum())).astype(np.uint16)
+    check_quant(gate, up, gpu, "subnormal products in a normal tensor")
+    gate2 = np.full((m, k), 0xC2B4, dtype=np.uint16)
+    up2 = (rng.integers(0x3800, 0x3C00, size=(m, k))).astype(np.uint16)
+    check_quant(gate2, up2, gpu, "all products subnormal")
+
+
+def test_extreme_magnitudes_plain(gpu):
+    """Plain quantization across the bf16 range: subnormal block scales, huge amax."""
+    m, k = 128, 512
+    rng = np.random.default_rng(2)
+    x = synth.normal_bf16(m, k, seed=11, tag=4, sigma=1.0)
+    x[0, 0] = 0x7F7F  # bf16 max
+    x[5, 17] = 0x0001  # smallest subnormal
+    x[9, :64] = 0x3F80
+    check_quant(x, None, gpu, "bf16 max amax")
+    y = synth.normal_bf16(m, k, seed=12, tag=4, sigma=1e-3)
+    y[3, 3] = 0x4528  # 2688
+    check_quant(y, None, gpu, "subnormal block scales")
+
+
+def test_workspace_reuse_and_determinism(gpu):
+    """Back-to-back calls on one workspace give identical bytes (the kernel returns the
+    workspace to zero), and the workspace is zero afterwards."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    w = synth.TINY
+    gate, up = w.activations()
+    g_t, u_t = parity.to_device_bf16(gate, gpu), parity.to_device_bf16(up, gpu)
+    ws = torch.zeros(nv.nvfp4_quantize_workspace_bytes(), dtype=torch.uint8, device=gpu)
+    outs = [nv.nvfp4_quantize_swiglu(g_t, u_t, workspace=ws) for _ in range(3)]
+    x_t = parity.to_device_bf16(w.weight(), gpu)
+    wq = nv.nvfp4_quantize(x_t, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.sum().item()) == 0
+    for o in outs[1:]:
+        assert torch.equal(o.qdata, outs[0].qdata) and torch.equal(o.scales, outs[0].scales)
+        assert torch.equal(o.global_scale, outs[0].global_scale)
+    rq, rs, rg = oracle.quantize(w.weight())
+    assert (wq.qdata.cpu().numpy() == rq).all() and float(wq.global_scale.item()) == rg
+
+
+@pytest.mark.parametrize("name", ["mid_fc2_slice", "qkv", "attn_out", "fc1"])
+def test_large_configs(gpu, name):
+    w = synth.BY_NAME[name]
+    acts = w.activations()
+    check_quant(acts[0], acts[1] if w.swiglu else None, gpu, name)
+
+
+def test_canonical_fc2(gpu):
+    w = synth.FC2
+    gate, up = w.activations()
+    qd, sc, g = check_quant(gate, up, gpu, "canonical fc2")
+    assert qd.shape == (37824, 7168) and sc.size == 37888 * 896
+    assert (qd[37810:] == 0).all()
+
+
+@pytest.mark.parametrize("m", synth.RAGGED_M)
+def test_ragged_m(gpu, m):
+    w = [r for r in synth.RAGGED if r.m == m][0]
+    gate, up = w.activations()
+    check_quant(gate, up, gpu, w.name)

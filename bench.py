@@ -79,6 +79,40 @@ def cpu_baseline(w, threads: int) -> dict:
     }
 
 
+def only_gemm(w, args, dev) -> int:
+    """GEMM-only timing on seeded random operand bytes: QDATA uniform over all 256 byte
+    values, scale bytes uniform in [0x30, 0x47] (0.5 .. 15), global scales 1."""
+    import statistics
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    import synth
+    tensors = []
+    for rows, tag in ((w.m, 101), (w.n, 102)):
+        t = nv.empty_nvfp4(rows, w.k, dev)
+        t.qdata.copy_(torch.from_numpy(synth.uniform_bytes(t.qdata.numel(), w.seed, tag)).view(t.qdata.shape))
+        t.scales.copy_(torch.from_numpy(synth.uniform_bytes(t.scales.numel(), w.seed, tag + 10, 0x30, 0x47)))
+        t.global_scale.fill_(1.0)
+        tensors.append(t)
+    a, wq = tensors
+    d = torch.empty((w.m_pad, w.n), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        nv.nvfp4_gemm_bf16out(a, wq, out=d)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record(stream)
+        nv.nvfp4_gemm_bf16out(a, wq, out=d)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    t_gemm = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs)
+    tflops = w.gemm_flops / (t_gemm * 1e-3) / 1e12
+    print(json.dumps({"mode": "only-gemm (random operand bytes)", "workload": w.name, "gemm_ms": round(t_gemm, 4),
+                      "tflops": round(tflops, 2), "frac_of_peak": round(tflops / PEAK_MFMA_TFLOPS, 4),
+                      "steps": args.steps}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,6 +120,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fc2_canonical")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-gemm", action="store_true",
+                    help="time the GEMM alone on seeded random NVFP4 operand bytes (no producer launch in "
+                         "the process; used for profiler counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path is single-GPU; see DESIGN.md for how it "
@@ -102,6 +139,9 @@ def main() -> int:
     torch.cuda.set_device(dev)
     nv.nvfp4_init()
 
+    if args.only_gemm:
+        return only_gemm(w, args, dev)
+
     t0 = time.perf_counter()
     acts = w.activations()
     W = w.weight()
@@ -117,7 +157,8 @@ def main() -> int:
 
     stream = torch.cuda.current_stream()
 
-    # weight quantization: once, outside the step
+    # weight quantization: once, outside the step (first call warms the kernel)
+    nv.nvfp4_quantize(wt, out=wq)
     ev_w0, ev_w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev_w0.record(stream)
     nv.nvfp4_quantize(wt, out=wq)

@@ -11,7 +11,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "../../include/nvfp4.h"
+#include "nvfp4.h"
 #include "common.hpp"
 
 namespace nvfp4 {

@@ -16,14 +16,24 @@
 // The exact fp16 operands feed v_mfma_f32_32x32x16_f16 with fp32 accumulation;
 // the epilogue multiplies by g_a * g_w in fp32 and rounds to bf16 once.
 //
-// Tiling: a 256 x 256 output tile per workgroup of 4 waves (2 x 2), each wave
-// 128 x 128 (4 x 4 MFMA tiles of 32 x 32, accumulators in AGPRs). K advances 128
-// per step; the packed operands (64 bytes per row) and their four 512-byte scale
-// tiles per operand are staged through double-buffered LDS. Within a K step the
-// lane's k-half h covers k in [64h, 64h + 64), eight consecutive k per MFMA, the
-// same assignment for both operands, so every lane reads 32 contiguous code bytes
-// and one scale dword per 32-row fragment. Global loads are buffer loads whose
-// range check returns zero past the end of A (rows >= m_padded) or W (rows >= n).
+// Tiling: a 256 x 256 output tile per workgroup of 4 waves (2 x 2), one wave per
+// SIMD, each wave 128 x 128 (4 x 4 MFMA tiles of 32 x 32, accumulators in the 256
+// AGPRs). A square wave tile needs the fewest dequantized fragments per MFMA: one
+// K16 step converts 8 fragments for 16 MFMAs, i.e. two conversions and two packed
+// multiplies per MFMA, which co-issue with the matrix pipe.
+//
+// Pipeline: K advances 128 per step. The packed operands (64 bytes per row) and
+// two 512-byte scale tiles per 128 rows are moved global -> LDS by direct-to-LDS
+// buffer loads (no VGPR staging) into a 3-stage ring, two K steps ahead; each
+// wave's nine loads of a step are spread over its first K16 steps so that they
+// issue between MFMAs. Rows of a stage are stored with an XOR swizzle of their
+// four 16-byte chunks, so the fragment reads hit distinct LDS banks. Within a K
+// step the lane's k-half h covers k in [64h, 64h + 64), eight consecutive k per
+// MFMA, the same assignment for both operands. The K loop body is branch-free
+// (the last two steps are peeled) so the scheduler can interleave the next K16
+// step's conversions, the LDS reads and the loads with the MFMAs. Buffer range
+// checks return zero past the end of A (rows >= m_padded) or W (rows >= n), and
+// past K for the upper half of a final 64-wide K step.
 //
 // Traversal: tiles are numbered m-band-major in bands of 8 M-tiles, and workgroup
 // ids (dispatched round-robin over the 8 XCDs) are remapped so that each XCD owns
@@ -33,13 +43,28 @@
 
 namespace nvfp4 {
 
-constexpr int kTM = 256, kTN = 256, kTK = 128;
-constexpr int kGemmThreads = 256;
-constexpr int kRowStride = 80;                   // LDS bytes per staged row (64 data + 16 pad)
-constexpr int kCodesBytes = 256 * kRowStride;    // one operand's codes per stage
-constexpr int kScaleBytes = 2048;                // one operand's 4 scale tiles per stage
-constexpr int kStageBytes = 2 * kCodesBytes + 2 * kScaleBytes;
+// Workgroup tile kTM x kTN = (WAVES_M * FM * 32) x (WAVES_N * FN * 32); each wave owns
+// FM x FN MFMA tiles of 32 x 32 with its accumulators in AGPRs, one wave per SIMD.
+constexpr int WAVES_M = 2, WAVES_N = 2, FM = 4, FN = 4;
+constexpr int kTM = WAVES_M * FM * 32, kTN = WAVES_N * FN * 32, kTK = 128;
+constexpr int kWaves = WAVES_M * WAVES_N;
+constexpr int kGemmThreads = 64 * kWaves;
+constexpr int kStages = 3;                       // LDS stages (loads run two K steps ahead)
+constexpr int kCodesA = kTM * 64;                // A codes per stage: 64 bytes per row
+constexpr int kCodesW = kTN * 64;
+constexpr int kScaleA = kTM / 128 * 1024;        // A scale tiles per stage (2 column groups)
+constexpr int kScaleW = kTN / 128 * 1024;
+constexpr int kStageBytes = kCodesA + kCodesW + kScaleA + kScaleW;
 constexpr int kBandM = 8;                        // M-tiles per traversal band
+// one wave-wide direct-to-LDS load moves 1 KiB: 16 rows of codes or one 1 KiB scale block
+constexpr int kWaveLoadsA = kCodesA / 1024, kWaveLoadsW = kCodesW / 1024;
+constexpr int kWaveLoadsS = (kScaleA + kScaleW) / 1024;
+constexpr int kLoadsPerWave = (kWaveLoadsA + kWaveLoadsW + kWaveLoadsS) / kWaves;
+static_assert((kWaveLoadsA + kWaveLoadsW + kWaveLoadsS) % kWaves == 0, "even load split");
+static_assert(kWaveLoadsA % kWaves == 0 && kWaveLoadsW % kWaves == 0 && kWaveLoadsS == kWaves,
+              "each wave issues the same mix of loads");
+static_assert(kTM % 128 == 0 && kTN % 128 == 0, "tiles cover whole 128-row scale tiles");
+static_assert(kLoadsPerWave <= 15, "vmcnt immediate");
 
 struct GemmArgs {
   const uint8_t* aq;
@@ -56,9 +81,12 @@ struct GemmArgs {
   int ksteps;
 };
 
-__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Position of 16-byte chunk c of code row r inside that row's 64 LDS bytes. The
+// XOR spreads the rows a fragment read touches (32 consecutive rows, one chunk
+// each) over distinct banks for both 32- and 64-bank LDS.
+__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
 
 template <int SEL>
 __device__ __forceinline__ f16x2_t dq2(uint32_t codes, f16x2_t sv) {
@@ -74,13 +102,67 @@ __device__ __forceinline__ f16x8_t dequant8(uint32_t codes, f16x2_t sv) {
   return r;
 }
 
+// Dequantize the FM + FN fragments of one K16 step into (fa, fw). The half-rate
+// conversions are issued in place, each multiply trails its conversion by four
+// pairs, so no instruction waits on the one just before it.
+template <int FM_, int FN_>
+__device__ __forceinline__ void dequant_step(f16x8_t (&fa)[FM_], f16x8_t (&fw)[FN_], const uint32_t (&codes)[FM_ + FN_],
+                                             const f16x2_t (&sv)[FM_ + FN_]) {
+  constexpr int NP = (FM_ + FN_) * 4;  // pairs
+  constexpr int LAG = 4;
+#pragma unroll
+  for (int q = 0; q < NP + LAG; ++q) {
+    if (q < NP) {
+      const int f = q / 4, e = q % 4;
+      f16x2_t v;
+      switch (e) {
+        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[f], 256.0f, 0); break;
+        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[f], 256.0f, 1); break;
+        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[f], 256.0f, 2); break;
+        default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[f], 256.0f, 3); break;
+      }
+      if (f < FM_) { fa[f][2 * e] = v[0]; fa[f][2 * e + 1] = v[1]; }
+      else { fw[f - FM_][2 * e] = v[0]; fw[f - FM_][2 * e + 1] = v[1]; }
+    }
+    if (q >= LAG) {
+      const int p = q - LAG, f = p / 4, e = p % 4;
+      f16x2_t v;
+      if (f < FM_) { v[0] = fa[f][2 * e]; v[1] = fa[f][2 * e + 1]; }
+      else { v[0] = fw[f - FM_][2 * e]; v[1] = fw[f - FM_][2 * e + 1]; }
+      v = v * sv[f];
+      if (f < FM_) { fa[f][2 * e] = v[0]; fa[f][2 * e + 1] = v[1]; }
+      else { fw[f - FM_][2 * e] = v[0]; fw[f - FM_][2 * e + 1] = v[1]; }
+    }
+  }
+}
+
 // fp16 pair (v(S) * 2^-8, v(S) * 2^-8) for scale byte b of a scale dword
 __device__ __forceinline__ f16x2_t scale_pair(uint32_t sdw, int b) {
-  uint32_t h = ((sdw >> (8 * b)) & 0xFFu) << 7;
-  uint32_t u = h | (h << 16);
+  // (S << 7) | (S << 23) == S * 0x800080 for S < 256: one byte-select multiply
+  uint32_t u = ((sdw >> (8 * b)) & 0xFFu) * 0x800080u;
   f16x2_t r;
   __builtin_memcpy(&r, &u, 4);
   return r;
+}
+
+// Scheduling hints: in each K16 step, interleave one MFMA with five VALU
+// instructions (the next step's dequantization and scale pairs).
+__device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+  for (int i = 0; i < FM * FN; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+  }
+}
+
+// Workgroup barrier for the LDS pipeline. Every wave has already waited for its
+// own outstanding LDS reads and direct-to-LDS loads (explicit counters), so only
+// the s_barrier is needed; the empty asm keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
@@ -102,8 +184,9 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
   const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int lr = lane & 31, h = lane >> 5;
 
   __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)a.aq, 0, a.a_qbytes, 0x00020000);
@@ -111,114 +194,182 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
   __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)a.as, 0, a.a_sbytes, 0x00020000);
   __amdgpu_buffer_rsrc_t rSW = __builtin_amdgcn_make_buffer_rsrc((void*)a.ws, 0, a.w_sbytes, 0x00020000);
   const int krow = (int)(a.k / 2);
+  constexpr int kOutOfRange = 0x7FFFFFF0;  // reads past a buffer's range return zero
 
-  // ---- global -> register prefetch of one K step ----
-  // codes: 1024 chunks of 16 bytes per operand, 4 per thread: chunk c -> row c/4, part c%4
-  // scales: threads 0..127 load A's 4 tiles, 128..255 W's (16 bytes each)
-  u32x4_t pa[4], pw[4], ps;
-  auto prefetch = [&](int ks) {
-    const bool half = (int64_t)(ks + 1) * kTK > a.k;  // only k-half 0 is inside K
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * kGemmThreads;
-      const int row = c >> 2, part = c & 3;
-      const bool ok = !(half && part >= 2);
-      const int offa = (int)((m0 + row) * krow) + ks * 64 + part * 16;
-      const int offw = (int)((n0 + row) * krow) + ks * 64 + part * 16;
-      u32x4_t z = {0u, 0u, 0u, 0u};
-      pa[i] = ok ? buf_load16(rA, offa) : z;
-      pw[i] = ok ? buf_load16(rW, offw) : z;
-    }
-    {
-      const int c = tid & 127;
-      const int rt = c >> 6, cg = (c >> 5) & 1, part = c & 31;
-      const bool ok = !(half && cg == 1);
-      const int64_t rt_g = (tid < 128 ? m0 : n0) / 128 + rt;
-      const int off = (int)((rt_g * a.cgroups + (int64_t)ks * 2 + cg) * 512) + part * 16;
-      u32x4_t z = {0u, 0u, 0u, 0u};
-      ps = ok ? buf_load16(tid < 128 ? rSA : rSW, off) : z;
+  // ---- direct-to-LDS loads of one K step into a stage ----
+  // Code wave-load j covers rows 16j .. 16j+15; lane L writes LDS bytes 16L..16L+15 of
+  // that 1 KiB, i.e. row 16j + L/4 at chunk position L%4, which holds global chunk
+  // chunk_pos(row, L%4) (the XOR is an involution). Scale wave-load q covers row
+  // tile q%2 of A (q < 2) or W (q >= 2): its two 512-byte column-group tiles.
+  // Load idx (0..kLoadsPerWave-1) of this wave's share of K step ks: idx < 4 are A code
+  // wave-loads, 4..7 W code wave-loads, 8 the scale block. Half K steps (K % 128 == 64)
+  // send the upper k-half past the buffer range, where reads return zero.
+  auto issue_one = [&](int ks, int stage, int idx) {
+    const int oor = ((int64_t)(ks + 1) * kTK > a.k) ? 0x7FFFFFF0 : 0;  // wave-uniform
+    unsigned char* st = smem + stage * kStageBytes;
+    const int rsub = lane >> 2, p = lane & 3;
+    if (idx < 2 * (kWaveLoadsA / kWaves)) {
+      const bool isA = idx < kWaveLoadsA / kWaves;
+      const int j = wave + (isA ? idx : idx - kWaveLoadsA / kWaves) * kWaves;
+      const int row = j * 16 + rsub;
+      const int c = chunk_pos(row, p);
+      const int off = ((int)(((isA ? m0 : n0) + row) * krow) + ks * 64 + c * 16) | (c >= 2 ? oor : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rW, (lds_void*)(st + (isA ? 0 : kCodesA) + j * 1024), 16, off,
+                                               0, 0, 0);
+    } else {
+      const int q = wave;  // kWaveLoadsS == kWaves
+      const bool isA = q < kScaleA / 1024;
+      const int rt = isA ? q : q - kScaleA / 1024;
+      const int64_t rt_g = (isA ? m0 : n0) / 128 + rt;
+      const int cg = lane >> 5;
+      const int off = ((int)((rt_g * a.cgroups + (int64_t)ks * 2) * 512) + lane * 16) | (cg == 1 ? oor : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rSA : rSW, (lds_void*)(st + kCodesA + kCodesW + q * 1024), 16,
+                                               off, 0, 0, 0);
     }
   };
-  auto stash = [&](int buf) {
-    unsigned char* st = smem + buf * kStageBytes;
+
+  // ---- per-wave views of a stage ----
+  const int rowA = wm * FM * 32 + lr, rowW = wn * FN * 32 + lr;
+  auto read_codes = [&](int stage, int kq, u32x4_t (&ca)[FM], u32x4_t (&cw)[FN]) {
+    const unsigned char* st = smem + stage * kStageBytes;
+    const int c = h * 2 + kq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * kGemmThreads;
-      const int row = c >> 2, part = c & 3;
-      *(u32x4_t*)(st + row * kRowStride + part * 16) = pa[i];
-      *(u32x4_t*)(st + kCodesBytes + row * kRowStride + part * 16) = pw[i];
+    for (int i = 0; i < FM; ++i) {
+      const int r = rowA + i * 32;
+      ca[i] = *(const u32x4_t*)(st + r * 64 + chunk_pos(r, c) * 16);
     }
-    const int c = tid & 127;
-    *(u32x4_t*)(st + 2 * kCodesBytes + (tid < 128 ? 0 : kScaleBytes) + c * 16) = ps;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = rowW + j * 32;
+      cw[j] = *(const u32x4_t*)(st + kCodesA + r * 64 + chunk_pos(r, c) * 16);
+    }
+  };
+  // scale dwords (the four blocks of this lane's k-half), one per fragment
+  auto read_scales = [&](int stage, uint32_t (&sa)[FM], uint32_t (&sw)[FN]) {
+    const unsigned char* ss = smem + stage * kStageBytes + kCodesA + kCodesW;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * FM * 32 + i * 32;
+      sa[i] = *(const uint32_t*)(ss + ((r >> 7) * 2 + h) * 512 + lr * 16 + ((r >> 5) & 3) * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * FN * 32 + j * 32;
+      sw[j] = *(const uint32_t*)(ss + kScaleA + ((r >> 7) * 2 + h) * 512 + lr * 16 + ((r >> 5) & 3) * 4);
+    }
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[FN][FM];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < FN; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-  prefetch(0);
-  stash(0);
-  __syncthreads();
-
-  for (int ks = 0; ks < a.ksteps; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < a.ksteps) prefetch(ks + 1);
-    const unsigned char* st = smem + buf * kStageBytes;
-    const unsigned char* stA = st;
-    const unsigned char* stW = st + kCodesBytes;
-    const unsigned char* ssA = st + 2 * kCodesBytes;
-    const unsigned char* ssW = ssA + kScaleBytes;
-
-    // scales: one dword per fragment (4 blocks of this lane's k-half)
-    uint32_t sa[4], sw[4];
+  // Software pipeline. K step ks lives in LDS stage ks % 3, loaded two K steps
+  // ahead; the loads of step ks + 2 are spread over K16 steps 0..4 of step ks so
+  // that they issue between MFMAs. Within a K step, K16 step kk (0..7) uses codes
+  // of half kk / 4, dword kk % 4, and scale block kk / 2. While the MFMAs of step kk
+  // run, the fragments of step kk + 1 are dequantized into the other register set.
+  // The second-half codes are read at kk = 1. At kk = 6 every wave waits for its
+  // own loads of the next K step, the workgroup synchronises (which also frees the
+  // stage read in the previous K step for the next loads), and the next step's
+  // scales and first-half codes are read; they are dequantized at kk = 7. The body
+  // is instantiated without branches: the last two K steps are peeled.
+  const int nks = a.ksteps;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = *(const uint32_t*)(ssA + (wm * 2 + h) * 512 + lr * 16 + i * 4);
-      sw[i] = *(const uint32_t*)(ssW + (wn * 2 + h) * 512 + lr * 16 + i * 4);
-    }
+  for (int idx = 0; idx < kLoadsPerWave; ++idx) issue_one(0, 0, idx);
+  if (nks > 1) {
 #pragma unroll
-    for (int kq = 0; kq < 2; ++kq) {
-      u32x4_t ca[4], cw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ca[i] = *(const u32x4_t*)(stA + (wm * 128 + i * 32 + lr) * kRowStride + h * 32 + kq * 16);
-        cw[i] = *(const u32x4_t*)(stW + (wn * 128 + i * 32 + lr) * kRowStride + h * 32 + kq * 16);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int blk = kq * 2 + (kk >> 1);
-        f16x8_t fa[4], fw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          fa[i] = dequant8(ca[i][kk], scale_pair(sa[i], blk));
-          fw[i] = dequant8(cw[i][kk], scale_pair(sw[i], blk));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fw[j], fa[i], acc[j][i], 0, 0, 0);
-      }
-    }
-    if (ks + 1 < a.ksteps) stash(buf ^ 1);
-    __syncthreads();
+    for (int idx = 0; idx < kLoadsPerWave; ++idx) issue_one(1, 1, idx);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerWave);  // vmcnt(kLoadsPerWave): step 0 has landed
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
+  stage_barrier();
+
+  u32x4_t ca[2][FM], cw[2][FN];
+  uint32_t sa[FM], sw[FN], nsa[FM], nsw[FN];
+  f16x8_t fa[2][FM], fw[2][FN];
+  // dequantize K16 step k (0..7) of the codes and scales in registers into set `set`
+  auto dequant_k = [&](int k, int set) __attribute__((always_inline)) {
+    uint32_t cd[FM + FN];
+    f16x2_t sv[FM + FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) { cd[i] = ca[k >> 2][i][k & 3]; sv[i] = scale_pair(sa[i], k >> 1); }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) { cd[FM + j] = cw[k >> 2][j][k & 3]; sv[FM + j] = scale_pair(sw[j], k >> 1); }
+    dequant_step(fa[set], fw[set], cd, sv);
+  };
+  read_scales(0, sa, sw);
+  read_codes(0, 0, ca[0], cw[0]);
+  dequant_k(0, 0);
+
+  // one K step; `loads`: issue the loads of step ks + 2; `next`: a step ks + 1 follows
+  auto kstep = [&](int ks, int stage, bool loads, bool next) __attribute__((always_inline)) {
+    const int next_stage = stage == 2 ? 0 : stage + 1;
+    const int far_stage = next_stage == 2 ? 0 : next_stage + 1;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (loads && kk < 5) {
+        issue_one(ks + 2, far_stage, 2 * kk);
+        if (kk < 4) issue_one(ks + 2, far_stage, 2 * kk + 1);
+      }
+      if (kk == 1) read_codes(stage, 1, ca[1], cw[1]);  // second half, needed from step 4
+      if (kk == 6 && next) {
+        // kept in place: the reads must follow the barrier and lead their use by a
+        // whole MFMA group
+        __builtin_amdgcn_sched_barrier(0);
+        if (loads) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerWave);  // this step's batch may fly
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        stage_barrier();
+        read_scales(next_stage, nsa, nsw);
+        read_codes(next_stage, 0, ca[0], cw[0]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kk < 7) {
+        dequant_k(kk + 1, nxt);
+      } else if (next) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) sa[i] = nsa[i];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) sw[j] = nsw[j];
+        dequant_k(0, nxt);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fw[cur][j], fa[cur][i], acc[j][i], 0, 0, 0);
+      interleave_hint();
+    }
+  };
+
+  int stage = 0, ks = 0;
+  for (; ks + 2 < nks; ++ks) {
+    kstep(ks, stage, true, true);
+    stage = stage == 2 ? 0 : stage + 1;
+  }
+  if (ks + 1 < nks) {
+    kstep(ks, stage, false, true);
+    stage = stage == 2 ? 0 : stage + 1;
+    ++ks;
+  }
+  kstep(ks, stage, false, false);
 
   // ---- epilogue: D[m, n] = RN_bf16(alpha * acc), alpha = g_a * g_w ----
   const float alpha = (*a.ga) * (*a.gw);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < FN; ++j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + wm * 128 + i * 32 + lr;
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + wm * FM * 32 + i * 32 + lr;
       if (m >= a.m_pad) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * 128 + j * 32 + q * 8 + h * 4;
+        const int64_t n = n0 + wn * FN * 32 + j * 32 + q * 8 + h * 4;
         if (n >= a.n) continue;
         bf16x2_t lo, hi;
         lo[0] = (__bf16)(acc[j][i][q * 4 + 0] * alpha);
@@ -238,7 +389,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
 
 // ---- host side -----------------------------------------------------------------------------
 
-size_t gemm_smem_bytes() { return 2 * (size_t)kStageBytes; }
+size_t gemm_smem_bytes() { return (size_t)kStages * kStageBytes; }
 const void* gemm_kernel_ptr() { return (const void*)gemm_kernel; }
 
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,

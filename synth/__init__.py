@@ -55,6 +55,9 @@ def _load():
     lib.synth_normal_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint64,
                                       ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
+    lib.synth_bytes.restype = ctypes.c_int
+    lib.synth_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint64,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -89,6 +92,16 @@ def normal_bf16(rows: int, cols: int, seed: int, tag: int, sigma: float,
                                    threads or default_threads())
     if rc != 0:
         raise ValueError(f"synth_normal_bf16 failed ({rc})")
+    return out
+
+
+def uniform_bytes(n: int, seed: int, tag: int, lo: int = 0, hi: int = 255,
+                  threads: Optional[int] = None) -> np.ndarray:
+    """n seeded uniform bytes in [lo, hi]."""
+    out = np.empty(n, dtype=np.uint8)
+    rc = _load().synth_bytes(out.ctypes.data, n, seed, tag, lo, hi, threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"synth_bytes failed ({rc})")
     return out
 
 

@@ -119,3 +119,17 @@ int synth_normal_bf16(uint16_t* out, int64_t rows, int64_t cols, int64_t ld, uin
   }
   return 0;
 }
+
+/*
+ * out[i] for i < n: seeded uniform bytes in [lo, hi] (inclusive), byte i from
+ * draw(key(seed, tag), i). Used for synthetic packed operands.
+ */
+int synth_bytes(uint8_t* out, int64_t n, uint64_t seed, uint64_t tag, int lo, int hi, int nthreads) {
+  if (!out || n < 0 || lo < 0 || hi > 255 || lo > hi) return -1;
+  const uint64_t key = stream_key(seed, tag);
+  const uint64_t span = (uint64_t)(hi - lo + 1);
+  (void)nthreads;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)(lo + (int)(draw(key, (uint64_t)i) % span));
+  return 0;
+}

@@ -107,9 +107,28 @@ def only_gemm(w, args, dev) -> int:
     torch.cuda.synchronize()
     t_gemm = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs)
     tflops = w.gemm_flops / (t_gemm * 1e-3) / 1e12
-    print(json.dumps({"mode": "only-gemm (random operand bytes)", "workload": w.name, "gemm_ms": round(t_gemm, 4),
-                      "tflops": round(tflops, 2), "frac_of_peak": round(tflops / PEAK_MFMA_TFLOPS, 4),
-                      "steps": args.steps}), flush=True)
+    out = {"mode": "only-gemm (random operand bytes)", "workload": w.name, "gemm_ms": round(t_gemm, 4),
+           "tflops": round(tflops, 2), "frac_of_peak": round(tflops / PEAK_MFMA_TFLOPS, 4), "steps": args.steps,
+           "gemm_distinct_bytes": gemm_bytes(w.m, w.n, w.k)}
+    if args.copy_bytes > 0:
+        # calibration for the profiler's byte counters: a plain elementwise pass that
+        # reads copy_bytes and writes copy_bytes (int32 x | 0), launched `steps` times
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.bitwise_or(src, 0, out=dst)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(args.steps):
+            torch.bitwise_or(src, 0, out=dst)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        t_copy = c0.elapsed_time(c1) / args.steps
+        out["copy_bytes"] = 4 * n
+        out["copy_ms"] = round(t_copy, 4)
+        out["copy_gbs"] = round(2 * 4 * n / (t_copy * 1e-3) / 1e9, 1)
+    print(json.dumps(out), flush=True)
     return 0
 
 
@@ -123,6 +142,9 @@ def main() -> int:
     ap.add_argument("--only-gemm", action="store_true",
                     help="time the GEMM alone on seeded random NVFP4 operand bytes (no producer launch in "
                          "the process; used for profiler counter runs)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="with --only-gemm: also run a plain elementwise copy of this many bytes (read + "
+                         "write), the calibration kernel for the profiler's FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path is single-GPU; see DESIGN.md for how it "

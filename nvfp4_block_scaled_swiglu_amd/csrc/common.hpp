@@ -22,9 +22,10 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 // Workspace of the producer: the tensor absmax (fp32 bits of a non-negative
 // bf16 value, so unsigned order is value order) and the grid-barrier counters.
 // All three are zero between calls.
+// Producer workspace: zero between calls (each launch returns it to zero).
 struct ProducerWorkspace {
-  uint32_t amax_bits;
-  uint32_t arrived;
+  uint32_t amax_bits;  // max |y| (fp32 bits) over the grid
+  uint32_t arrived;    // grid barrier after pass 1
   uint32_t departed;
   uint32_t pad[61];
 };
@@ -57,7 +58,7 @@ __device__ __forceinline__ uint32_t rn_bf16_from_double(double v) {
   int ex = ((int)((u >> 52) & 0x7FF)) - 1023;  // a >= 2^-1022 for every product here
   int lead = ex < -126 ? -126 : ex;
   double q = ldexp(1.0, lead - 7);
-  double n = rint(a / q);                         // exact division; rint is ties-to-even
+  double n = rint(a * ldexp(1.0, 7 - lead));      // exact scaling; rint is ties-to-even
   double r = n * q;
   if (r >= 0x1p128) return sign | 0x7F80u;
   return sign | (__float_as_uint((float)r) >> 16);  // r has <= 8 significant bits: exact

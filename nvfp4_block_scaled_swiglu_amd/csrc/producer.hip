@@ -14,19 +14,25 @@
 //   QDATA   = two codes per byte (even element low), rows [m, m_pad) zero
 //   scales  = 512-byte tiles of 128 rows x 4 scale columns, padding zero
 //
-// Structure: a persistent grid (co-resident through a cooperative launch) walks
-// work items of 128 rows x 256 columns. Pass 1 reduces |y| (wavefront shuffles,
-// LDS across waves, one agent-scope atomic max per workgroup); a grid barrier
-// publishes amax; pass 2 walks the items in reverse order (so the rows read
-// last in pass 1, still in the memory-side cache, are read first), recomputes y,
-// and writes coalesced QDATA rows (each wave instruction stores 2 full 128-byte
-// rows) and whole 512-byte scale tiles staged in LDS.
+// Structure: a persistent grid (co-resident through a cooperative launch, one
+// 16-wave workgroup per CU, the bf16 SiLU table in LDS) walks work items of 128 rows
+// x 256 columns; each lane owns one 16-element block of a row per step (a wave
+// covers 4 rows x 16 blocks). Pass 1 reduces |y| with the next item's loads in
+// flight (wavefront shuffles, LDS across waves, one agent-scope atomic max per
+// workgroup); a grid barrier publishes amax; pass 2 walks the items in reverse order
+// (so the rows read last in pass 1, still in the memory-side cache, are read first),
+// recomputes y, and stores QDATA rows (16 lanes store one full 128-byte row segment)
+// and each scale byte at its place in its 512-byte tile. Pass 2 has no workgroup
+// barrier, so the 16 waves drift apart and hide each other's load latency; each
+// tile's bytes all come from the one workgroup that owns its item.
 //
 // Exactness: every rounding decision equals the exact one.
-//  - y: a product of two bf16 values is exact in fp32 when it is >= 2^-126; smaller
-//    (or zero) products are recomputed in fp64 and rounded once.
-//  - S: an fp64 estimate adjusted by exact fp64 compares (v(e) * 6g has <= 30
-//    significant bits).
+//  - y: a product of two bf16 values is exact in fp32 when it is >= 2^-126; a block
+//    with some |y| <= 2^-126 (or zero) has its nonzero subnormal products
+//    recomputed in fp64 and rounded once.
+//  - S: read off the bits of an fp32 estimate of bmax / 6g (relative error below
+//    2^-22); estimates within 2^-17 of a grid point are settled by exact fp64
+//    compares (v(e) * 6g has <= 30 significant bits).
 //  - codes: the hardware fp32 -> E2M1 conversion (round to nearest even) is applied
 //    to |y| * r_lo and |y| * r_hi, two brackets of the exact quotient built from a
 //    1-ulp reciprocal with a 2^-20 margin; when the two codes agree the exact code
@@ -36,11 +42,13 @@
 
 namespace nvfp4 {
 
-constexpr int kProdThreads = 512;  // 8 waves
-constexpr int kItemRows = 128;     // one scale row-tile
-constexpr int kItemCols = 256;     // one 128-byte QDATA segment per row
-constexpr int kSteps = 8;          // 128 rows / (8 waves * 2 rows per wave-step)
-constexpr int kStagingBytes = 2048;  // four 512-byte scale tiles
+constexpr int kProdThreads = 1024;   // 16 waves, four per SIMD
+constexpr int kWaves = kProdThreads / 64;
+constexpr int kItemRows = 128;       // one scale row-tile
+constexpr int kItemCols = 256;       // 16 blocks of 16 columns: one 128-byte QDATA segment per row
+constexpr int kRowsPerStep = kWaves * 4;  // lane = (row of 4) x (block of 16)
+constexpr int kRedBytes = 128;       // wave maxima and two broadcast slots
+constexpr int kSteps = kItemRows / kRowsPerStep;
 
 struct ProducerArgs {
   const uint16_t* x;  // gate (SwiGLU) or x (plain)
@@ -91,25 +99,41 @@ __device__ __forceinline__ float global_scale_from_amax(float amax) {
   return g;
 }
 
-// smallest UE4M3 byte e with v(e) * g6 >= bmax (g6 = 6 g, exact in fp64); bmax > 0
-__device__ __forceinline__ uint32_t block_scale_byte(float bmax, double g6) {
-  double b = (double)bmax;
-  double r = b / g6;
-  int e;
-  if (r >= 0x1p-6) {
-    uint64_t u = (uint64_t)__double_as_longlong(r);
-    int E = (int)((u >> 52) & 0x7FF) - 1023 + 7;
-    if (E > 15) E = 15;
-    int mant = (int)((u >> 49) & 7u);
-    int rest = (u & ((1ull << 49) - 1)) != 0;
-    e = ((E << 3) | mant) + rest;
-  } else {
-    e = (int)ceil(r * 512.0);
-  }
+// Exact adjustment of a UE4M3 byte estimate e to the smallest e in [1, 126] with
+// v(e) * g6 >= b (g6 = 6 g; v(e) * g6 has at most 30 significant bits, exact in fp64).
+__device__ __noinline__ uint32_t block_scale_adjust(int e, double b, double g6) {
   e = e < 1 ? 1 : (e > 126 ? 126 : e);
   while (e < 126 && ue4m3_to_double((uint32_t)e) * g6 < b) ++e;
   while (e > 1 && ue4m3_to_double((uint32_t)(e - 1)) * g6 >= b) --e;
   return (uint32_t)e;
+}
+
+// Smallest UE4M3 byte e in [1, 126] with v(e) * 6g >= bmax (bmax > 0). q = bmax / (6g)
+// is formed in fp32 as (bmax * bscale) * inv_f, inv_f = RN(bscale^-1 / 6g), with a
+// relative error below 2^-22 whenever q is a normal number. The UE4M3 grid points are the fp32
+// values whose mantissa has only its top three bits set (normal range, q >= 2^-6) and
+// the multiples of 2^-9 below it, so the ceiling of q on the grid is read off q's
+// bits. When q lies within 2^-17 (relative) of a grid point, or outside the range
+// the method can produce, the estimate is settled by exact fp64 compares.
+__device__ __forceinline__ uint32_t block_scale_byte(float bmax, float bscale, float inv_f, double g6) {
+  const float q = (bmax * bscale) * inv_f;
+  int e;
+  bool near;
+  if (q >= 0x1p-6f) {
+    const uint32_t bits = __float_as_uint(q);
+    const uint32_t rest = bits & 0xFFFFFu;
+    // (biased exponent - 120) * 8 + top three mantissa bits, rounded up
+    e = (int)((bits + 0xFFFFFu) >> 20) - 960;
+    near = rest < 64u || rest > 0xFFFFFu - 64u || !(q < 0x1p+9f);
+  } else {
+    const float t = q * 512.0f;  // exact scaling: the grid points are the integers
+    const float fl = floorf(t);
+    e = (int)fl + 1;
+    const float fr = t - fl;     // exact
+    near = fr < 0x1p-16f || fr > 1.0f - 0x1p-16f;
+  }
+  if (near) return block_scale_adjust(e, (double)bmax, g6);
+  return (uint32_t)(e > 126 ? 126 : e);
 }
 
 // E2M1 codes (hardware round-to-nearest-even) of the bf16 pair yb scaled by the two
@@ -140,17 +164,83 @@ __device__ __noinline__ uint32_t e2m1_code_exact(uint32_t y16, uint32_t s, float
 
 // ---- the kernel ------------------------------------------------------------------------------
 
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// A nonzero product below 2^-126 may have been rounded in fp32: redo such products
+// exactly. (A product that rounds to zero in fp32 is below 2^-149 and rounds to a
+// zero of the same sign in bf16 as well.)
+struct Y8 {
+  uint32_t v[8];
+};
+__device__ __noinline__ Y8 block_y_fix(u32x4_t g0, u32x4_t g1, u32x4_t u0, u32x4_t u1, Y8 yb, const uint16_t* tab) {
+  for (int j = 0; j < 16; ++j) {
+    const u32x4_t& gq = j < 8 ? g0 : g1;
+    const u32x4_t& uq = j < 8 ? u0 : u1;
+    const uint32_t g16 = (gq[(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
+    const uint32_t u16 = (uq[(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
+    const float p = bf16_bits_to_float(tab[g16]) * bf16_bits_to_float(u16);
+    if (fabsf(p) < 0x1p-126f && p != 0.0f) {
+      const double pd = (double)bf16_bits_to_float(tab[g16]) * (double)bf16_bits_to_float(u16);
+      const uint32_t y = rn_bf16_from_double(pd);
+      const int sh = 16 * (j & 1);
+      yb.v[j >> 1] = (yb.v[j >> 1] & ~(0xFFFFu << sh)) | (y << sh);
+    }
+  }
+  return yb;
+}
+
+// y for the 16 elements of one block, as 8 packed bf16 pairs. Products are formed in
+// fp32 (exact whenever the result is a normal fp32 number); the caller detects blocks
+// that may hold a rounded subnormal product and repairs them with block_y_fix.
+template <bool SWIGLU>
+__device__ __forceinline__ void block_y(const u32x4_t (&gv)[2], const u32x4_t (&uv)[2], const uint16_t* tab,
+                                        uint32_t (&yb)[8]) {
+  if (SWIGLU) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t gw = gv[w >> 2][w & 3], uw = uv[w >> 2][w & 3];
+      const float p0 = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16) * __uint_as_float(uw << 16);
+      const float p1 = __uint_as_float((uint32_t)tab[gw >> 16] << 16) * __uint_as_float(uw & 0xFFFF0000u);
+      yb[w] = cvt_pk_bf16(p0, p1);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) yb[w] = gv[w >> 2][w & 3];
+  }
+}
+
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
+
+__device__ __forceinline__ u16x2_t as_u16x2(uint32_t v) {
+  u16x2_t r;
+  __builtin_memcpy(&r, &v, 4);
+  return r;
+}
+
+// largest and smallest bf16 magnitude (bits) among the 16 elements, packed 16-bit ops
+__device__ __forceinline__ void block_mag_range(const uint32_t (&yb)[8], uint32_t& mx, uint32_t& mn) {
+  u16x2_t hi = as_u16x2(yb[0] & 0x7FFF7FFFu), lo = hi;
+#pragma unroll
+  for (int w = 1; w < 8; ++w) {
+    const u16x2_t m = as_u16x2(yb[w] & 0x7FFF7FFFu);
+    hi = __builtin_elementwise_max(hi, m);
+    lo = __builtin_elementwise_min(lo, m);
+  }
+  mx = hi.x > hi.y ? hi.x : hi.y;
+  mn = lo.x < lo.y ? lo.x : lo.y;
+}
+
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint8_t* staging = smem;                                  // kStagingBytes
-  uint32_t* red = (uint32_t*)(smem + kStagingBytes);        // 8 wave maxima + broadcast
-  uint16_t* tab = (uint16_t*)(smem + kStagingBytes + 64);   // 65,536 entries (SwiGLU only)
+  uint32_t* red = (uint32_t*)smem;                          // wave maxima + two broadcast slots
+  uint16_t* tab = (uint16_t*)(smem + kRedBytes);            // 65,536 entries (SwiGLU only)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int chunk = lane & 31;  // 8-element chunk of the 256-column segment
+  const int r4 = lane >> 4;    // row within the wave's 4 rows of a step
+  const int blk = lane & 15;   // 16-column block of the 256-column segment
   const int nitems = a.items_m * a.items_k;
 
   if (SWIGLU) {
@@ -160,31 +250,37 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
     __syncthreads();
   }
 
-  auto load_item = [&](int item, u32x4_t (&gv)[kSteps], u32x4_t (&uv)[kSteps]) {
+  // the 16 bf16 values of this lane's block in each step of an item (zero outside
+  // the logical rows and columns)
+  auto load_item = [&](int item, u32x4_t (&gv)[kSteps][2], u32x4_t (&uv)[kSteps][2]) {
     const int rt = item / a.items_k, kt = item - rt * a.items_k;
-    const int64_t col = (int64_t)kt * kItemCols + chunk * 8;
+    const int64_t col = (int64_t)kt * kItemCols + blk * 16;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int64_t row = (int64_t)rt * kItemRows + s * 16 + wave * 2 + (lane >> 5);
+      const int64_t row = (int64_t)rt * kItemRows + s * kRowsPerStep + wave * 4 + r4;
       const bool ok = row < a.m && col < a.k;
-      u32x4_t z = {0u, 0u, 0u, 0u};
-      gv[s] = ok ? *(const u32x4_t*)(a.x + row * a.ldx + col) : z;
-      if (SWIGLU) uv[s] = ok ? *(const u32x4_t*)(a.u + row * a.ldu + col) : z;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      const u32x4_t* px = (const u32x4_t*)(a.x + row * a.ldx + col);
+      gv[s][0] = ok ? px[0] : z;
+      gv[s][1] = ok ? px[1] : z;
+      if (SWIGLU) {
+        const u32x4_t* pu = (const u32x4_t*)(a.u + row * a.ldu + col);
+        uv[s][0] = ok ? pu[0] : z;
+        uv[s][1] = ok ? pu[1] : z;
+      }
     }
   };
 
   // ---------------- pass 1: absmax ----------------
   uint32_t local_bits = 0;  // fp32 bits of a non-negative value
-  bool needs_exact = false;
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    u32x4_t gv[kSteps], uv[kSteps];
-    load_item(item, gv, uv);
+  auto absmax_item = [&](const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < 8; ++w) {
+        const uint32_t gw = gv[s][w >> 2][w & 3];
         if (SWIGLU) {
-          const uint32_t gw = gv[s][w], uw = uv[s][w];
+          const uint32_t uw = uv[s][w >> 2][w & 3];
           const float s0 = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16);
           const float s1 = __uint_as_float((uint32_t)tab[gw >> 16] << 16);
           const float p0 = fabsf(s0 * __uint_as_float(uw << 16));
@@ -192,15 +288,32 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
           const uint32_t b = __float_as_uint(fmaxf(p0, p1));
           local_bits = b > local_bits ? b : local_bits;
         } else {
-          const uint32_t gw = gv[s][w];
           const uint32_t m0 = gw & 0x7FFFu, m1 = (gw >> 16) & 0x7FFFu;
           const uint32_t b = (m0 > m1 ? m0 : m1) << 16;
           local_bits = b > local_bits ? b : local_bits;
         }
       }
     }
+  };
+  {
+    // the next item's loads are in flight while the current item is reduced
+    u32x4_t gA[kSteps][2], uA[kSteps][2], gB[kSteps][2], uB[kSteps][2];
+    int item = blockIdx.x;
+    if (item < nitems) load_item(item, gA, uA);
+    while (item < nitems) {
+      const int n1 = item + (int)gridDim.x;
+      if (n1 < nitems) load_item(n1, gB, uB);
+      absmax_item(gA, uA);
+      item = n1;
+      if (item >= nitems) break;
+      const int n2 = item + (int)gridDim.x;
+      if (n2 < nitems) load_item(n2, gA, uA);
+      absmax_item(gB, uB);
+      item = n2;
+    }
   }
   // workgroup max of the unrounded |products| (SwiGLU) or of |x|
+  bool needs_exact = false;
   {
     uint32_t wmax = wave_max_u32(local_bits);
     if (lane == 0) red[wave] = wmax;
@@ -208,10 +321,10 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
     if (tid == 0) {
       uint32_t v = 0;
       for (int i = 0; i < kProdThreads / 64; ++i) v = red[i] > v ? red[i] : v;
-      red[8] = v;
+      red[kWaves] = v;
     }
     __syncthreads();
-    local_bits = red[8];
+    local_bits = red[kWaves];
     // A product below 2^-126 may have been rounded in fp32; if this workgroup's
     // maximum is such a product, redo its elements exactly (never taken for
     // inputs whose absmax is a normal number).
@@ -221,12 +334,12 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
   if (SWIGLU && needs_exact) {
     uint32_t best = 0;  // bf16 magnitude bits
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-      u32x4_t gv[kSteps], uv[kSteps];
+      u32x4_t gv[kSteps][2], uv[kSteps][2];
       load_item(item, gv, uv);
       for (int s = 0; s < kSteps; ++s)
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t g16 = (gv[s][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-          const uint32_t u16 = (uv[s][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t g16 = (gv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
+          const uint32_t u16 = (uv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
           const double p = (double)bf16_bits_to_float(tab[g16]) * (double)bf16_bits_to_float(u16);
           const uint32_t y = rn_bf16_from_double(p) & 0x7FFFu;
           best = y > best ? y : best;
@@ -238,10 +351,10 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
     if (tid == 0) {
       uint32_t v = 0;
       for (int i = 0; i < kProdThreads / 64; ++i) v = red[i] > v ? red[i] : v;
-      red[8] = v << 16;
+      red[kWaves] = v << 16;
     }
     __syncthreads();
-    local_bits = red[8];
+    local_bits = red[kWaves];
   } else if (SWIGLU) {
     // RN_bf16 is monotone, so the rounded maximum is the maximum of the rounded values.
     local_bits = (cvt_pk_bf16(__uint_as_float(local_bits), 0.0f) & 0xFFFFu) << 16;
@@ -255,7 +368,7 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
     while (__hip_atomic_load(&ws->arrived, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x)
       __builtin_amdgcn_s_sleep(2);
     const uint32_t amax = __hip_atomic_load(&ws->amax_bits, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    red[9] = amax;
+    red[kWaves + 1] = amax;
     // the last workgroup to leave returns the workspace to zero for the next call
     const uint32_t d = __hip_atomic_fetch_add(&ws->departed, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (d == gridDim.x - 1) {
@@ -265,113 +378,99 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
     }
   }
   __syncthreads();
-  const float amax = __uint_as_float(red[9]);
+  const float amax = __uint_as_float(red[kWaves + 1]);
   const float g = global_scale_from_amax(amax);
   const double g6 = 6.0 * (double)g;
+  // 1 / (6g) in fp32; for a tiny g both factors of bmax / (6g) are scaled by 2^64 (exact)
+  double inv_g6 = g6 > 0.0 ? 1.0 / g6 : 0.0;
+  float bscale = 1.0f;
+  if (inv_g6 > 0x1p+100) {
+    inv_g6 *= 0x1p-64;
+    bscale = 0x1p+64f;
+  }
+  const float inv_f = (float)inv_g6;
   if (blockIdx.x == 0 && tid == 0) *a.gout = g;
 
   // ---------------- pass 2: scales, codes, pack, swizzle ----------------
   const int64_t qrow_bytes = a.k / 2;
-  for (int item = nitems - 1 - (int)blockIdx.x; item >= 0; item -= gridDim.x) {
+  auto quantize_item = [&](int item, const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
     const int rt = item / a.items_k, kt = item - rt * a.items_k;
-    u32x4_t gv[kSteps], uv[kSteps];
-    load_item(item, gv, uv);
-    const int64_t col = (int64_t)kt * kItemCols + chunk * 8;
+    const int64_t col = (int64_t)kt * kItemCols + blk * 16;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int lrow = s * 16 + wave * 2 + (lane >> 5);
+      const int lrow = s * kRowsPerStep + wave * 4 + r4;
       const int64_t row = (int64_t)rt * kItemRows + lrow;
-      // y as four packed bf16 pairs
-      uint32_t yb[4];
-      if (SWIGLU) {
-        float p[8];
-        bool tiny = false;
+      uint32_t yb[8];
+      block_y<SWIGLU>(gv[s], uv[s], tab, yb);
+      // block maximum of |y| (bf16 magnitudes compare as integers)
+      uint32_t mx, mn;
+      block_mag_range(yb, mx, mn);
+      if (SWIGLU && mn <= 0x0080u) {
+        // some |y| <= 2^-126 (or zero): its fp32 product may have been subnormal and
+        // rounded; redo such products exactly
+        Y8 y;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t gw = gv[s][w], uw = uv[s][w];
-          p[2 * w] = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16) * __uint_as_float(uw << 16);
-          p[2 * w + 1] = __uint_as_float((uint32_t)tab[gw >> 16] << 16) * __uint_as_float(uw & 0xFFFF0000u);
-          tiny |= fabsf(p[2 * w]) < 0x1p-126f;
-          tiny |= fabsf(p[2 * w + 1]) < 0x1p-126f;
-          yb[w] = cvt_pk_bf16(p[2 * w], p[2 * w + 1]);
-        }
-        if (tiny) {
+        for (int w = 0; w < 8; ++w) y.v[w] = yb[w];
+        y = block_y_fix(gv[s][0], gv[s][1], uv[s][0], uv[s][1], y, tab);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            if (fabsf(p[j]) < 0x1p-126f) {
-              const uint32_t g16 = (gv[s][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-              const uint32_t u16 = (uv[s][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-              const double pd = (double)bf16_bits_to_float(tab[g16]) * (double)bf16_bits_to_float(u16);
-              const uint32_t y = rn_bf16_from_double(pd);
-              const int sh = 16 * (j & 1);
-              yb[j >> 1] = (yb[j >> 1] & ~(0xFFFFu << sh)) | (y << sh);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) yb[w] = gv[s][w];
+        for (int w = 0; w < 8; ++w) yb[w] = y.v[w];
+        block_mag_range(yb, mx, mn);
       }
-      // block maximum over the lane pair (16 elements)
-      uint32_t mx = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t m0 = yb[w] & 0x7FFFu, m1 = (yb[w] >> 16) & 0x7FFFu;
-        mx = m0 > mx ? m0 : mx;
-        mx = m1 > mx ? m1 : mx;
-      }
-      const uint32_t other = (uint32_t)__shfl_xor((int)mx, 1, 64);
-      mx = other > mx ? other : mx;
-      const float bmax = bf16_bits_to_float(mx);
-      const uint32_t S = (mx == 0) ? 0u : block_scale_byte(bmax, g6);
+      const uint32_t S = (mx == 0) ? 0u : block_scale_byte(bf16_bits_to_float(mx), bscale, inv_f, g6);
 
-      // E2M1 codes of the 8 elements of this lane
+      // E2M1 codes of the 16 elements
       const float unit = ue4m3_to_float(S) * g;
       const bool exact_block = (S != 0) && !(unit >= 0x1p-100f);
       const float rcp = (S == 0) ? 1.0f : __builtin_amdgcn_rcpf(unit);
       const float rlo = rcp * (1.0f - 0x1p-20f);
       const float rhi = rcp * (1.0f + 0x1p-20f);
-      uint32_t clo = 0, chi = 0;
-      fp4_pair<0>(clo, chi, yb[0], rlo, rhi);
-      fp4_pair<1>(clo, chi, yb[1], rlo, rhi);
-      fp4_pair<2>(clo, chi, yb[2], rlo, rhi);
-      fp4_pair<3>(clo, chi, yb[3], rlo, rhi);
-      if (clo != chi || exact_block) {
-        uint32_t c = 0;
-        for (int j = 0; j < 8; ++j) {
+      uint32_t clo0 = 0, chi0 = 0, clo1 = 0, chi1 = 0;
+      fp4_pair<0>(clo0, chi0, yb[0], rlo, rhi);
+      fp4_pair<1>(clo0, chi0, yb[1], rlo, rhi);
+      fp4_pair<2>(clo0, chi0, yb[2], rlo, rhi);
+      fp4_pair<3>(clo0, chi0, yb[3], rlo, rhi);
+      fp4_pair<0>(clo1, chi1, yb[4], rlo, rhi);
+      fp4_pair<1>(clo1, chi1, yb[5], rlo, rhi);
+      fp4_pair<2>(clo1, chi1, yb[6], rlo, rhi);
+      fp4_pair<3>(clo1, chi1, yb[7], rlo, rhi);
+      if (clo0 != chi0 || clo1 != chi1 || exact_block) {
+        uint32_t c[2] = {0u, 0u};
+        for (int j = 0; j < 16; ++j) {
           const uint32_t y16 = (yb[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-          const uint32_t nib_lo = (clo >> (4 * j)) & 15u, nib_hi = (chi >> (4 * j)) & 15u;
+          const uint32_t lo = j < 8 ? clo0 : clo1, hi = j < 8 ? chi0 : chi1;
+          const uint32_t nib_lo = (lo >> (4 * (j & 7))) & 15u, nib_hi = (hi >> (4 * (j & 7))) & 15u;
           const uint32_t code = (nib_lo == nib_hi && !exact_block) ? nib_lo : e2m1_code_exact(y16, S, g);
-          c |= code << (4 * j);
+          c[j >> 3] |= code << (4 * (j & 7));
         }
-        clo = c;
+        clo0 = c[0];
+        clo1 = c[1];
       }
-      if (row < a.m_pad && col < a.k)
-        *(uint32_t*)(a.qdata + row * qrow_bytes + col / 2) = clo;
-      if ((lane & 1) == 0) {
-        const int b = chunk >> 1;  // block within the segment, 0..15
-        staging[(b >> 2) * 512 + (lrow & 31) * 16 + ((lrow >> 5) & 3) * 4 + (b & 3)] = (uint8_t)S;
+      if (row < a.m_pad && col < a.k) {
+        const u32x2_t v = {clo0, clo1};
+        *(u32x2_t*)(a.qdata + row * qrow_bytes + col / 2) = v;
       }
-    }
-    __syncthreads();
-    {
-      // write the item's scale tiles: 4 tiles of 512 bytes, one dword per thread
-      const int64_t seg_cols = a.k - (int64_t)kt * kItemCols;
-      const int ntiles = (int)((seg_cols >= kItemCols ? kItemCols : seg_cols) / 64);
-      const int tile = tid >> 7;
-      if (tile < ntiles) {
-        const int64_t off = ((int64_t)rt * (a.cpad / 4) + (int64_t)kt * 4 + tile) * 512 + (tid & 127) * 4;
-        *(uint32_t*)(a.scales + off) = ((const uint32_t*)staging)[tid];
+      // the scale byte at its place in the 128 x 4 tile (rows past m_pad hold zero);
+      // the byte stores of the workgroup's 16 waves fill each 512-byte tile
+      if (col < a.k) {
+        const int64_t tile = (int64_t)rt * (a.cpad / 4) + (int64_t)kt * 4 + (blk >> 2);
+        a.scales[tile * 512 + (lrow & 31) * 16 + ((lrow >> 5) & 3) * 4 + (blk & 3)] = (uint8_t)S;
       }
     }
-    __syncthreads();
+  };
+  // items in reverse order: the rows read last in pass 1, still in the memory-side
+  // cache, are read first. No workgroup barrier: the 16 waves drift apart and hide
+  // each other's load latency.
+  for (int item = nitems - 1 - (int)blockIdx.x; item >= 0; item -= (int)gridDim.x) {
+    u32x4_t gv[kSteps][2], uv[kSteps][2];
+    load_item(item, gv, uv);
+    quantize_item(item, gv, uv);
   }
 }
 
 // ---- host side --------------------------------------------------------------------------------
 
 size_t producer_smem_bytes(bool swiglu) {
-  return kStagingBytes + 64 + (swiglu ? 65536 * 2 : 0);
+  return kRedBytes + (swiglu ? 65536 * 2 : 0);
 }
 
 const void* producer_kernel_ptr(bool swiglu) {

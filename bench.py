@@ -48,34 +48,61 @@ def gemm_bytes(m: int, n: int, k: int) -> int:
     return a + w + m_pad * n * 2
 
 
+GEMM_SOURCES = ("nvfp4_block_scaled_swiglu_amd/csrc/gemm.hip", "nvfp4_block_scaled_swiglu_amd/csrc/common.hpp")
+GEMM_TRAFFIC_SUMMARY = "profiles/gemm_fc2_hbm_traffic.md"
+
+
+def measured_gemm_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by a copy kernel of known size), or None when the summary
+    was taken on a different kernel source than the one built here."""
+    import hashlib
+    try:
+        h = hashlib.sha256()
+        for f in GEMM_SOURCES:
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        vals = {}
+        with open(os.path.join(ROOT, GEMM_TRAFFIC_SUMMARY)) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith(("#", "|", "`")):
+                    k, _, v = line.partition(":")
+                    vals[k.strip()] = v.strip()
+        if vals.get("source_sha256") != h.hexdigest():
+            return None
+        return int(vals["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, threads: int) -> dict:
-    """The CPU oracle timed on a bounded sample of the same workload: the exact GEMM on
-    sampled rows (all N columns, full K), scaled to TFLOP/s. The oracle is an
+    """The CPU oracle timed on a bounded sample of the same workload (about 10-15 s
+    of CPU work on 16 cores): the exact GEMM on 16,384 evenly spaced rows (all N
+    columns, full K), scaled to TFLOP/s, and the exact producer over the whole
+    activation. The oracle is an
     exact-arithmetic correctness reference, not a tuned CPU GEMM."""
     import numpy as np
     import oracle
-    import synth
-    rows = 1024
-    acts = w.activations(rows=rows, threads=threads)
+    rows = min(16384, w.m)
+    acts = w.activations(threads=threads)
+    t0 = time.perf_counter()
     aq, as_, ga = oracle.quantize(acts[0], acts[1] if w.swiglu else None, threads=threads)
+    t_prod = time.perf_counter() - t0
+    del acts
     W = w.weight(threads=threads)
     wq, ws, gw = oracle.quantize(W, threads=threads)
+    sel = np.arange(rows) * (w.m // rows)
     t0 = time.perf_counter()
-    oracle.gemm_rows(aq, as_, rows, ga, wq, ws, w.n, gw, w.k, np.arange(rows), threads=threads)
+    oracle.gemm_rows(aq, as_, w.m, ga, wq, ws, w.n, gw, w.k, sel, threads=threads)
     t_gemm = time.perf_counter() - t0
-    prod_rows = 4096
-    acts = w.activations(rows=prod_rows, threads=threads)
-    t0 = time.perf_counter()
-    oracle.quantize(acts[0], acts[1] if w.swiglu else None, threads=threads)
-    t_prod = time.perf_counter() - t0
     return {
         "value": 2.0 * rows * w.n * w.k / t_gemm / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"exact int64 GEMM of {rows} sampled rows x {w.n} x {w.k} ({t_gemm:.2f} s); producer "
-                  f"over {prod_rows} rows x {w.k}: {producer_bytes(prod_rows, w.k, w.swiglu) / t_prod / 1e9:.3f} "
-                  f"GB/s ({t_prod:.2f} s)",
+        "sample": f"exact int64 GEMM of {rows} rows (every {w.m // rows}th of {w.m}) x {w.n} x {w.k} "
+                  f"({t_gemm:.2f} s); exact producer over all {w.m} x {w.k}: "
+                  f"{producer_bytes(w.m, w.k, w.swiglu) / t_prod / 1e9:.3f} GB/s ({t_prod:.2f} s)",
     }
 
 
@@ -132,6 +159,42 @@ def only_gemm(w, args, dev) -> int:
     return 0
 
 
+def only_producer(w, args, dev) -> int:
+    """Producer-only timing on the workload's seeded inputs (no GEMM in the process)."""
+    import statistics
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    from tests import parity
+    acts = w.activations()
+    x = parity.to_device_bf16(acts[0], dev)
+    u = parity.to_device_bf16(acts[1], dev) if w.swiglu else None
+    del acts
+    a = nv.empty_nvfp4(w.m, w.k, dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        if w.swiglu:
+            nv.nvfp4_quantize_swiglu(x, u, out=a)
+        else:
+            nv.nvfp4_quantize(x, out=a)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    t_prod = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs)
+    pbytes = producer_bytes(w.m, w.k, w.swiglu)
+    print(json.dumps({"mode": "only-producer", "workload": w.name, "producer_ms": round(t_prod, 4),
+                      "gbs": round(pbytes / (t_prod * 1e-3) / 1e9, 1), "algorithmic_bytes": pbytes,
+                      "steps": args.steps}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +205,8 @@ def main() -> int:
     ap.add_argument("--only-gemm", action="store_true",
                     help="time the GEMM alone on seeded random NVFP4 operand bytes (no producer launch in "
                          "the process; used for profiler counter runs)")
+    ap.add_argument("--only-producer", action="store_true",
+                    help="time the producer alone on the workload's seeded inputs (no GEMM launch)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only-gemm: also run a plain elementwise copy of this many bytes (read + "
                          "write), the calibration kernel for the profiler's FETCH_SIZE / WRITE_SIZE")
@@ -163,6 +228,8 @@ def main() -> int:
 
     if args.only_gemm:
         return only_gemm(w, args, dev)
+    if args.only_producer:
+        return only_producer(w, args, dev)
 
     t0 = time.perf_counter()
     acts = w.activations()
@@ -250,7 +317,8 @@ def main() -> int:
             "peak": PEAK_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_gemm_traffic() if w.name == "fc2_canonical" else None,
+            "traffic_summary": GEMM_TRAFFIC_SUMMARY,
             "kernel": "nvfp4::gemm_kernel",
             "algorithmic_per_launch": f"{w.gemm_flops:.4e} FLOP (2*M*N*K, logical M)",
             "avg_launch_ms": round(t_gemm, 4),

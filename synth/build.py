@@ -10,7 +10,7 @@ LIB = os.path.join(HERE, "libsynth.so")
 def build(verbose: bool = False) -> str:
     src = os.path.join(HERE, "synth.c")
     tmp = LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-pthread", "-fPIC", "-shared", "-std=c11",
            "-Wall", "-Wextra", src, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -28,6 +28,7 @@
  *   shuffled order are the outlier columns.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -89,20 +90,58 @@ int synth_outlier_mask(uint8_t* mask, int64_t cols, uint64_t seed, uint64_t tag,
 }
 
 /*
- * out[r * ld + c] for r < rows, c < cols: bf16 bits of the seeded normal with
- * standard deviation sigma, x20 on columns where mask[c] != 0 (mask may be
- * NULL). Elements of a row beyond cols (ld > cols) are left untouched.
+ * A parallel loop over [0, n) on nthreads threads (the caller included): fn runs on
+ * contiguous slices; every thread is joined before returning, so no thread outlives
+ * a call. Each element is a pure function of its index, so the thread count never
+ * changes the result.
  */
-int synth_normal_bf16(uint16_t* out, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
-                      uint64_t tag, float sigma, const uint8_t* mask, int nthreads) {
-  if (!out || rows < 0 || cols < 0 || ld < cols) return -1;
-  const uint64_t key = stream_key(seed, tag);
-  const int64_t total = rows * cols;
-  const int64_t npairs = (total + 1) / 2;
-  (void)nthreads;
-#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
-  for (int64_t p = 0; p < npairs; ++p) {
-    uint64_t h = draw(key, (uint64_t)p);
+typedef void (*slice_fn)(void* ctx, int64_t begin, int64_t end);
+typedef struct {
+  slice_fn fn;
+  void* ctx;
+  int64_t begin, end;
+} slice_job;
+
+static void* slice_main(void* arg) {
+  slice_job* j = (slice_job*)arg;
+  j->fn(j->ctx, j->begin, j->end);
+  return NULL;
+}
+
+static void parallel_for(int64_t n, int nthreads, slice_fn fn, void* ctx) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 64) nthreads = 64;
+  if ((int64_t)nthreads > n) nthreads = n > 0 ? (int)n : 1;
+  slice_job jobs[64];
+  pthread_t tids[64];
+  int started[64];
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t].fn = fn;
+    jobs[t].ctx = ctx;
+    jobs[t].begin = n * t / nthreads;
+    jobs[t].end = n * (t + 1) / nthreads;
+    started[t] = 0;
+  }
+  for (int t = 1; t < nthreads; ++t) started[t] = pthread_create(&tids[t], NULL, slice_main, &jobs[t]) == 0;
+  slice_main(&jobs[0]);
+  for (int t = 1; t < nthreads; ++t) {
+    if (started[t]) pthread_join(tids[t], NULL);
+    else slice_main(&jobs[t]);  /* thread creation failed: run the slice here */
+  }
+}
+
+typedef struct {
+  uint16_t* out;
+  int64_t total, cols, ld;
+  uint64_t key;
+  float sigma;
+  const uint8_t* mask;
+} normal_ctx;
+
+static void normal_slice(void* vc, int64_t begin, int64_t end) {
+  const normal_ctx* c = (const normal_ctx*)vc;
+  for (int64_t p = begin; p < end; ++p) {
+    uint64_t h = draw(c->key, (uint64_t)p);
     double u1 = ((double)(h >> 32) + 0.5) * (1.0 / 4294967296.0);
     double u2 = (double)(h & 0xFFFFFFFFu) * (1.0 / 4294967296.0);
     double rad = sqrt(-2.0 * log(u1));
@@ -110,14 +149,44 @@ int synth_normal_bf16(uint16_t* out, int64_t rows, int64_t cols, int64_t ld, uin
     double nv[2] = {rad * cos(th), rad * sin(th)};
     for (int s = 0; s < 2; ++s) {
       int64_t i = 2 * p + s;
-      if (i >= total) break;
-      int64_t r = i / cols, c = i - r * cols;
-      float v = (float)((double)sigma * nv[s]);
-      if (mask && mask[c]) v = v * 20.0f;
-      out[r * ld + c] = float_to_bf16_rne(v);
+      if (i >= c->total) break;
+      int64_t r = i / c->cols, col = i - r * c->cols;
+      float v = (float)((double)c->sigma * nv[s]);
+      if (c->mask && c->mask[col]) v = v * 20.0f;
+      c->out[r * c->ld + col] = float_to_bf16_rne(v);
     }
   }
+}
+
+/*
+ * out[r * ld + c] for r < rows, c < cols: bf16 bits of the seeded normal with
+ * standard deviation sigma, x20 on columns where mask[c] != 0 (mask may be
+ * NULL). Elements of a row beyond cols (ld > cols) are left untouched.
+ */
+int synth_normal_bf16(uint16_t* out, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
+                      uint64_t tag, float sigma, const uint8_t* mask, int nthreads) {
+  if (!out || rows < 0 || cols < 0 || ld < cols) return -1;
+  normal_ctx c;
+  c.out = out;
+  c.total = rows * cols;
+  c.cols = cols;
+  c.ld = ld;
+  c.key = stream_key(seed, tag);
+  c.sigma = sigma;
+  c.mask = mask;
+  parallel_for((c.total + 1) / 2, nthreads, normal_slice, &c);
   return 0;
+}
+
+typedef struct {
+  uint8_t* out;
+  uint64_t key, span;
+  int lo;
+} bytes_ctx;
+
+static void bytes_slice(void* vc, int64_t begin, int64_t end) {
+  const bytes_ctx* c = (const bytes_ctx*)vc;
+  for (int64_t i = begin; i < end; ++i) c->out[i] = (uint8_t)(c->lo + (int)(draw(c->key, (uint64_t)i) % c->span));
 }
 
 /*
@@ -126,10 +195,11 @@ int synth_normal_bf16(uint16_t* out, int64_t rows, int64_t cols, int64_t ld, uin
  */
 int synth_bytes(uint8_t* out, int64_t n, uint64_t seed, uint64_t tag, int lo, int hi, int nthreads) {
   if (!out || n < 0 || lo < 0 || hi > 255 || lo > hi) return -1;
-  const uint64_t key = stream_key(seed, tag);
-  const uint64_t span = (uint64_t)(hi - lo + 1);
-  (void)nthreads;
-#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
-  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)(lo + (int)(draw(key, (uint64_t)i) % span));
+  bytes_ctx c;
+  c.out = out;
+  c.key = stream_key(seed, tag);
+  c.span = (uint64_t)(hi - lo + 1);
+  c.lo = lo;
+  parallel_for(n, nthreads, bytes_slice, &c);
   return 0;
 }

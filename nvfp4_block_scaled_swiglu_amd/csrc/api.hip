@@ -28,7 +28,7 @@ size_t gemm_smem_bytes();
 const void* gemm_kernel_ptr();
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
-                       hipStream_t stream);
+                       int cu_count, hipStream_t stream);
 }  // namespace nvfp4
 
 namespace {
@@ -220,7 +220,7 @@ int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const 
   if (m_padded == 0) return ok();
   hipError_t e = nvfp4::launch_gemm((const uint8_t*)a_qdata_dev, (const uint8_t*)a_scales_dev, a_global_dev,
                                     (const uint8_t*)w_qdata_dev, (const uint8_t*)w_scales_dev, w_global_dev,
-                                    (uint16_t*)d_dev, m_padded, n, k, (hipStream_t)stream);
+                                    (uint16_t*)d_dev, m_padded, n, k, st->cu_count, (hipStream_t)stream);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -43,28 +43,43 @@
 
 namespace nvfp4 {
 
-// Workgroup tile kTM x kTN = (WAVES_M * FM * 32) x (WAVES_N * FN * 32); each wave owns
-// FM x FN MFMA tiles of 32 x 32 with its accumulators in AGPRs, one wave per SIMD.
-constexpr int WAVES_M = 2, WAVES_N = 2, FM = 4, FN = 4;
-constexpr int kTM = WAVES_M * FM * 32, kTN = WAVES_N * FN * 32, kTK = 128;
+// A workgroup of 4 waves (2 x 2, one per SIMD) computes a tile of
+// (2 * FM * 32) x (2 * FN * 32); each wave owns FM x FN MFMA tiles of 32 x 32 with its
+// accumulators in AGPRs. Full tiles are 256 x 256 (FM = FN = 4); when the last round
+// of tiles would leave most CUs idle, its tiles are split into 128 x 128 quarters
+// (FM = FN = 2), so that the tail is spread over four times as many CUs.
+constexpr int WAVES_M = 2, WAVES_N = 2;
 constexpr int kWaves = WAVES_M * WAVES_N;
 constexpr int kGemmThreads = 64 * kWaves;
+constexpr int kTK = 128;                         // K per step
 constexpr int kStages = 3;                       // LDS stages (loads run two K steps ahead)
-constexpr int kCodesA = kTM * 64;                // A codes per stage: 64 bytes per row
-constexpr int kCodesW = kTN * 64;
-constexpr int kScaleA = kTM / 128 * 1024;        // A scale tiles per stage (2 column groups)
-constexpr int kScaleW = kTN / 128 * 1024;
-constexpr int kStageBytes = kCodesA + kCodesW + kScaleA + kScaleW;
 constexpr int kBandM = 8;                        // M-tiles per traversal band
-// one wave-wide direct-to-LDS load moves 1 KiB: 16 rows of codes or one 1 KiB scale block
-constexpr int kWaveLoadsA = kCodesA / 1024, kWaveLoadsW = kCodesW / 1024;
-constexpr int kWaveLoadsS = (kScaleA + kScaleW) / 1024;
-constexpr int kLoadsPerWave = (kWaveLoadsA + kWaveLoadsW + kWaveLoadsS) / kWaves;
-static_assert((kWaveLoadsA + kWaveLoadsW + kWaveLoadsS) % kWaves == 0, "even load split");
-static_assert(kWaveLoadsA % kWaves == 0 && kWaveLoadsW % kWaves == 0 && kWaveLoadsS == kWaves,
-              "each wave issues the same mix of loads");
-static_assert(kTM % 128 == 0 && kTN % 128 == 0, "tiles cover whole 128-row scale tiles");
-static_assert(kLoadsPerWave <= 15, "vmcnt immediate");
+constexpr int kTileBig = 256;                    // full tile edge
+constexpr int kTileQuarter = 128;                // tail tile edge
+
+template <int FM_, int FN_>
+struct TileShape {
+  static constexpr int TM = WAVES_M * FM_ * 32, TN = WAVES_N * FN_ * 32;
+  static constexpr int CodesA = TM * 64, CodesW = TN * 64;         // 64 code bytes per row per K step
+  static constexpr int ScaleA = TM / 128 * 1024, ScaleW = TN / 128 * 1024;  // two 512-B tiles per 128 rows
+  static constexpr int StageBytes = CodesA + CodesW + ScaleA + ScaleW;
+  // per wave and K step: code wave-loads of 1 KiB (16 rows) and scale loads
+  static constexpr int LoadsA = CodesA / 1024 / kWaves, LoadsW = CodesW / 1024 / kWaves;
+  static constexpr int ScalePerWave = (ScaleA + ScaleW) / kWaves;   // bytes
+  static constexpr int ScaleLoadBytes = ScalePerWave >= 1024 ? 1024 : 256;  // dwordx4 or dword per lane
+  static constexpr int LoadsS = ScalePerWave / ScaleLoadBytes;
+  static constexpr int Loads = LoadsA + LoadsW + LoadsS;
+  // VALU per MFMA of one K16 step: 8 per fragment (4 conversions, 4 multiplies) + a scale pair
+  static constexpr int ValuPerMfma = ((FM_ + FN_) * 9 + FM_ * FN_ - 1) / (FM_ * FN_);
+  static_assert(CodesA % (1024 * kWaves) == 0 && CodesW % (1024 * kWaves) == 0, "even code-load split");
+  static_assert((ScaleA + ScaleW) % (ScaleLoadBytes * kWaves) == 0, "even scale-load split");
+  static_assert(TM % 128 == 0 && TN % 128 == 0, "tiles cover whole 128-row scale tiles");
+  static_assert(Loads <= 15, "vmcnt immediate");
+};
+using BigTile = TileShape<4, 4>;
+using QuarterTile = TileShape<2, 2>;
+static_assert(BigTile::TM == kTileBig && BigTile::TN == kTileBig, "full tile");
+static_assert(QuarterTile::TM == kTileQuarter && QuarterTile::TN == kTileQuarter, "quarter tile");
 
 struct GemmArgs {
   const uint8_t* aq;
@@ -76,7 +91,8 @@ struct GemmArgs {
   uint16_t* d;
   int64_t m_pad, n, k;
   int a_qbytes, w_qbytes, a_sbytes, w_sbytes;  // buffer sizes for the range checks
-  int tiles_m, tiles_n;
+  int tiles_m, tiles_n;                        // 256 x 256 tiles
+  int big_tiles;                               // tiles [0, big_tiles) run whole; the rest as quarters
   int cgroups;                                 // scale column groups = C / 4
   int ksteps;
 };
@@ -145,13 +161,15 @@ __device__ __forceinline__ f16x2_t scale_pair(uint32_t sdw, int b) {
   return r;
 }
 
-// Scheduling hints: in each K16 step, interleave one MFMA with five VALU
-// instructions (the next step's dequantization and scale pairs).
+// Scheduling hints: in each K16 step, interleave each MFMA with its share of the
+// VALU work (the next step's dequantization and scale pairs): five per MFMA for the
+// full tile, nine for the quarter tile.
+template <int NMFMA, int NVALU>
 __device__ __forceinline__ void interleave_hint() {
 #pragma unroll
-  for (int i = 0; i < FM * FN; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);  // its share of VALU
   }
 }
 
@@ -165,23 +183,13 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-
-  // ---- tile assignment: XCD-contiguous ranges, m-band-major order ----
-  const int ntiles = a.tiles_m * a.tiles_n;
-  const int b = blockIdx.x;
-  const int nb = gridDim.x;
-  const int per = nb / 8, rem = nb % 8;
-  const int xcd = b % 8, idx = b / 8;
-  const int t = xcd * per + (xcd < rem ? xcd : rem) + idx;
-  if (t >= ntiles) return;
-  const int band = t / (kBandM * a.tiles_n);
-  const int in_band = t - band * kBandM * a.tiles_n;
-  const int band_m = (a.tiles_m - band * kBandM) < kBandM ? (a.tiles_m - band * kBandM) : kBandM;
-  const int tm = band * kBandM + in_band % band_m;
-  const int tn = in_band / band_m;
-  const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
+// One output tile: the whole K loop and the epilogue for rows [m0, m0 + TM) and
+// columns [n0, n0 + TN), by the workgroup's 4 waves.
+template <int FM, int FN>
+__device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, const int64_t n0, unsigned char* smem) {
+  using T = TileShape<FM, FN>;
+  constexpr int kStageBytes = T::StageBytes, kCodesA = T::CodesA, kCodesW = T::CodesW, kScaleA = T::ScaleA;
+  constexpr int kLoads = T::Loads;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -194,37 +202,42 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
   __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)a.as, 0, a.a_sbytes, 0x00020000);
   __amdgpu_buffer_rsrc_t rSW = __builtin_amdgcn_make_buffer_rsrc((void*)a.ws, 0, a.w_sbytes, 0x00020000);
   const int krow = (int)(a.k / 2);
-  constexpr int kOutOfRange = 0x7FFFFFF0;  // reads past a buffer's range return zero
 
   // ---- direct-to-LDS loads of one K step into a stage ----
   // Code wave-load j covers rows 16j .. 16j+15; lane L writes LDS bytes 16L..16L+15 of
   // that 1 KiB, i.e. row 16j + L/4 at chunk position L%4, which holds global chunk
-  // chunk_pos(row, L%4) (the XOR is an involution). Scale wave-load q covers row
-  // tile q%2 of A (q < 2) or W (q >= 2): its two 512-byte column-group tiles.
-  // Load idx (0..kLoadsPerWave-1) of this wave's share of K step ks: idx < 4 are A code
-  // wave-loads, 4..7 W code wave-loads, 8 the scale block. Half K steps (K % 128 == 64)
-  // send the upper k-half past the buffer range, where reads return zero.
+  // chunk_pos(row, L%4) (the XOR is an involution). The scale part of a stage is one
+  // 1 KiB block per 128 rows (A blocks, then W blocks), each the two 512-byte
+  // column-group tiles of that row tile for the K step, contiguous in global memory;
+  // each wave loads an equal share of it in pieces of ScaleLoadBytes.
+  // Load idx (0..kLoads-1) of this wave's share of K step ks: code loads of A, then
+  // of W, then scale pieces. Half K steps (K % 128 == 64) send the upper k-half past
+  // the buffer range, where reads return zero.
   auto issue_one = [&](int ks, int stage, int idx) {
     const int oor = ((int64_t)(ks + 1) * kTK > a.k) ? 0x7FFFFFF0 : 0;  // wave-uniform
     unsigned char* st = smem + stage * kStageBytes;
-    const int rsub = lane >> 2, p = lane & 3;
-    if (idx < 2 * (kWaveLoadsA / kWaves)) {
-      const bool isA = idx < kWaveLoadsA / kWaves;
-      const int j = wave + (isA ? idx : idx - kWaveLoadsA / kWaves) * kWaves;
+    if (idx < T::LoadsA + T::LoadsW) {
+      const int rsub = lane >> 2, p = lane & 3;
+      const bool isA = idx < T::LoadsA;
+      const int j = wave + (isA ? idx : idx - T::LoadsA) * kWaves;
       const int row = j * 16 + rsub;
       const int c = chunk_pos(row, p);
       const int off = ((int)(((isA ? m0 : n0) + row) * krow) + ks * 64 + c * 16) | (c >= 2 ? oor : 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rW, (lds_void*)(st + (isA ? 0 : kCodesA) + j * 1024), 16, off,
                                                0, 0, 0);
     } else {
-      const int q = wave;  // kWaveLoadsS == kWaves
-      const bool isA = q < kScaleA / 1024;
-      const int rt = isA ? q : q - kScaleA / 1024;
+      // scale piece q of the stage's scale bytes
+      constexpr int B = T::ScaleLoadBytes;
+      const int q = wave * T::LoadsS + (idx - T::LoadsA - T::LoadsW);
+      const int byte0 = q * B;                      // offset inside the scale part of the stage
+      const bool isA = byte0 < kScaleA;
+      const int rel = isA ? byte0 : byte0 - kScaleA;
+      const int rt = rel >> 10, part = rel & 1023;  // row tile, offset inside its 1 KiB block
       const int64_t rt_g = (isA ? m0 : n0) / 128 + rt;
-      const int cg = lane >> 5;
-      const int off = ((int)((rt_g * a.cgroups + (int64_t)ks * 2) * 512) + lane * 16) | (cg == 1 ? oor : 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rSA : rSW, (lds_void*)(st + kCodesA + kCodesW + q * 1024), 16,
-                                               off, 0, 0, 0);
+      const int lo = part + lane * (B / 64);        // this lane's bytes inside the block
+      const int off = ((int)((rt_g * a.cgroups + (int64_t)ks * 2) * 512) + lo) | (lo >= 512 ? oor : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rSA : rSW, (lds_void*)(st + kCodesA + kCodesW + byte0),
+                                               TileShape<FM, FN>::ScaleLoadBytes / 64, off, 0, 0, 0);
     }
   };
 
@@ -268,22 +281,23 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
   // Software pipeline. K step ks lives in LDS stage ks % 3, loaded two K steps
-  // ahead; the loads of step ks + 2 are spread over K16 steps 0..4 of step ks so
-  // that they issue between MFMAs. Within a K step, K16 step kk (0..7) uses codes
-  // of half kk / 4, dword kk % 4, and scale block kk / 2. While the MFMAs of step kk
-  // run, the fragments of step kk + 1 are dequantized into the other register set.
-  // The second-half codes are read at kk = 1. At kk = 6 every wave waits for its
-  // own loads of the next K step, the workgroup synchronises (which also frees the
-  // stage read in the previous K step for the next loads), and the next step's
-  // scales and first-half codes are read; they are dequantized at kk = 7. The body
-  // is instantiated without branches: the last two K steps are peeled.
+  // ahead; the loads of step ks + 2 are spread over the first K16 steps of step ks
+  // (two per K16 step) so that they issue between MFMAs. Within a K step, K16 step
+  // kk (0..7) uses codes of half kk / 4, dword kk % 4, and scale block kk / 2. While
+  // the MFMAs of step kk run, the fragments of step kk + 1 are dequantized into the
+  // other register set. The second-half codes are read at kk = 1. At kk = 6 every
+  // wave waits for its own loads of the next K step, the workgroup synchronises
+  // (which also frees the stage read in the previous K step for the next loads),
+  // and the next step's scales and first-half codes are read; they are dequantized
+  // at kk = 7. The body is instantiated without branches: the last two K steps are
+  // peeled.
   const int nks = a.ksteps;
 #pragma unroll
-  for (int idx = 0; idx < kLoadsPerWave; ++idx) issue_one(0, 0, idx);
+  for (int idx = 0; idx < kLoads; ++idx) issue_one(0, 0, idx);
   if (nks > 1) {
 #pragma unroll
-    for (int idx = 0; idx < kLoadsPerWave; ++idx) issue_one(1, 1, idx);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerWave);  // vmcnt(kLoadsPerWave): step 0 has landed
+    for (int idx = 0; idx < kLoads; ++idx) issue_one(1, 1, idx);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);  // vmcnt(kLoads): step 0 has landed
   } else {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
@@ -313,16 +327,16 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int cur = kk & 1, nxt = cur ^ 1;
-      if (loads && kk < 5) {
-        issue_one(ks + 2, far_stage, 2 * kk);
-        if (kk < 4) issue_one(ks + 2, far_stage, 2 * kk + 1);
+      if (loads) {
+        if (2 * kk < kLoads) issue_one(ks + 2, far_stage, 2 * kk);
+        if (2 * kk + 1 < kLoads) issue_one(ks + 2, far_stage, 2 * kk + 1);
       }
       if (kk == 1) read_codes(stage, 1, ca[1], cw[1]);  // second half, needed from step 4
       if (kk == 6 && next) {
         // kept in place: the reads must follow the barrier and lead their use by a
         // whole MFMA group
         __builtin_amdgcn_sched_barrier(0);
-        if (loads) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerWave);  // this step's batch may fly
+        if (loads) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);  // this step's batch may fly
         else __builtin_amdgcn_s_waitcnt(0x0F70);
         stage_barrier();
         read_scales(next_stage, nsa, nsw);
@@ -343,7 +357,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fw[cur][j], fa[cur][i], acc[j][i], 0, 0, 0);
-      interleave_hint();
+      interleave_hint<FM * FN, T::ValuPerMfma>();
     }
   };
 
@@ -387,14 +401,50 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // Tiles (256 x 256) are numbered m-band-major: band = 8 M-tiles, within a band M
+  // first. Workgroups [0, big_tiles) run tiles [0, big_tiles) whole, remapped so that
+  // each XCD (workgroups are dispatched round-robin over the 8 XCDs) owns one
+  // contiguous range of tiles. Workgroups past that run the remaining tiles as
+  // 128 x 128 quarters; they are dispatched last and fill the CUs that free up.
+  const int b = blockIdx.x;
+  int t, quarter = -1;
+  if (b < a.big_tiles) {
+    const int nb = a.big_tiles;
+    const int per = nb / 8, rem = nb % 8;
+    const int xcd = b % 8, idx = b / 8;
+    t = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  } else {
+    const int q = b - a.big_tiles;
+    t = a.big_tiles + q / 4;
+    quarter = q % 4;
+  }
+  const int ntiles = a.tiles_m * a.tiles_n;
+  if (t >= ntiles) return;
+  const int band = t / (kBandM * a.tiles_n);
+  const int in_band = t - band * kBandM * a.tiles_n;
+  const int band_m = (a.tiles_m - band * kBandM) < kBandM ? (a.tiles_m - band * kBandM) : kBandM;
+  const int tm = band * kBandM + in_band % band_m;
+  const int tn = in_band / band_m;
+  const int64_t m0 = (int64_t)tm * kTileBig, n0 = (int64_t)tn * kTileBig;
+  if (quarter < 0) {
+    run_tile<4, 4>(a, m0, n0, smem);
+  } else {
+    const int64_t qm0 = m0 + (quarter >> 1) * kTileQuarter, qn0 = n0 + (quarter & 1) * kTileQuarter;
+    if (qm0 >= a.m_pad || qn0 >= a.n) return;  // a quarter wholly past the padded output
+    run_tile<2, 2>(a, qm0, qn0, smem);
+  }
+}
+
 // ---- host side -----------------------------------------------------------------------------
 
-size_t gemm_smem_bytes() { return (size_t)kStages * kStageBytes; }
+size_t gemm_smem_bytes() { return (size_t)kStages * BigTile::StageBytes; }
 const void* gemm_kernel_ptr() { return (const void*)gemm_kernel; }
 
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
-                       hipStream_t stream) {
+                       int cu_count, hipStream_t stream) {
   GemmArgs args;
   args.aq = aq;
   args.as = as;
@@ -411,13 +461,18 @@ hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, co
   args.w_qbytes = (int)(n * (k / 2));
   args.a_sbytes = (int)(((m_pad + 127) / 128 * 128) * cpad);
   args.w_sbytes = (int)(((n + 127) / 128 * 128) * cpad);
-  args.tiles_m = (int)((m_pad + kTM - 1) / kTM);
-  args.tiles_n = (int)((n + kTN - 1) / kTN);
+  args.tiles_m = (int)((m_pad + kTileBig - 1) / kTileBig);
+  args.tiles_n = (int)((n + kTileBig - 1) / kTileBig);
   args.cgroups = (int)(cpad / 4);
   args.ksteps = (int)((k + kTK - 1) / kTK);
   const int ntiles = args.tiles_m * args.tiles_n;
   if (ntiles == 0) return hipSuccess;
-  gemm_kernel<<<dim3(ntiles), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);
+  // One workgroup per CU at a time. When the last round of whole tiles would hold
+  // at most a quarter of the CUs' worth, its tiles run as 128 x 128 quarters.
+  const int tail = cu_count > 0 ? ntiles % cu_count : 0;
+  args.big_tiles = (tail > 0 && ntiles > cu_count && 4 * tail <= cu_count) ? ntiles - tail : ntiles;
+  const int grid = args.big_tiles + 4 * (ntiles - args.big_tiles);
+  gemm_kernel<<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);
   return hipGetLastError();
 }
 

@@ -62,6 +62,26 @@ def test_small_shapes(gpu, m, n, k):
     run_path(w, gpu, None, 0)
 
 
+def test_tail_quarter_tiles(gpu):
+    """When the last round of 256 x 256 tiles would hold at most a quarter of the CUs'
+    worth, those tiles run as 128 x 128 quarters. The shape is chosen from the
+    device's CU count so that the split happens, with an M tail (quarters wholly and
+    partly past m_padded), an N tail and a half K step inside the quarters; every
+    output element is compared."""
+    import torch
+    cu = torch.cuda.get_device_properties(gpu).multi_processor_count
+    tiles_n = 17
+    tiles_m = (cu + cu // 16 + tiles_n - 1) // tiles_n
+    tiles = tiles_m * tiles_n
+    tail = tiles % cu
+    assert tiles > cu and 0 < tail and 4 * tail <= cu, (cu, tiles_m, tiles_n)
+    m = tiles_m * 256 - 96              # m_pad = m: the last quarter row is partly past it
+    n = tiles_n * 256 - 16
+    w = synth.Workload(f"tail_quarters_{m}x{n}", m=m, n=n, k=320, seed=17, swiglu=True)
+    _say(f"[tail] {cu} CUs: {tiles} tiles, {tail} run as quarters")
+    run_path(w, gpu, None, 0)
+
+
 def test_subnormal_scales(gpu):
     """Operands whose block scales are UE4M3 subnormals (E = 0) on both sides."""
     import torch

@@ -173,6 +173,18 @@ __device__ __forceinline__ void interleave_hint() {
   }
 }
 
+// the same, with NDS LDS reads and NVM global loads placed two per MFMA from the start
+template <int NMFMA, int NVALU, int NDS, int NVM>
+__device__ __forceinline__ void interleave_hint_mem() {
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // 1 MFMA
+    if (2 * i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads, two at a time
+    if (i < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global loads
+    __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);  // its share of VALU
+  }
+}
+
 // Workgroup barrier for the LDS pipeline. Every wave has already waited for its
 // own outstanding LDS reads and direct-to-LDS loads (explicit counters), so only
 // the s_barrier is needed; the empty asm keeps the compiler from moving LDS
@@ -333,15 +345,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
       }
       if (kk == 1) read_codes(stage, 1, ca[1], cw[1]);  // second half, needed from step 4
       if (kk == 6 && next) {
-        // kept in place: the reads must follow the barrier and lead their use by a
-        // whole MFMA group
+        // the barrier stays in place; the reads after it (held below it by its memory
+        // clobbers) are spread over this K16 step's first MFMAs and still lead their
+        // use at kk = 7 by a whole MFMA group
         __builtin_amdgcn_sched_barrier(0);
         if (loads) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);  // this step's batch may fly
         else __builtin_amdgcn_s_waitcnt(0x0F70);
         stage_barrier();
         read_scales(next_stage, nsa, nsw);
         read_codes(next_stage, 0, ca[0], cw[0]);
-        __builtin_amdgcn_sched_barrier(0);
       }
       if (kk < 7) {
         dequant_k(kk + 1, nxt);
@@ -357,7 +369,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
 #pragma unroll
         for (int i = 0; i < FM; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fw[cur][j], fa[cur][i], acc[j][i], 0, 0, 0);
-      interleave_hint<FM * FN, T::ValuPerMfma>();
+      if (kk == 6 && next) {
+        // the next step's LDS reads (after the barrier) spread over the first MFMAs
+        interleave_hint_mem<FM * FN, T::ValuPerMfma, (FM + FN) + 2, 0>();
+      } else {
+        interleave_hint<FM * FN, T::ValuPerMfma>();
+      }
     }
   };
 
@@ -374,30 +391,55 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
   kstep(ks, stage, false, false);
 
   // ---- epilogue: D[m, n] = RN_bf16(alpha * acc), alpha = g_a * g_w ----
+  // Each wave stages its tile in its own quarter of the (now idle) LDS, 64 rows at a
+  // time, then stores whole row segments: a store instruction writes 4 rows x 256 B
+  // (full tile) or 8 rows x 128 B (quarter tile) instead of 16-byte pieces of 32 rows.
   const float alpha = (*a.ga) * (*a.gw);
+  constexpr int kWaveCols = FN * 32, kRowBytes = kWaveCols * 2 + 16;  // padded against bank conflicts
+  constexpr int kChunksPerRow = kWaveCols / 8, kRowsPerStore = 64 / kChunksPerRow;
+  static_assert(64 * kRowBytes <= kStages * BigTile::StageBytes / kWaves, "staging fits the wave's LDS share");
+  unsigned char* stg = smem + wave * (kStages * BigTile::StageBytes / kWaves);
+  const int64_t wrow0 = m0 + wm * FM * 32, wcol0 = n0 + wn * FN * 32;
+  stage_barrier();  // every wave has finished reading the last K step's stage
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
+  for (int half = 0; half < FM / 2; ++half) {
+    // registers -> LDS: fragments i = 2 half, 2 half + 1 hold rows 64 half .. 64 half + 63
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t m = m0 + wm * FM * 32 + i * 32 + lr;
-      if (m >= a.m_pad) continue;
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * half + ii;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * FN * 32 + j * 32 + q * 8 + h * 4;
-        if (n >= a.n) continue;
-        bf16x2_t lo, hi;
-        lo[0] = (__bf16)(acc[j][i][q * 4 + 0] * alpha);
-        lo[1] = (__bf16)(acc[j][i][q * 4 + 1] * alpha);
-        hi[0] = (__bf16)(acc[j][i][q * 4 + 2] * alpha);
-        hi[1] = (__bf16)(acc[j][i][q * 4 + 3] * alpha);
-        uint32_t ul, uh;
-        __builtin_memcpy(&ul, &lo, 4);
-        __builtin_memcpy(&uh, &hi, 4);
-        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
-        u32x2_t v = {ul, uh};
-        *(u32x2_t*)(a.d + m * a.n + n) = v;
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16x2_t lo, hi;
+          lo[0] = (__bf16)(acc[j][i][q * 4 + 0] * alpha);
+          lo[1] = (__bf16)(acc[j][i][q * 4 + 1] * alpha);
+          hi[0] = (__bf16)(acc[j][i][q * 4 + 2] * alpha);
+          hi[1] = (__bf16)(acc[j][i][q * 4 + 3] * alpha);
+          uint32_t ul, uh;
+          __builtin_memcpy(&ul, &lo, 4);
+          __builtin_memcpy(&uh, &hi, 4);
+          typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+          const u32x2_t v = {ul, uh};
+          const int r = ii * 32 + lr, c = j * 32 + q * 8 + h * 4;
+          *(u32x2_t*)(stg + r * kRowBytes + c * 2) = v;
+        }
       }
     }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+    asm volatile("" ::: "memory");
+    // LDS -> global: lane L takes 8 columns of one row
+#pragma unroll
+    for (int it = 0; it < 64 / kRowsPerStore; ++it) {
+      const int r = it * kRowsPerStore + lane / kChunksPerRow, ch = lane % kChunksPerRow;
+      const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
+      const int64_t m = wrow0 + half * 64 + r, n = wcol0 + ch * 8;
+      if (m < a.m_pad && n < a.n) *(u32x4_t*)(a.d + m * a.n + n) = v;
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next half overwrites
+    asm volatile("" ::: "memory");
   }
 }
 

@@ -195,6 +195,62 @@ def only_producer(w, args, dev) -> int:
     return 0
 
 
+SHAPES = ("fc2_canonical", "qkv", "qkv_pages", "attn_out", "fc1")
+
+
+def shapes(args, dev) -> int:
+    """Producer + GEMM on each projection shape (seeded inputs of that shape; weights
+    quantized once outside the timing). One JSON line per shape."""
+    import statistics
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    import synth
+    from tests import parity
+    stream = torch.cuda.current_stream()
+    for name in SHAPES:
+        w = synth.BY_NAME[name]
+        acts = w.activations()
+        x = parity.to_device_bf16(acts[0], dev)
+        u = parity.to_device_bf16(acts[1], dev) if w.swiglu else None
+        del acts
+        wt = parity.to_device_bf16(w.weight(), dev)
+        a = nv.empty_nvfp4(w.m, w.k, dev)
+        wq = nv.empty_nvfp4(w.n, w.k, dev)
+        nv.nvfp4_quantize(wt, out=wq)
+        d = torch.empty((w.m_pad, w.n), dtype=torch.bfloat16, device=dev)
+
+        def producer():
+            if w.swiglu:
+                nv.nvfp4_quantize_swiglu(x, u, out=a)
+            else:
+                nv.nvfp4_quantize(x, out=a)
+
+        for _ in range(args.warmup):
+            producer()
+            nv.nvfp4_gemm_bf16out(a, wq, out=d)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for e in evs:
+            e[0].record(stream)
+            producer()
+            e[1].record(stream)
+            nv.nvfp4_gemm_bf16out(a, wq, out=d)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        t_prod = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs)
+        t_gemm = statistics.fmean(e[1].elapsed_time(e[2]) for e in evs)
+        tflops = w.gemm_flops / (t_gemm * 1e-3) / 1e12
+        pbytes = producer_bytes(w.m, w.k, w.swiglu)
+        print(json.dumps({"mode": "shapes", "workload": name, "m": w.m, "n": w.n, "k": w.k,
+                          "producer": "swiglu" if w.swiglu else "plain", "producer_ms": round(t_prod, 4),
+                          "producer_gbs": round(pbytes / (t_prod * 1e-3) / 1e9, 1), "gemm_ms": round(t_gemm, 4),
+                          "gemm_tflops": round(tflops, 2), "gemm_frac_of_peak": round(tflops / PEAK_MFMA_TFLOPS, 4),
+                          "steps": args.steps}), flush=True)
+        del x, u, wt, a, wq, d
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +261,8 @@ def main() -> int:
     ap.add_argument("--only-gemm", action="store_true",
                     help="time the GEMM alone on seeded random NVFP4 operand bytes (no producer launch in "
                          "the process; used for profiler counter runs)")
+    ap.add_argument("--shapes", action="store_true",
+                    help="producer + GEMM on every projection shape, one JSON line each")
     ap.add_argument("--only-producer", action="store_true",
                     help="time the producer alone on the workload's seeded inputs (no GEMM launch)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -230,6 +288,8 @@ def main() -> int:
         return only_gemm(w, args, dev)
     if args.only_producer:
         return only_producer(w, args, dev)
+    if args.shapes:
+        return shapes(args, dev)
 
     t0 = time.perf_counter()
     acts = w.activations()

@@ -28,7 +28,7 @@ TAG_UP = 2
 TAG_WEIGHT = 3
 TAG_OUTLIER = 5
 TAG_PLAIN_X = {"qkv": 11, "attn_out": 21, "fc1": 31}
-TAG_PLAIN_W = {"qkv": 12, "attn_out": 22, "fc1": 32}
+TAG_PLAIN_W = {"qkv": 12, "attn_out": 22, "fc1": 32, "qkv_pages": 42}
 
 
 def default_threads() -> int:
@@ -168,9 +168,13 @@ ATTN_OUT = Workload("attn_out", m=37810, n=5376, k=7168, seed=7, swiglu=False,
                     tag_x=TAG_PLAIN_X["attn_out"], tag_w=TAG_PLAIN_W["attn_out"])
 FC1 = Workload("fc1", m=37810, n=28672, k=5376, seed=7, swiglu=False,
                tag_x=TAG_PLAIN_X["fc1"], tag_w=TAG_PLAIN_W["fc1"])
+# The QKV projection at the width the pages' kernel grid implies (168 N-tiles of 128:
+# 21,504 = 3 x 7,168), beside the configured 16,128.
+QKV_PAGES = Workload("qkv_pages", m=37810, n=21504, k=5376, seed=7, swiglu=False,
+                     tag_x=TAG_PLAIN_X["qkv"], tag_w=TAG_PLAIN_W["qkv_pages"])
 RAGGED_M: List[int] = [37711, 37725, 37742, 37774, 37809, 37838, 37966, 38222]
 RAGGED = [Workload(f"fc2_ragged_m{m}", m=m, n=5376, k=14336, seed=100 + i, swiglu=True, outliers=True)
           for i, m in enumerate(RAGGED_M)]
-PLAIN = [QKV, ATTN_OUT, FC1]
+PLAIN = [QKV, ATTN_OUT, FC1, QKV_PAGES]
 ALL = [TINY, MID, FC2] + PLAIN + RAGGED
 BY_NAME = {w.name: w for w in ALL}

@@ -118,7 +118,8 @@ def test_gemm_deterministic_and_prefix_invariant(gpu):
     assert torch.equal(d1[:512], d3)
 
 
-@pytest.mark.parametrize("name,rows", [("mid_fc2_slice", 1024), ("qkv", 1024), ("attn_out", 1024), ("fc1", 512)])
+@pytest.mark.parametrize("name,rows", [("mid_fc2_slice", 1024), ("qkv", 1024), ("attn_out", 1024), ("fc1", 512),
+                                       ("qkv_pages", 512)])
 def test_large_configs(gpu, name, rows):
     run_path(synth.BY_NAME[name], gpu, rows, 17)
 

@@ -15,16 +15,15 @@
 //   scales  = 512-byte tiles of 128 rows x 4 scale columns, padding zero
 //
 // Structure: a persistent grid (co-resident through a cooperative launch, one
-// 16-wave workgroup per CU, the bf16 SiLU table in LDS) walks work items of 128 rows
-// x 256 columns; each lane owns one 16-element block of a row per step (a wave
-// covers 4 rows x 16 blocks). Pass 1 reduces |y| with the next item's loads in
+// 16-wave workgroup per CU, the bf16 SiLU table in LDS) walks work items of 64 rows
+// x 512 columns; each lane owns one 16-element block of a row per step (a wave
+// covers 2 rows x 32 blocks). Pass 1 reduces |y| with the next item's loads in
 // flight (wavefront shuffles, LDS across waves, one agent-scope atomic max per
 // workgroup); a grid barrier publishes amax; pass 2 walks the items in reverse order
 // (so the rows read last in pass 1, still in the memory-side cache, are read first),
-// recomputes y, and stores QDATA rows (16 lanes store one full 128-byte row segment)
+// recomputes y, and stores QDATA rows (32 lanes store one full 256-byte row segment)
 // and each scale byte at its place in its 512-byte tile. Pass 2 has no workgroup
-// barrier, so the 16 waves drift apart and hide each other's load latency; each
-// tile's bytes all come from the one workgroup that owns its item.
+// barrier, so the 16 waves drift apart and hide each other's load latency.
 //
 // Exactness: every rounding decision equals the exact one.
 //  - y: a product of two bf16 values is exact in fp32 when it is >= 2^-126; a block
@@ -44,9 +43,15 @@ namespace nvfp4 {
 
 constexpr int kProdThreads = 1024;   // 16 waves, four per SIMD
 constexpr int kWaves = kProdThreads / 64;
-constexpr int kItemRows = 128;       // one scale row-tile
-constexpr int kItemCols = 256;       // 16 blocks of 16 columns: one 128-byte QDATA segment per row
-constexpr int kRowsPerStep = kWaves * 4;  // lane = (row of 4) x (block of 16)
+// A work item is 64 rows x 512 columns: each lane owns one 16-column block of a row
+// per step, a wave covers 2 rows x 32 blocks (1 KB of each bf16 input row, one
+// 256-byte QDATA row segment), and the 16 waves cover the 64 rows in 2 steps. Runs
+// of 1 KB per row keep HBM page use and the spread of addresses over the XCDs even.
+constexpr int kItemCols = 512;
+constexpr int kLanesPerRow = kItemCols / 16;
+constexpr int kWaveRows = 64 / kLanesPerRow;
+constexpr int kRowsPerStep = kWaves * kWaveRows;
+constexpr int kItemRows = 2 * kRowsPerStep;
 constexpr int kRedBytes = 128;       // wave maxima and two broadcast slots
 constexpr int kSteps = kItemRows / kRowsPerStep;
 
@@ -239,8 +244,8 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int r4 = lane >> 4;    // row within the wave's 4 rows of a step
-  const int blk = lane & 15;   // 16-column block of the 256-column segment
+  const int r4 = lane / kLanesPerRow;   // row within the wave's rows of a step
+  const int blk = lane % kLanesPerRow;  // 16-column block of the item's column segment
   const int nitems = a.items_m * a.items_k;
 
   if (SWIGLU) {
@@ -257,7 +262,7 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
     const int64_t col = (int64_t)kt * kItemCols + blk * 16;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int64_t row = (int64_t)rt * kItemRows + s * kRowsPerStep + wave * 4 + r4;
+      const int64_t row = (int64_t)rt * kItemRows + s * kRowsPerStep + wave * kWaveRows + r4;
       const bool ok = row < a.m && col < a.k;
       const u32x4_t z = {0u, 0u, 0u, 0u};
       const u32x4_t* px = (const u32x4_t*)(a.x + row * a.ldx + col);
@@ -398,7 +403,7 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
     const int64_t col = (int64_t)kt * kItemCols + blk * 16;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int lrow = s * kRowsPerStep + wave * 4 + r4;
+      const int lrow = s * kRowsPerStep + wave * kWaveRows + r4;
       const int64_t row = (int64_t)rt * kItemRows + lrow;
       uint32_t yb[8];
       block_y<SWIGLU>(gv[s], uv[s], tab, yb);
@@ -449,11 +454,11 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
         const u32x2_t v = {clo0, clo1};
         *(u32x2_t*)(a.qdata + row * qrow_bytes + col / 2) = v;
       }
-      // the scale byte at its place in the 128 x 4 tile (rows past m_pad hold zero);
-      // the byte stores of the workgroup's 16 waves fill each 512-byte tile
+      // the scale byte at its place in its 128 x 4 tile (rows past m_pad hold zero)
       if (col < a.k) {
-        const int64_t tile = (int64_t)rt * (a.cpad / 4) + (int64_t)kt * 4 + (blk >> 2);
-        a.scales[tile * 512 + (lrow & 31) * 16 + ((lrow >> 5) & 3) * 4 + (blk & 3)] = (uint8_t)S;
+        const int64_t bc = (int64_t)kt * kLanesPerRow + blk;  // block column
+        const int64_t tile = (row >> 7) * (a.cpad / 4) + (bc >> 2);
+        a.scales[tile * 512 + (row & 31) * 16 + ((row >> 5) & 3) * 4 + (bc & 3)] = (uint8_t)S;
       }
     }
   };

@@ -51,6 +51,8 @@ def _load():
         "oracle_scale_offset": (_I64, [_I64, _I64, _I64]),
         "oracle_quantize": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P,
                                            ctypes.c_int]),
+        "oracle_quantize_amax": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_double, _P, _P,
+                                                _P, ctypes.c_int]),
         "oracle_gemm_rows": (ctypes.c_int, [_P, _P, _I64, ctypes.c_float, _P, _P, _I64,
                                             ctypes.c_float, _I64, _P, _I64, _P, ctypes.c_int]),
     }
@@ -152,6 +154,27 @@ def quantize(x: np.ndarray, up: Optional[np.ndarray] = None, m: Optional[int] = 
         raise ValueError(f"oracle_quantize failed ({rc})")
     if return_y:
         return qdata, scales, float(g[0]), y
+    return qdata, scales, float(g[0])
+
+
+def quantize_amax(x: np.ndarray, up: Optional[np.ndarray], amax: float, m: Optional[int] = None,
+                  threads: Optional[int] = None):
+    """O11: quantize y = swiglu(x, up) (up given) or y = x with the caller's amax
+    instead of max |y|. Returns (qdata, scales, g) as ``quantize``."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    m = x.shape[0] if m is None else m
+    k = x.shape[1]
+    if up is not None:
+        up = np.ascontiguousarray(up, dtype=np.uint16)
+        assert up.shape[1] == k and up.shape[0] >= m
+    qdata = np.empty((padded_rows(m), k // 2), dtype=np.uint8)
+    scales = np.empty(scale_bytes(m, k), dtype=np.uint8)
+    g = np.zeros(1, dtype=np.float32)
+    rc = _load().oracle_quantize_amax(x.ctypes.data, k, None if up is None else up.ctypes.data, k, m, k,
+                                      float(amax), qdata.ctypes.data, scales.ctypes.data, g.ctypes.data,
+                                      threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_amax failed ({rc})")
     return qdata, scales, float(g[0])
 
 

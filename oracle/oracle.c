@@ -29,6 +29,8 @@
  *                                + ((r>>5)&3)*4 + (c&3); uncovered bytes zero
  *   O10 GEMM          RN_bf16(g_a g_w sum_b v(SA) v(SW) sum_k e2m1 e2m1),
  *                     evaluated exactly in integers
+ *   O11 given amax    O4-O8 with amax supplied by the caller (single-read
+ *                     producer); a block above v(126) * 6 * g saturates
  *
  * Pins (tests/test_oracle_*.py): O1 against 50-digit decimal arithmetic for
  * all 65,536 inputs; O2 against torch's CPU bf16 multiply; O4-O6 against exact
@@ -219,9 +221,9 @@ int64_t oracle_scale_offset(int64_t r, int64_t c, int64_t cpad) {
  *   *g_out the fp32 global scale
  * y_out (optional, [m, k] bf16 bits) receives y for inspection.
  */
-int oracle_quantize(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t ldu, int64_t m,
-                    int64_t k, uint8_t* qdata, uint8_t* scales, float* g_out, uint16_t* y_out,
-                    int nthreads) {
+static int quantize_core(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t ldu, int64_t m,
+                         int64_t k, const double* amax_given, uint8_t* qdata, uint8_t* scales, float* g_out,
+                         uint16_t* y_out, int nthreads) {
   if (!x || !qdata || !scales || !g_out || m < 0 || k <= 0 || k % 16 != 0 || ldx < k ||
       (up && ldu < k))
     return OR_EINVAL;
@@ -264,12 +266,16 @@ int oracle_quantize(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t 
     return OR_ENONFINITE;
   }
 
-  /* O3 */
+  /* O3, or the caller's amax (O11) */
   double amax = 0.0;
+  if (amax_given) {
+    amax = *amax_given;
+  } else {
 #pragma omp parallel for schedule(static) num_threads(nthreads) reduction(max : amax)
-  for (int64_t i = 0; i < m * k; ++i) {
-    double a = fabs(bf16_to_double(y[i]));
-    if (a > amax) amax = a;
+    for (int64_t i = 0; i < m * k; ++i) {
+      double a = fabs(bf16_to_double(y[i]));
+      if (a > amax) amax = a;
+    }
   }
   /* O4 */
   const float g = oracle_global_scale(amax);
@@ -296,6 +302,7 @@ int oracle_quantize(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t 
         if (av > bmax) bmax = av;
       }
       uint8_t s = oracle_block_scale(bmax, g);
+      if (s == 0xFF) s = 126; /* O11: a given amax below the block maximum saturates */
       scales[oracle_scale_offset(r, b, cpad)] = s;
       uint8_t code[16];
       for (int t = 0; t < 16; ++t) {
@@ -316,6 +323,25 @@ int oracle_quantize(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t 
   free(y);
   *g_out = g;
   return OR_OK;
+}
+
+int oracle_quantize(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t ldu, int64_t m,
+                    int64_t k, uint8_t* qdata, uint8_t* scales, float* g_out, uint16_t* y_out,
+                    int nthreads) {
+  return quantize_core(x, ldx, up, ldu, m, k, NULL, qdata, scales, g_out, y_out, nthreads);
+}
+
+/*
+ * O11: the single-read producer. Identical to oracle_quantize except that amax
+ * is the caller's value instead of O3's maximum (g = O4(amax)). When that value
+ * is below a block's maximum, no byte satisfies O5; the block then takes the
+ * largest finite byte, 126, and O6 saturates its codes at 6 (a reading: the pages
+ * always derive amax from the data, so they never meet this case).
+ */
+int oracle_quantize_amax(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t ldu, int64_t m,
+                         int64_t k, double amax, uint8_t* qdata, uint8_t* scales, float* g_out,
+                         int nthreads) {
+  return quantize_core(x, ldx, up, ldu, m, k, &amax, qdata, scales, g_out, NULL, nthreads);
 }
 
 /* ---------- GEMM ------------------------------------------------------------- */

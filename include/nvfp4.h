@@ -125,6 +125,33 @@ int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_
 int nvfp4_quantize(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, void* qdata_dev,
                    void* scales_dev, float* global_scale_dev, void* workspace_dev, void* stream);
 
+/*
+ * Single-read producer: nvfp4_quantize_swiglu with the tensor amax supplied by the
+ * caller, so every input byte is read once. The component-2 summary's conclusions
+ * name the global scale as the dependency an exact fused producer must synchronize
+ * on, and the boundary between two NVFP4 stages as the place where traffic is worth
+ * removing; here the upstream stage that writes gate and up (e.g. the FC1 GEMM
+ * epilogue) also produces max |y|.
+ *
+ * amax_dev : device float, read on the device: max |y| over the m logical rows
+ *            (y as defined above), or any finite value above it; 4-byte aligned.
+ *            g = amax / 2688 rounded up to FP32 is written to global_scale_dev;
+ *            a NaN, zero or negative amax gives g = 0.
+ * Every other argument, layout and output as nvfp4_quantize_swiglu; no workspace.
+ * An amax below the true maximum is the caller's error; the result is still
+ * defined: a block whose maximum exceeds v(126) * 6 * g gets scale byte 126 and
+ * its codes saturate at +-6 (magnitude code 7). One ordinary (non-cooperative)
+ * launch; nvfp4_init sizes its grid as for the two-pass producer.
+ */
+int nvfp4_quantize_swiglu_amax(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up,
+                               int64_t m, int64_t k, const float* amax_dev, void* qdata_dev,
+                               void* scales_dev, float* global_scale_dev, void* stream);
+
+/* Single-read plain quantization (y = x) with the caller's amax: the contract of
+ * nvfp4_quantize_swiglu_amax with one bf16 [rows, k] input of row stride ld_x. */
+int nvfp4_quantize_amax(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, const float* amax_dev,
+                        void* qdata_dev, void* scales_dev, float* global_scale_dev, void* stream);
+
 /* ---- stage G: GEMM ---------------------------------------------------------------------- */
 
 /*

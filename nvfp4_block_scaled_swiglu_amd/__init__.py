@@ -51,6 +51,8 @@ SIGNATURES = {
     "nvfp4_init": (_INT, []),
     "nvfp4_quantize_swiglu": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_quantize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "nvfp4_quantize_swiglu_amax": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "nvfp4_quantize_amax": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_gemm_bf16out": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "nvfp4_silu_bf16": (_INT, [_P, _P, _I64, _P]),
     "nvfp4_status_string": (ctypes.c_char_p, [_INT]),
@@ -230,6 +232,41 @@ def nvfp4_quantize(x, out: Optional[Nvfp4Tensor] = None, rows: Optional[int] = N
     ws = _workspace(x.device, sh) if workspace is None else workspace
     _call("nvfp4_quantize", x.data_ptr(), x.stride(0), rows, k, out.qdata.data_ptr(), out.scales.data_ptr(),
           out.global_scale.data_ptr(), ws.data_ptr(), sh)
+    return out
+
+
+def _amax_ptr(amax) -> int:
+    import torch
+    if not isinstance(amax, torch.Tensor) or amax.dtype != torch.float32 or not amax.is_cuda or amax.numel() < 1:
+        raise ValueError("amax must be a float32 CUDA tensor holding at least one element")
+    return amax.data_ptr()
+
+
+def nvfp4_quantize_swiglu_amax(gate, up, amax, out: Optional[Nvfp4Tensor] = None, m: Optional[int] = None,
+                               stream=None) -> Nvfp4Tensor:
+    """Single-read SwiGLU -> NVFP4 with the caller's tensor amax (a device float32 scalar)."""
+    _bf16_2d(gate, "gate")
+    _bf16_2d(up, "up")
+    m = gate.shape[0] if m is None else m
+    k = gate.shape[1]
+    if up.shape[1] != k or up.shape[0] < m or gate.shape[0] < m:
+        raise ValueError("gate/up shapes disagree")
+    out = empty_nvfp4(m, k, gate.device) if out is None else out
+    _call("nvfp4_quantize_swiglu_amax", gate.data_ptr(), gate.stride(0), up.data_ptr(), up.stride(0), m, k,
+          _amax_ptr(amax), out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(),
+          _stream_handle(stream))
+    return out
+
+
+def nvfp4_quantize_amax(x, amax, out: Optional[Nvfp4Tensor] = None, rows: Optional[int] = None,
+                        stream=None) -> Nvfp4Tensor:
+    """Single-read plain NVFP4 quantization with the caller's tensor amax."""
+    _bf16_2d(x, "x")
+    rows = x.shape[0] if rows is None else rows
+    k = x.shape[1]
+    out = empty_nvfp4(rows, k, x.device) if out is None else out
+    _call("nvfp4_quantize_amax", x.data_ptr(), x.stride(0), rows, k, _amax_ptr(amax), out.qdata.data_ptr(),
+          out.scales.data_ptr(), out.global_scale.data_ptr(), _stream_handle(stream))
     return out
 
 

@@ -19,11 +19,12 @@ hipError_t silu_table_address(const uint16_t** p);
 hipError_t launch_silu_table_init(hipStream_t stream);
 hipError_t launch_silu_apply(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
 size_t producer_smem_bytes(bool swiglu);
-const void* producer_kernel_ptr(bool swiglu);
+const void* producer_kernel_ptr(bool swiglu, bool given);
 int producer_block_threads();
 hipError_t launch_producer(bool swiglu, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
                            int64_t m, int64_t k, uint8_t* qdata, uint8_t* scales, float* gout,
-                           void* workspace, const uint16_t* silu_table, int max_blocks, hipStream_t stream);
+                           const float* amax_in, void* workspace, const uint16_t* silu_table, int max_blocks,
+                           hipStream_t stream);
 size_t gemm_smem_bytes();
 const void* gemm_kernel_ptr();
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
@@ -92,11 +93,13 @@ int ensure_device(DeviceState** out) {
 
   // kernels with more than 64 KiB of dynamic LDS must opt in
   for (int sw = 0; sw < 2; ++sw) {
-    e = hipFuncSetAttribute(nvfp4::producer_kernel_ptr(sw != 0), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)nvfp4::producer_smem_bytes(sw != 0));
-    if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer LDS attribute: %s", hipGetErrorString(e));
+    for (int given = 0; given < 2; ++given) {
+      e = hipFuncSetAttribute(nvfp4::producer_kernel_ptr(sw != 0, given != 0),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)nvfp4::producer_smem_bytes(sw != 0));
+      if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer LDS attribute: %s", hipGetErrorString(e));
+    }
     int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nvfp4::producer_kernel_ptr(sw != 0),
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nvfp4::producer_kernel_ptr(sw != 0, false),
                                                      nvfp4::producer_block_threads(),
                                                      nvfp4::producer_smem_bytes(sw != 0));
     if (e != hipSuccess || per_cu < 1)
@@ -122,13 +125,15 @@ int ensure_device(DeviceState** out) {
   return NVFP4_OK;
 }
 
+// ws: the workspace of the two-pass producer, or the caller's amax of the single-pass one
 int check_quant_args(const void* x, int64_t ldx, const void* u, int64_t ldu, bool swiglu, int64_t m, int64_t k,
-                     const void* qdata, const void* scales, const float* g, const void* ws) {
+                     const void* qdata, const void* scales, const float* g, const void* ws, bool given) {
   if (!g) return fail(NVFP4_ERR_INVALID_ARG, "null global-scale pointer");
   // with no rows nothing is read or written except the global scale
   if (m != 0 && (!x || (swiglu && !u) || !qdata || !scales))
     return fail(NVFP4_ERR_INVALID_ARG, "null input or output pointer");
-  if (!ws) return fail(NVFP4_ERR_WORKSPACE, "null workspace");
+  if (given && !ws) return fail(NVFP4_ERR_INVALID_ARG, "null amax pointer");
+  if (!given && !ws) return fail(NVFP4_ERR_WORKSPACE, "null workspace");
   if (m < 0 || k <= 0) return fail(NVFP4_ERR_INVALID_ARG, "bad shape m=%lld k=%lld", (long long)m, (long long)k);
   if (k % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k=%lld is not a multiple of 64", (long long)k);
   if (ldx < k || (swiglu && ldu < k))
@@ -137,8 +142,8 @@ int check_quant_args(const void* x, int64_t ldx, const void* u, int64_t ldu, boo
   if (ldx % 8 != 0 || (swiglu && ldu % 8 != 0))
     return fail(NVFP4_ERR_MISALIGNED, "row strides must be multiples of 8 elements");
   if (!aligned16(x) || (swiglu && !aligned16(u)) || !aligned16(qdata) || !aligned16(scales) || ((uintptr_t)g & 3u) ||
-      !aligned16(ws))
-    return fail(NVFP4_ERR_MISALIGNED, "pointers must be 16-byte aligned (global scale 4-byte)");
+      (given ? ((uintptr_t)ws & 3u) != 0 : !aligned16(ws)))
+    return fail(NVFP4_ERR_MISALIGNED, "pointers must be 16-byte aligned (global scale and amax 4-byte)");
   const int64_t rows_pad = (m + 15) / 16 * 16;
   const int64_t srows = (rows_pad + 127) / 128 * 128;
   if (srows / 128 * ((k + 255) / 256) > (int64_t)1 << 30)
@@ -167,15 +172,16 @@ int nvfp4_init(void) {
   return rc == NVFP4_OK ? ok() : rc;
 }
 
-static int quantize_common(bool swiglu, const void* x, int64_t ldx, const void* u, int64_t ldu, int64_t m, int64_t k,
-                           void* qdata, void* scales, float* g, void* ws, void* stream) {
-  int rc = check_quant_args(x, ldx, u, ldu, swiglu, m, k, qdata, scales, g, ws);
+static int quantize_common(bool swiglu, bool given, const void* x, int64_t ldx, const void* u, int64_t ldu,
+                           int64_t m, int64_t k, void* qdata, void* scales, float* g, const float* amax, void* ws,
+                           void* stream) {
+  int rc = check_quant_args(x, ldx, u, ldu, swiglu, m, k, qdata, scales, g, given ? (const void*)amax : ws, given);
   if (rc != NVFP4_OK) return rc;
   DeviceState* st = nullptr;
   rc = ensure_device(&st);
   if (rc != NVFP4_OK) return rc;
   hipError_t e = nvfp4::launch_producer(swiglu, (const uint16_t*)x, ldx, (const uint16_t*)u, ldu, m, k,
-                                        (uint8_t*)qdata, (uint8_t*)scales, g, ws, st->silu_table,
+                                        (uint8_t*)qdata, (uint8_t*)scales, g, amax, ws, st->silu_table,
                                         swiglu ? st->producer_blocks_swiglu : st->producer_blocks_plain,
                                         (hipStream_t)stream);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer launch: %s", hipGetErrorString(e));
@@ -185,14 +191,27 @@ static int quantize_common(bool swiglu, const void* x, int64_t ldx, const void* 
 int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up, int64_t m,
                           int64_t k, void* qdata_dev, void* scales_dev, float* global_scale_dev, void* workspace_dev,
                           void* stream) {
-  return quantize_common(true, gate_dev, ld_gate, up_dev, ld_up, m, k, qdata_dev, scales_dev, global_scale_dev,
-                         workspace_dev, stream);
+  return quantize_common(true, false, gate_dev, ld_gate, up_dev, ld_up, m, k, qdata_dev, scales_dev, global_scale_dev,
+                         nullptr, workspace_dev, stream);
+}
+
+int nvfp4_quantize_swiglu_amax(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up, int64_t m,
+                               int64_t k, const float* amax_dev, void* qdata_dev, void* scales_dev,
+                               float* global_scale_dev, void* stream) {
+  return quantize_common(true, true, gate_dev, ld_gate, up_dev, ld_up, m, k, qdata_dev, scales_dev, global_scale_dev,
+                         amax_dev, nullptr, stream);
 }
 
 int nvfp4_quantize(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, void* qdata_dev, void* scales_dev,
                    float* global_scale_dev, void* workspace_dev, void* stream) {
-  return quantize_common(false, x_dev, ld_x, nullptr, 0, rows, k, qdata_dev, scales_dev, global_scale_dev,
-                         workspace_dev, stream);
+  return quantize_common(false, false, x_dev, ld_x, nullptr, 0, rows, k, qdata_dev, scales_dev, global_scale_dev,
+                         nullptr, workspace_dev, stream);
+}
+
+int nvfp4_quantize_amax(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, const float* amax_dev,
+                        void* qdata_dev, void* scales_dev, float* global_scale_dev, void* stream) {
+  return quantize_common(false, true, x_dev, ld_x, nullptr, 0, rows, k, qdata_dev, scales_dev, global_scale_dev,
+                         amax_dev, nullptr, stream);
 }
 
 int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,

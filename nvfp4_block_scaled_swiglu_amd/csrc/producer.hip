@@ -66,6 +66,7 @@ struct ProducerArgs {
   uint8_t* qdata;
   uint8_t* scales;
   float* gout;
+  const float* amax_in;  // caller-supplied amax (single-pass variant), else unused
   ProducerWorkspace* ws;
   const uint16_t* silu_table;
 };
@@ -235,7 +236,9 @@ __device__ __forceinline__ void block_mag_range(const uint32_t (&yb)[8], uint32_
   mn = lo.x < lo.y ? lo.x : lo.y;
 }
 
-template <bool SWIGLU>
+// GIVEN: the tensor amax comes from the caller (a device float); pass 1 and the grid
+// barrier are skipped and the launch needs no co-residency.
+template <bool SWIGLU, bool GIVEN>
 __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint32_t* red = (uint32_t*)smem;                          // wave maxima + two broadcast slots
@@ -276,114 +279,119 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
     }
   };
 
-  // ---------------- pass 1: absmax ----------------
-  uint32_t local_bits = 0;  // fp32 bits of a non-negative value
-  auto absmax_item = [&](const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
+  float amax;
+  if constexpr (GIVEN) {
+    amax = a.amax_in[0];
+  } else {
+    // ---------------- pass 1: absmax ----------------
+    uint32_t local_bits = 0;  // fp32 bits of a non-negative value
+    auto absmax_item = [&](const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
+      for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const uint32_t gw = gv[s][w >> 2][w & 3];
-        if (SWIGLU) {
-          const uint32_t uw = uv[s][w >> 2][w & 3];
-          const float s0 = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16);
-          const float s1 = __uint_as_float((uint32_t)tab[gw >> 16] << 16);
-          const float p0 = fabsf(s0 * __uint_as_float(uw << 16));
-          const float p1 = fabsf(s1 * __uint_as_float(uw & 0xFFFF0000u));
-          const uint32_t b = __float_as_uint(fmaxf(p0, p1));
-          local_bits = b > local_bits ? b : local_bits;
-        } else {
-          const uint32_t m0 = gw & 0x7FFFu, m1 = (gw >> 16) & 0x7FFFu;
-          const uint32_t b = (m0 > m1 ? m0 : m1) << 16;
-          local_bits = b > local_bits ? b : local_bits;
+        for (int w = 0; w < 8; ++w) {
+          const uint32_t gw = gv[s][w >> 2][w & 3];
+          if (SWIGLU) {
+            const uint32_t uw = uv[s][w >> 2][w & 3];
+            const float s0 = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16);
+            const float s1 = __uint_as_float((uint32_t)tab[gw >> 16] << 16);
+            const float p0 = fabsf(s0 * __uint_as_float(uw << 16));
+            const float p1 = fabsf(s1 * __uint_as_float(uw & 0xFFFF0000u));
+            const uint32_t b = __float_as_uint(fmaxf(p0, p1));
+            local_bits = b > local_bits ? b : local_bits;
+          } else {
+            const uint32_t m0 = gw & 0x7FFFu, m1 = (gw >> 16) & 0x7FFFu;
+            const uint32_t b = (m0 > m1 ? m0 : m1) << 16;
+            local_bits = b > local_bits ? b : local_bits;
+          }
         }
       }
+    };
+    {
+      // the next item's loads are in flight while the current item is reduced
+      u32x4_t gA[kSteps][2], uA[kSteps][2], gB[kSteps][2], uB[kSteps][2];
+      int item = blockIdx.x;
+      if (item < nitems) load_item(item, gA, uA);
+      while (item < nitems) {
+        const int n1 = item + (int)gridDim.x;
+        if (n1 < nitems) load_item(n1, gB, uB);
+        absmax_item(gA, uA);
+        item = n1;
+        if (item >= nitems) break;
+        const int n2 = item + (int)gridDim.x;
+        if (n2 < nitems) load_item(n2, gA, uA);
+        absmax_item(gB, uB);
+        item = n2;
+      }
     }
-  };
-  {
-    // the next item's loads are in flight while the current item is reduced
-    u32x4_t gA[kSteps][2], uA[kSteps][2], gB[kSteps][2], uB[kSteps][2];
-    int item = blockIdx.x;
-    if (item < nitems) load_item(item, gA, uA);
-    while (item < nitems) {
-      const int n1 = item + (int)gridDim.x;
-      if (n1 < nitems) load_item(n1, gB, uB);
-      absmax_item(gA, uA);
-      item = n1;
-      if (item >= nitems) break;
-      const int n2 = item + (int)gridDim.x;
-      if (n2 < nitems) load_item(n2, gA, uA);
-      absmax_item(gB, uB);
-      item = n2;
+    // workgroup max of the unrounded |products| (SwiGLU) or of |x|
+    bool needs_exact = false;
+    {
+      uint32_t wmax = wave_max_u32(local_bits);
+      if (lane == 0) red[wave] = wmax;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t v = 0;
+        for (int i = 0; i < kProdThreads / 64; ++i) v = red[i] > v ? red[i] : v;
+        red[kWaves] = v;
+      }
+      __syncthreads();
+      local_bits = red[kWaves];
+      // A product below 2^-126 may have been rounded in fp32; if this workgroup's
+      // maximum is such a product, redo its elements exactly (never taken for
+      // inputs whose absmax is a normal number).
+      needs_exact = SWIGLU && local_bits != 0 && local_bits < 0x00800000u;
+      __syncthreads();
     }
-  }
-  // workgroup max of the unrounded |products| (SwiGLU) or of |x|
-  bool needs_exact = false;
-  {
-    uint32_t wmax = wave_max_u32(local_bits);
-    if (lane == 0) red[wave] = wmax;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t v = 0;
-      for (int i = 0; i < kProdThreads / 64; ++i) v = red[i] > v ? red[i] : v;
-      red[kWaves] = v;
+    if (SWIGLU && needs_exact) {
+      uint32_t best = 0;  // bf16 magnitude bits
+      for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+        u32x4_t gv[kSteps][2], uv[kSteps][2];
+        load_item(item, gv, uv);
+        for (int s = 0; s < kSteps; ++s)
+          for (int j = 0; j < 16; ++j) {
+            const uint32_t g16 = (gv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
+            const uint32_t u16 = (uv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
+            const double p = (double)bf16_bits_to_float(tab[g16]) * (double)bf16_bits_to_float(u16);
+            const uint32_t y = rn_bf16_from_double(p) & 0x7FFFu;
+            best = y > best ? y : best;
+          }
+      }
+      uint32_t wmax = wave_max_u32(best);
+      if (lane == 0) red[wave] = wmax;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t v = 0;
+        for (int i = 0; i < kProdThreads / 64; ++i) v = red[i] > v ? red[i] : v;
+        red[kWaves] = v << 16;
+      }
+      __syncthreads();
+      local_bits = red[kWaves];
+    } else if (SWIGLU) {
+      // RN_bf16 is monotone, so the rounded maximum is the maximum of the rounded values.
+      local_bits = (cvt_pk_bf16(__uint_as_float(local_bits), 0.0f) & 0xFFFFu) << 16;
     }
-    __syncthreads();
-    local_bits = red[kWaves];
-    // A product below 2^-126 may have been rounded in fp32; if this workgroup's
-    // maximum is such a product, redo its elements exactly (never taken for
-    // inputs whose absmax is a normal number).
-    needs_exact = SWIGLU && local_bits != 0 && local_bits < 0x00800000u;
-    __syncthreads();
-  }
-  if (SWIGLU && needs_exact) {
-    uint32_t best = 0;  // bf16 magnitude bits
-    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-      u32x4_t gv[kSteps][2], uv[kSteps][2];
-      load_item(item, gv, uv);
-      for (int s = 0; s < kSteps; ++s)
-        for (int j = 0; j < 16; ++j) {
-          const uint32_t g16 = (gv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
-          const uint32_t u16 = (uv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
-          const double p = (double)bf16_bits_to_float(tab[g16]) * (double)bf16_bits_to_float(u16);
-          const uint32_t y = rn_bf16_from_double(p) & 0x7FFFu;
-          best = y > best ? y : best;
-        }
-    }
-    uint32_t wmax = wave_max_u32(best);
-    if (lane == 0) red[wave] = wmax;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t v = 0;
-      for (int i = 0; i < kProdThreads / 64; ++i) v = red[i] > v ? red[i] : v;
-      red[kWaves] = v << 16;
-    }
-    __syncthreads();
-    local_bits = red[kWaves];
-  } else if (SWIGLU) {
-    // RN_bf16 is monotone, so the rounded maximum is the maximum of the rounded values.
-    local_bits = (cvt_pk_bf16(__uint_as_float(local_bits), 0.0f) & 0xFFFFu) << 16;
-  }
 
-  // ---------------- grid barrier: publish amax ----------------
-  if (tid == 0) {
-    ProducerWorkspace* ws = a.ws;
-    __hip_atomic_fetch_max(&ws->amax_bits, local_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(&ws->arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    while (__hip_atomic_load(&ws->arrived, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x)
-      __builtin_amdgcn_s_sleep(2);
-    const uint32_t amax = __hip_atomic_load(&ws->amax_bits, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    red[kWaves + 1] = amax;
-    // the last workgroup to leave returns the workspace to zero for the next call
-    const uint32_t d = __hip_atomic_fetch_add(&ws->departed, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == gridDim.x - 1) {
-      __hip_atomic_store(&ws->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&ws->arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&ws->departed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---------------- grid barrier: publish amax ----------------
+    if (tid == 0) {
+      ProducerWorkspace* ws = a.ws;
+      __hip_atomic_fetch_max(&ws->amax_bits, local_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&ws->arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      while (__hip_atomic_load(&ws->arrived, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x)
+        __builtin_amdgcn_s_sleep(2);
+      const uint32_t amax = __hip_atomic_load(&ws->amax_bits, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+      red[kWaves + 1] = amax;
+      // the last workgroup to leave returns the workspace to zero for the next call
+      const uint32_t d = __hip_atomic_fetch_add(&ws->departed, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == gridDim.x - 1) {
+        __hip_atomic_store(&ws->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ws->arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ws->departed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
+    __syncthreads();
+    amax = __uint_as_float(red[kWaves + 1]);
   }
-  __syncthreads();
-  const float amax = __uint_as_float(red[kWaves + 1]);
   const float g = global_scale_from_amax(amax);
   const double g6 = 6.0 * (double)g;
   // 1 / (6g) in fp32; for a tiny g both factors of bmax / (6g) are scaled by 2^64 (exact)
@@ -478,15 +486,18 @@ size_t producer_smem_bytes(bool swiglu) {
   return kRedBytes + (swiglu ? 65536 * 2 : 0);
 }
 
-const void* producer_kernel_ptr(bool swiglu) {
-  return swiglu ? (const void*)producer_kernel<true> : (const void*)producer_kernel<false>;
+const void* producer_kernel_ptr(bool swiglu, bool given) {
+  if (given) return swiglu ? (const void*)producer_kernel<true, true> : (const void*)producer_kernel<false, true>;
+  return swiglu ? (const void*)producer_kernel<true, false> : (const void*)producer_kernel<false, false>;
 }
 
 int producer_block_threads() { return kProdThreads; }
 
+// amax_in == nullptr: the two-pass producer (cooperative launch, workspace used);
+// otherwise the single-pass producer with the caller's amax (ordinary launch).
 hipError_t launch_producer(bool swiglu, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
                            int64_t m, int64_t k, uint8_t* qdata, uint8_t* scales, float* gout,
-                           void* workspace, const uint16_t* silu_table, int max_blocks,
+                           const float* amax_in, void* workspace, const uint16_t* silu_table, int max_blocks,
                            hipStream_t stream) {
   ProducerArgs args;
   args.x = x;
@@ -503,13 +514,17 @@ hipError_t launch_producer(bool swiglu, const uint16_t* x, int64_t ldx, const ui
   args.qdata = qdata;
   args.scales = scales;
   args.gout = gout;
+  args.amax_in = amax_in;
   args.ws = (ProducerWorkspace*)workspace;
   args.silu_table = silu_table;
   const int64_t nitems = (int64_t)args.items_m * args.items_k;
   int blocks = (int)(nitems < max_blocks ? nitems : max_blocks);
   if (blocks < 1) blocks = 1;
   void* kargs[] = {&args};
-  return hipLaunchCooperativeKernel(producer_kernel_ptr(swiglu), dim3(blocks), dim3(kProdThreads), kargs,
+  if (amax_in)
+    return hipLaunchKernel(producer_kernel_ptr(swiglu, true), dim3(blocks), dim3(kProdThreads), kargs,
+                           producer_smem_bytes(swiglu), stream);
+  return hipLaunchCooperativeKernel(producer_kernel_ptr(swiglu, false), dim3(blocks), dim3(kProdThreads), kargs,
                                     (unsigned)producer_smem_bytes(swiglu), stream);
 }
 

@@ -101,6 +101,37 @@ def test_swiglu_validation(kw, status):
     assert call_swiglu(**kw) == status
 
 
+def call_swiglu_amax(**kw):
+    args = dict(g_=FAKE, ldg=64, u=FAKE, ldu=64, m=16, k=64, a=FAKE, q=FAKE, s=FAKE, g=FAKE)
+    args.update(kw)
+    return nv.lib().nvfp4_quantize_swiglu_amax(args["g_"], args["ldg"], args["u"], args["ldu"], args["m"],
+                                               args["k"], args["a"], args["q"], args["s"], args["g"], None)
+
+
+def call_quant_amax(**kw):
+    args = dict(x=FAKE, ld=64, rows=16, k=64, a=FAKE, q=FAKE, s=FAKE, g=FAKE)
+    args.update(kw)
+    return nv.lib().nvfp4_quantize_amax(args["x"], args["ld"], args["rows"], args["k"], args["a"], args["q"],
+                                        args["s"], args["g"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=None), 1), (dict(a=FAKE + 2), 3), (dict(u=None), 1), (dict(q=None), 1), (dict(k=32, ldg=32, ldu=32), 2),
+    (dict(ldu=16), 1), (dict(ldg=68), 3), (dict(s=FAKE + 4), 3), (dict(m=-1), 1),
+])
+def test_swiglu_amax_validation(kw, status):
+    """The single-read producer validates like the two-pass one; its amax pointer
+    must be non-null and 4-byte aligned (an amax at FAKE + 4 is fine)."""
+    assert call_swiglu_amax(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=None), 1), (dict(a=FAKE + 1), 3), (dict(x=None), 1), (dict(g=None), 1), (dict(k=96, ld=96), 2),
+])
+def test_quantize_amax_validation(kw, status):
+    assert call_quant_amax(**kw) == status
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(aq=None), 1), (dict(d=None), 1), (dict(ga=None), 1), (dict(n=0), 1), (dict(m=-16), 1),
     (dict(m=8), 2), (dict(n=24), 2), (dict(k=96), 2), (dict(d=FAKE + 8), 3), (dict(gw=FAKE + 1), 3),

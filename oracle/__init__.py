@@ -53,6 +53,8 @@ def _load():
                                            ctypes.c_int]),
         "oracle_quantize_amax": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_double, _P, _P,
                                                 _P, ctypes.c_int]),
+        "oracle_gemm_rows_ex": (ctypes.c_int, [_P, _P, _I64, ctypes.c_float, _P, _P, _I64, ctypes.c_float,
+                                               _I64, _P, _I64, _P, _P, _P, _I64, _P, _P, ctypes.c_int]),
         "oracle_gemm_rows": (ctypes.c_int, [_P, _P, _I64, ctypes.c_float, _P, _P, _I64,
                                             ctypes.c_float, _I64, _P, _I64, _P, ctypes.c_int]),
     }
@@ -194,6 +196,39 @@ def gemm_rows(a_q: np.ndarray, a_s: np.ndarray, a_rows: int, ga: float, w_q: np.
     if rc != 0:
         raise ValueError(f"oracle_gemm_rows failed ({rc})")
     return out
+
+
+def gemm_rows_ex(a_q: np.ndarray, a_s: np.ndarray, a_rows: int, ga: float, w_q: np.ndarray,
+                 w_s: np.ndarray, n: int, gw: float, k: int, rows: Sequence[int],
+                 bias: Optional[np.ndarray] = None, gate: Optional[np.ndarray] = None,
+                 res: Optional[np.ndarray] = None, threads: Optional[int] = None):
+    """O12: (D1, D) for the selected activation rows, [len(rows), n] bf16 bits each.
+    bias, gate: bf16 bits [n] or None; res: bf16 bits [a_padded_rows, >= n] or None
+    (indexed by activation row). D = D1 without a residual."""
+    a_q = np.ascontiguousarray(a_q, dtype=np.uint8)
+    a_s = np.ascontiguousarray(a_s, dtype=np.uint8)
+    w_q = np.ascontiguousarray(w_q, dtype=np.uint8)
+    w_s = np.ascontiguousarray(w_s, dtype=np.uint8)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+    gate = None if gate is None else np.ascontiguousarray(gate, dtype=np.uint16)
+    res = None if res is None else np.ascontiguousarray(res, dtype=np.uint16)
+    if bias is not None:
+        assert bias.shape == (n,)
+    if gate is not None:
+        assert gate.shape == (n,)
+    d1 = np.empty((rows.shape[0], n), dtype=np.uint16)
+    d = np.empty((rows.shape[0], n), dtype=np.uint16)
+    rc = _load().oracle_gemm_rows_ex(a_q.ctypes.data, a_s.ctypes.data, a_rows, ga, w_q.ctypes.data,
+                                     w_s.ctypes.data, n, gw, k, rows.ctypes.data, rows.shape[0],
+                                     None if bias is None else bias.ctypes.data,
+                                     None if gate is None else gate.ctypes.data,
+                                     None if res is None else res.ctypes.data,
+                                     0 if res is None else res.shape[1], d1.ctypes.data, d.ctypes.data,
+                                     threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_rows_ex failed ({rc})")
+    return d1, d
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

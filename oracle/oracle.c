@@ -31,6 +31,10 @@
  *                     evaluated exactly in integers
  *   O11 given amax    O4-O8 with amax supplied by the caller (single-read
  *                     producer); a block above v(126) * 6 * g saturates
+ *   O12 epilogue      D1 = RN_bf16(O10's exact value + bias[n]); with a residual,
+ *                     D = RN_bf16(res[m,n] + gate[n] * D1): the unfused chain of a
+ *                     bf16 GEMM output followed by a gated residual add, each
+ *                     step rounded once
  *
  * Pins (tests/test_oracle_*.py): O1 against 50-digit decimal arithmetic for
  * all 65,536 inputs; O2 against torch's CPU bf16 multiply; O4-O6 against exact
@@ -385,6 +389,70 @@ static uint16_t rn_bf16_exact(int negative, unsigned __int128 P, int E) {
   return sign | (uint16_t)(u >> 16);
 }
 
+/* bf16 bits -> sign, integer mantissa B (< 2^8) and exponent: value = +-B * 2^E. */
+static void bf16_parts(uint16_t b, int* negative, int64_t* B, int* E) {
+  int e = (b >> 7) & 0xFF, f = b & 0x7F;
+  *negative = (b & 0x8000u) != 0;
+  if (e == 0) {
+    *B = f;
+    *E = -133;
+  } else {
+    *B = 128 + f;
+    *E = e - 134;
+  }
+}
+
+/* Shift right by s >= 0 keeping a sticky bit: any nonzero bit shifted out sets the
+ * lowest bit of the result (enough for one later rounding far above it). */
+static unsigned __int128 shr_sticky(unsigned __int128 v, int s) {
+  if (s <= 0) return v;
+  if (s >= 127) return v != 0;
+  unsigned __int128 r = v >> s;
+  if ((r << s) != v) r |= 1;
+  return r;
+}
+
+/*
+ * O12, first step: RN_bf16(X + bias) with X = sign * P * 2^E exact (P < 2^112) and
+ * bias a bf16. Both terms are aligned on a common exponent in 128-bit integers; a
+ * term far below the other is kept as a sticky bit only (it cannot move the
+ * rounding point, which lies more than 100 bits above it).
+ */
+static uint16_t rn_bf16_sum_exact(int negative, unsigned __int128 P, int E, uint16_t bias) {
+  int bn, Eb;
+  int64_t B;
+  bf16_parts(bias, &bn, &B, &Eb);
+  if (B == 0) return rn_bf16_exact(negative, P, E);
+  if (P == 0) return bias;
+  unsigned __int128 x, y;
+  int base;
+  if (Eb >= E) {
+    if (Eb - E <= 118) {
+      base = E;
+      x = P;
+      y = (unsigned __int128)B << (Eb - E);
+    } else {
+      base = Eb - 118;
+      x = shr_sticky(P, base - E);
+      y = (unsigned __int128)B << 118;
+    }
+  } else {
+    if (E - Eb <= 15) {
+      base = Eb;
+      x = P << (E - Eb);
+      y = (unsigned __int128)B;
+    } else {
+      base = E - 15;
+      x = P << 15;
+      y = shr_sticky((unsigned __int128)B, base - Eb);
+    }
+  }
+  /* signed sum of +-x and +-y (both < 2^127) */
+  if (negative == bn) return rn_bf16_exact(negative, x + y, base);
+  if (x >= y) return rn_bf16_exact(negative, x - y, base);
+  return rn_bf16_exact(bn, y - x, base);
+}
+
 /* One output row: exact integer sums per column, rounded once. */
 __attribute__((target_clones("avx2", "default")))
 static void gemm_row(const int8_t* a, const int64_t* sa, const int8_t* W, const int64_t* SW, int64_t n,
@@ -406,15 +474,48 @@ static void gemm_row(const int8_t* a, const int64_t* sa, const int8_t* W, const 
   }
 }
 
+/* One output row with the epilogue of O12: D1 = RN_bf16(X + bias[j]); with a
+ * residual row, D = RN_bf16(res[j] + gate[j] * D1) (gate absent: 1), the sum of a bf16
+ * and an exact 16-bit product rounded once (TwoSum in long double). */
+static void gemm_row_ex(const int8_t* a, const int64_t* sa, const int8_t* W, const int64_t* SW, int64_t n,
+                        int64_t nb, uint64_t Ga, uint64_t Gw, int Ebase, const uint16_t* bias,
+                        const uint16_t* gate, const uint16_t* res, uint16_t* out_d1, uint16_t* out_d) {
+  const int64_t k = nb * 16;
+  for (int64_t j = 0; j < n; ++j) {
+    const int8_t* w = W + j * k;
+    const int64_t* sw = SW + j * nb;
+    int64_t total = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+      int32_t dot = 0;
+      for (int t = 0; t < 16; ++t) dot += (int32_t)a[b * 16 + t] * (int32_t)w[b * 16 + t];
+      total += (int64_t)dot * (sa[b] * sw[b]);
+    }
+    int neg = total < 0;
+    unsigned __int128 P = (unsigned __int128)(neg ? -total : total);
+    P *= (unsigned __int128)Ga * Gw;
+    uint16_t d1 = bias ? rn_bf16_sum_exact(neg, P, Ebase, bias[j]) : rn_bf16_exact(neg, P, Ebase);
+    if (out_d1) out_d1[j] = d1;
+    uint16_t d = d1;
+    if (res) {
+      long double gv = gate ? (long double)bf16_to_double(gate[j]) : 1.0L;
+      long double prod = gv * (long double)bf16_to_double(d1); /* exact: 16 significant bits */
+      d = rn_bf16_pair((long double)bf16_to_double(res[j]), prod);
+    }
+    out_d[j] = d;
+  }
+}
+
 /*
  * D[i, j] for i < nrows (activation row rows[i]) and j < n:
  *   RN_bf16(g_a g_w sum_b v(SA[rows[i],b]) v(SW[j,b]) sum_{k in b} e2m1(A) e2m1(W))
  * computed exactly. a_rows_total / w_rows_total are the logical row counts the
  * scale buffers were sized for (their padded forms give the swizzle geometry).
  */
-int oracle_gemm_rows(const uint8_t* aq, const uint8_t* as, int64_t a_rows_total, float ga,
-                     const uint8_t* wq, const uint8_t* ws, int64_t n, float gw, int64_t k,
-                     const int64_t* rows, int64_t nrows, uint16_t* out, int nthreads) {
+static int gemm_rows_core(const uint8_t* aq, const uint8_t* as, int64_t a_rows_total, float ga,
+                          const uint8_t* wq, const uint8_t* ws, int64_t n, float gw, int64_t k,
+                          const int64_t* rows, int64_t nrows, const uint16_t* ep_bias, const uint16_t* ep_gate,
+                          const uint16_t* ep_res, int64_t ep_ldres, uint16_t* ep_d1, uint16_t* out,
+                          int nthreads) {
   if (!aq || !as || !wq || !ws || !rows || !out || n <= 0 || k <= 0 || k % 16 != 0 ||
       !(ga >= 0.0f) || !(gw >= 0.0f))
     return OR_EINVAL;
@@ -456,8 +557,39 @@ int oracle_gemm_rows(const uint8_t* aq, const uint8_t* as, int64_t a_rows_total,
   const int Ebase = (ea - 24) + (ew - 24) - 20; /* 2^-20: (1/2)^2 from q2, (2^-9)^2 from s9 */
 
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
-  for (int64_t i = 0; i < nrows; ++i)
-    gemm_row(A + i * k, SA + i * nb, W, SW, n, nb, Ga, Gw, Ebase, out + i * n);
+  for (int64_t i = 0; i < nrows; ++i) {
+    if (ep_bias || ep_res)
+      gemm_row_ex(A + i * k, SA + i * nb, W, SW, n, nb, Ga, Gw, Ebase, ep_bias, ep_gate,
+                  ep_res ? ep_res + rows[i] * ep_ldres : NULL, ep_d1 ? ep_d1 + i * n : NULL, out + i * n);
+    else
+      gemm_row(A + i * k, SA + i * nb, W, SW, n, nb, Ga, Gw, Ebase, out + i * n);
+  }
   free(A); free(W); free(SA); free(SW);
   return OR_OK;
+}
+
+int oracle_gemm_rows(const uint8_t* aq, const uint8_t* as, int64_t a_rows_total, float ga,
+                     const uint8_t* wq, const uint8_t* ws, int64_t n, float gw, int64_t k,
+                     const int64_t* rows, int64_t nrows, uint16_t* out, int nthreads) {
+  return gemm_rows_core(aq, as, a_rows_total, ga, wq, ws, n, gw, k, rows, nrows, NULL, NULL, NULL, 0, NULL, out,
+                        nthreads);
+}
+
+/*
+ * O12: the GEMM with its epilogue fusions, for the selected rows. bias (bf16 [n])
+ * or NULL; gate (bf16 [n]) or NULL; res (bf16 rows of ldres elements, indexed by the
+ * activation row rows[i]) or NULL. out_d1 (optional) receives
+ * D1 = RN_bf16(g_a g_w sum ... + bias[j]); out receives D = RN_bf16(res + gate * D1)
+ * when res is given, else D1. Gate without residual is rejected.
+ */
+int oracle_gemm_rows_ex(const uint8_t* aq, const uint8_t* as, int64_t a_rows_total, float ga,
+                        const uint8_t* wq, const uint8_t* ws, int64_t n, float gw, int64_t k,
+                        const int64_t* rows, int64_t nrows, const uint16_t* bias, const uint16_t* gate,
+                        const uint16_t* res, int64_t ldres, uint16_t* out_d1, uint16_t* out, int nthreads) {
+  if ((gate && !res) || (res && ldres < n)) return OR_EINVAL;
+  if (bias)
+    for (int64_t j = 0; j < n; ++j)
+      if (!bf16_is_finite(bias[j])) return OR_ENONFINITE;
+  return gemm_rows_core(aq, as, a_rows_total, ga, wq, ws, n, gw, k, rows, nrows, bias, gate, res, ldres, out_d1,
+                        out, nthreads);
 }

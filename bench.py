@@ -374,12 +374,29 @@ def main() -> int:
     torch.cuda.synchronize()
     same_bytes = bool(torch.equal(a1.qdata, a.qdata) and torch.equal(a1.scales, a.scales))
 
+    # the fused epilogue (bias, gate, residual in place of the plain store), timed the
+    # same way on the same operands: its cost over the plain GEMM is the epilogue's
+    bias_t = (torch.randn(w.n, device=dev) * 0.5).bfloat16()
+    gate_t = (torch.randn(w.n, device=dev) * 0.7).bfloat16()
+    res_t = (torch.randn(w.m_pad, w.n, device=dev) * 0.3).bfloat16()
+    d_f = torch.empty_like(d)
+    nv.nvfp4_gemm_bf16out_fused(a, wq, bias=bias_t, gate=gate_t, residual=res_t, out=d_f)
+    torch.cuda.synchronize()
+    evs2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in evs2:
+        e[0].record(stream)
+        nv.nvfp4_gemm_bf16out_fused(a, wq, bias=bias_t, gate=gate_t, residual=res_t, out=d_f)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    del res_t, d_f
+
     prod_ms = [e[0].elapsed_time(e[1]) for e in evs]
     gemm_ms = [e[1].elapsed_time(e[2]) for e in evs]
     import statistics
     t_prod = statistics.fmean(prod_ms)
     t_gemm = statistics.fmean(gemm_ms)
     t_single = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs1)
+    t_fused = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs2)
     sbytes = producer_single_read_bytes(w.m, w.k, w.swiglu)
     ms_per_step = wall * 1e3 / args.steps
     tflops = w.gemm_flops / (t_gemm * 1e-3) / 1e12
@@ -439,6 +456,13 @@ def main() -> int:
             "achieved_gbs": round(sbytes / (t_single * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(sbytes / (t_single * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "bytes_equal_two_pass": same_bytes,
+        },
+        "gemm_fused_epilogue": {
+            "entry": "nvfp4_gemm_bf16out_fused",
+            "epilogue": "bias[n] before the rounding, then residual + gate[n] * D1",
+            "avg_launch_ms": round(t_fused, 4),
+            "tflops": round(w.gemm_flops / (t_fused * 1e-3) / 1e12, 2),
+            "over_plain_ms": round(t_fused - t_gemm, 4),
         },
         "producer_ms": round(t_prod, 4),
         "gemm_ms": round(t_gemm, 4),

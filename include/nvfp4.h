@@ -172,6 +172,35 @@ int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const 
                        const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
                        void* d_dev, int64_t m_padded, int64_t n, int64_t k, void* stream);
 
+/*
+ * The GEMM with its epilogue fusions. The FC2 kernel named on the pages carries a
+ * bf16 bias in its epilogue, and the step profile of the pages keeps a
+ * gate/residual add after the GEMM ("remaining_gate_add" among the production
+ * components); both are folded into the store of D here:
+ *
+ *   D1[m, n] = RN_bf16(g_a * g_w * sum(...) + bias[n])   (bias_dev NULL: no bias)
+ *   D[m, n]  = RN_bf16(residual[m, n] + gate[n] * D1[m, n]) with a residual
+ *              (gate_dev NULL: gate 1), else D = D1.
+ *
+ * The chain is that of the unfused pipeline (a bf16 GEMM output, then a gated
+ * residual add). Each step is an FP32 sum (the gate product exact) rounded to
+ * bf16; the accumulation is FP32 as in nvfp4_gemm_bf16out.
+ *
+ * bias_dev     : bf16 [n] or NULL; 16-byte aligned; finite.
+ * gate_dev     : bf16 [n] or NULL; needs residual_dev; 16-byte aligned.
+ * residual_dev : bf16 [m_padded, n] row-major (row stride n) or NULL; 16-byte
+ *                aligned; may be d_dev itself (in-place update of the residual
+ *                stream): each element is read before the same thread writes it.
+ * Every other argument as nvfp4_gemm_bf16out. Rows past the logical rows of the
+ * activation come out RN_bf16(bias) (zero activation rows), combined with the
+ * residual like any other row. No workspace; errors as nvfp4_gemm_bf16out, plus
+ * NVFP4_ERR_INVALID_ARG for a gate without a residual.
+ */
+int nvfp4_gemm_bf16out_fused(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
+                             const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
+                             void* d_dev, int64_t m_padded, int64_t n, int64_t k, const void* bias_dev,
+                             const void* gate_dev, const void* residual_dev, void* stream);
+
 /* ---- self-test hook ---------------------------------------------------------------------- */
 
 /* y[i] = silu_bf16(x[i]) for i < count, bf16 bit patterns, with the table the

@@ -54,6 +54,7 @@ SIGNATURES = {
     "nvfp4_quantize_swiglu_amax": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_quantize_amax": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_gemm_bf16out": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "nvfp4_gemm_bf16out_fused": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_silu_bf16": (_INT, [_P, _P, _I64, _P]),
     "nvfp4_status_string": (ctypes.c_char_p, [_INT]),
     "nvfp4_last_error": (ctypes.c_char_p, []),
@@ -284,6 +285,29 @@ def nvfp4_gemm_bf16out(a: Nvfp4Tensor, w: Nvfp4Tensor, out=None, stream=None):
     _call("nvfp4_gemm_bf16out", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
           w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), out.data_ptr(), m_pad, n, a.k,
           _stream_handle(stream))
+    return out
+
+
+def nvfp4_gemm_bf16out_fused(a: Nvfp4Tensor, w: Nvfp4Tensor, bias=None, gate=None, residual=None, out=None,
+                             stream=None):
+    """D = RN_bf16(residual + gate * RN_bf16(g_a g_w sum + bias)) (each term optional;
+    without a residual D is the biased GEMM output). out may be residual (in place)."""
+    import torch
+    if a.k != w.k:
+        raise ValueError("k mismatch")
+    m_pad = a.padded_rows
+    n = w.rows
+    if out is None:
+        out = torch.empty((m_pad, n), dtype=torch.bfloat16, device=a.qdata.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (m_pad, n) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [m_padded, n] tensor")
+    for name, t, shape in (("bias", bias, (n,)), ("gate", gate, (n,)), ("residual", residual, (m_pad, n))):
+        if t is not None and (t.dtype != torch.bfloat16 or tuple(t.shape) != shape or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor of shape {shape}")
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _call("nvfp4_gemm_bf16out_fused", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
+          w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), out.data_ptr(), m_pad, n, a.k,
+          ptr(bias), ptr(gate), ptr(residual), _stream_handle(stream))
     return out
 
 

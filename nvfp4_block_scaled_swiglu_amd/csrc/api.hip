@@ -26,10 +26,11 @@ hipError_t launch_producer(bool swiglu, const uint16_t* x, int64_t ldx, const ui
                            const float* amax_in, void* workspace, const uint16_t* silu_table, int max_blocks,
                            hipStream_t stream);
 size_t gemm_smem_bytes();
-const void* gemm_kernel_ptr();
+const void* gemm_kernel_ptr(bool fused);
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
-                       int cu_count, hipStream_t stream);
+                       const uint16_t* bias, const uint16_t* gate, const uint16_t* res, bool fused, int cu_count,
+                       hipStream_t stream);
 }  // namespace nvfp4
 
 namespace {
@@ -106,9 +107,11 @@ int ensure_device(DeviceState** out) {
       return fail(NVFP4_ERR_LAUNCH, "producer occupancy query: %s (%d)", hipGetErrorString(e), per_cu);
     (sw ? st.producer_blocks_swiglu : st.producer_blocks_plain) = per_cu * st.cu_count;
   }
-  e = hipFuncSetAttribute(nvfp4::gemm_kernel_ptr(), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)nvfp4::gemm_smem_bytes());
-  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "gemm LDS attribute: %s", hipGetErrorString(e));
+  for (int fused = 0; fused < 2; ++fused) {
+    e = hipFuncSetAttribute(nvfp4::gemm_kernel_ptr(fused != 0), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)nvfp4::gemm_smem_bytes());
+    if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "gemm LDS attribute: %s", hipGetErrorString(e));
+  }
 
   e = nvfp4::silu_table_address(&st.silu_table);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "silu table address: %s", hipGetErrorString(e));
@@ -214,9 +217,10 @@ int nvfp4_quantize_amax(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k
                          amax_dev, nullptr, stream);
 }
 
-int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
+static int gemm_common(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
                        const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev, void* d_dev,
-                       int64_t m_padded, int64_t n, int64_t k, void* stream) {
+                       int64_t m_padded, int64_t n, int64_t k, const void* bias_dev, const void* gate_dev,
+                       const void* residual_dev, bool fused, void* stream) {
   if (!a_qdata_dev || !a_scales_dev || !a_global_dev || !w_qdata_dev || !w_scales_dev || !w_global_dev || !d_dev)
     return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
   if (m_padded < 0 || n <= 0 || k <= 0)
@@ -228,6 +232,9 @@ int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const 
   if (!aligned16(a_qdata_dev) || !aligned16(a_scales_dev) || !aligned16(w_qdata_dev) || !aligned16(w_scales_dev) ||
       !aligned16(d_dev) || ((uintptr_t)a_global_dev & 3u) || ((uintptr_t)w_global_dev & 3u))
     return fail(NVFP4_ERR_MISALIGNED, "pointers must be 16-byte aligned (global scales 4-byte)");
+  if (gate_dev && !residual_dev) return fail(NVFP4_ERR_INVALID_ARG, "a gate needs a residual");
+  if (!aligned16(bias_dev) || !aligned16(gate_dev) || !aligned16(residual_dev))
+    return fail(NVFP4_ERR_MISALIGNED, "bias, gate and residual must be 16-byte aligned");
   const int64_t mt = (m_padded + 255) / 256 * 256, nt = (n + 255) / 256 * 256;
   if (mt * (k / 2) >= kMaxBufferBytes || nt * (k / 2) >= kMaxBufferBytes ||
       (mt + 128) * nvfp4_scale_cols(k) >= kMaxBufferBytes || (nt + 128) * nvfp4_scale_cols(k) >= kMaxBufferBytes ||
@@ -239,9 +246,26 @@ int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const 
   if (m_padded == 0) return ok();
   hipError_t e = nvfp4::launch_gemm((const uint8_t*)a_qdata_dev, (const uint8_t*)a_scales_dev, a_global_dev,
                                     (const uint8_t*)w_qdata_dev, (const uint8_t*)w_scales_dev, w_global_dev,
-                                    (uint16_t*)d_dev, m_padded, n, k, st->cu_count, (hipStream_t)stream);
+                                    (uint16_t*)d_dev, m_padded, n, k, (const uint16_t*)bias_dev,
+                                    (const uint16_t*)gate_dev, (const uint16_t*)residual_dev, fused, st->cu_count,
+                                    (hipStream_t)stream);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
+                       const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev, void* d_dev,
+                       int64_t m_padded, int64_t n, int64_t k, void* stream) {
+  return gemm_common(a_qdata_dev, a_scales_dev, a_global_dev, w_qdata_dev, w_scales_dev, w_global_dev, d_dev,
+                     m_padded, n, k, nullptr, nullptr, nullptr, false, stream);
+}
+
+int nvfp4_gemm_bf16out_fused(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
+                             const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
+                             void* d_dev, int64_t m_padded, int64_t n, int64_t k, const void* bias_dev,
+                             const void* gate_dev, const void* residual_dev, void* stream) {
+  return gemm_common(a_qdata_dev, a_scales_dev, a_global_dev, w_qdata_dev, w_scales_dev, w_global_dev, d_dev,
+                     m_padded, n, k, bias_dev, gate_dev, residual_dev, true, stream);
 }
 
 int nvfp4_silu_bf16(const void* x_dev, void* y_dev, int64_t count, void* stream) {

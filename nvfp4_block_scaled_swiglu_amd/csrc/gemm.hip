@@ -95,8 +95,24 @@ struct GemmArgs {
   int big_tiles;                               // tiles [0, big_tiles) run whole; the rest as quarters
   int cgroups;                                 // scale column groups = C / 4
   int ksteps;
+  // fused epilogue (the EPI = 1 kernel): bias and gate bf16 [n] or null, residual
+  // bf16 [m_pad, n] (row stride n, may alias d) or null
+  const uint16_t* bias;
+  const uint16_t* gate;
+  const uint16_t* res;
 };
 
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+// RN_bf16 of a float (ties to even), as a 16-bit pattern
+__device__ __forceinline__ uint32_t bf16_bits_rn(float v) {
+  bf16x2_t c;
+  c[0] = (__bf16)v;
+  c[1] = (__bf16)0.0f;
+  uint32_t r;
+  __builtin_memcpy(&r, &c, 4);
+  return r & 0xFFFFu;
+}
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Position of 16-byte chunk c of code row r inside that row's 64 LDS bytes. The
@@ -195,9 +211,27 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// alpha * acc of fragment row I (rows 32 I .. 32 I + 31 of the wave's band) into the
+// wave's fp32 staging rows; I is a compile-time constant so that acc stays in registers.
+template <int I, int FM, int FN, int kRowBytes>
+__device__ __forceinline__ void stage_fragment_f32(const f32x16_t (&acc)[FN][FM], unsigned char* stg, float alpha,
+                                                   int lr, int h) {
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4_t v = {acc[j][I][q * 4 + 0] * alpha, acc[j][I][q * 4 + 1] * alpha, acc[j][I][q * 4 + 2] * alpha,
+                         acc[j][I][q * 4 + 3] * alpha};
+      *(f32x4_t*)(stg + lr * kRowBytes + (j * 32 + q * 8 + h * 4) * 4) = v;
+    }
+  }
+}
+
 // One output tile: the whole K loop and the epilogue for rows [m0, m0 + TM) and
 // columns [n0, n0 + TN), by the workgroup's 4 waves.
-template <int FM, int FN>
+// EPI = 0: D = RN_bf16(alpha * acc). EPI = 1: the fused epilogue, D1 = RN_bf16(alpha
+// * acc + bias[n]) and, with a residual, D = RN_bf16(res + gate[n] * D1).
+template <int FM, int FN, int EPI>
 __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, const int64_t n0, unsigned char* smem) {
   using T = TileShape<FM, FN>;
   constexpr int kStageBytes = T::StageBytes, kCodesA = T::CodesA, kCodesW = T::CodesW, kScaleA = T::ScaleA;
@@ -390,59 +424,137 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
   }
   kstep(ks, stage, false, false);
 
-  // ---- epilogue: D[m, n] = RN_bf16(alpha * acc), alpha = g_a * g_w ----
-  // Each wave stages its tile in its own quarter of the (now idle) LDS, 64 rows at a
-  // time, then stores whole row segments: a store instruction writes 4 rows x 256 B
-  // (full tile) or 8 rows x 128 B (quarter tile) instead of 16-byte pieces of 32 rows.
-  const float alpha = (*a.ga) * (*a.gw);
-  constexpr int kWaveCols = FN * 32, kRowBytes = kWaveCols * 2 + 16;  // padded against bank conflicts
-  constexpr int kChunksPerRow = kWaveCols / 8, kRowsPerStore = 64 / kChunksPerRow;
-  static_assert(64 * kRowBytes <= kStages * BigTile::StageBytes / kWaves, "staging fits the wave's LDS share");
-  unsigned char* stg = smem + wave * (kStages * BigTile::StageBytes / kWaves);
-  const int64_t wrow0 = m0 + wm * FM * 32, wcol0 = n0 + wn * FN * 32;
-  stage_barrier();  // every wave has finished reading the last K step's stage
-#pragma unroll
-  for (int half = 0; half < FM / 2; ++half) {
-    // registers -> LDS: fragments i = 2 half, 2 half + 1 hold rows 64 half .. 64 half + 63
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = 2 * half + ii;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bf16x2_t lo, hi;
-          lo[0] = (__bf16)(acc[j][i][q * 4 + 0] * alpha);
-          lo[1] = (__bf16)(acc[j][i][q * 4 + 1] * alpha);
-          hi[0] = (__bf16)(acc[j][i][q * 4 + 2] * alpha);
-          hi[1] = (__bf16)(acc[j][i][q * 4 + 3] * alpha);
-          uint32_t ul, uh;
-          __builtin_memcpy(&ul, &lo, 4);
-          __builtin_memcpy(&uh, &hi, 4);
-          typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
-          const u32x2_t v = {ul, uh};
-          const int r = ii * 32 + lr, c = j * 32 + q * 8 + h * 4;
-          *(u32x2_t*)(stg + r * kRowBytes + c * 2) = v;
+  if constexpr (EPI == 0) {
+    // ---- epilogue: D[m, n] = RN_bf16(alpha * acc), alpha = g_a * g_w ----
+    // Each wave stages its tile in its own quarter of the (now idle) LDS, 64 rows at a
+    // time, then stores whole row segments: a store instruction writes 4 rows x 256 B
+    // (full tile) or 8 rows x 128 B (quarter tile) instead of 16-byte pieces of 32 rows.
+    const float alpha = (*a.ga) * (*a.gw);
+    constexpr int kWaveCols = FN * 32, kRowBytes = kWaveCols * 2 + 16;  // padded against bank conflicts
+    constexpr int kChunksPerRow = kWaveCols / 8, kRowsPerStore = 64 / kChunksPerRow;
+    static_assert(64 * kRowBytes <= kStages * BigTile::StageBytes / kWaves, "staging fits the wave's LDS share");
+    unsigned char* stg = smem + wave * (kStages * BigTile::StageBytes / kWaves);
+    const int64_t wrow0 = m0 + wm * FM * 32, wcol0 = n0 + wn * FN * 32;
+    stage_barrier();  // every wave has finished reading the last K step's stage
+  #pragma unroll
+    for (int half = 0; half < FM / 2; ++half) {
+      // registers -> LDS: fragments i = 2 half, 2 half + 1 hold rows 64 half .. 64 half + 63
+  #pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * half + ii;
+  #pragma unroll
+        for (int j = 0; j < FN; ++j) {
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            bf16x2_t lo, hi;
+            lo[0] = (__bf16)(acc[j][i][q * 4 + 0] * alpha);
+            lo[1] = (__bf16)(acc[j][i][q * 4 + 1] * alpha);
+            hi[0] = (__bf16)(acc[j][i][q * 4 + 2] * alpha);
+            hi[1] = (__bf16)(acc[j][i][q * 4 + 3] * alpha);
+            uint32_t ul, uh;
+            __builtin_memcpy(&ul, &lo, 4);
+            __builtin_memcpy(&uh, &hi, 4);
+            typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+            const u32x2_t v = {ul, uh};
+            const int r = ii * 32 + lr, c = j * 32 + q * 8 + h * 4;
+            *(u32x2_t*)(stg + r * kRowBytes + c * 2) = v;
+          }
         }
       }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+      asm volatile("" ::: "memory");
+      // LDS -> global: lane L takes 8 columns of one row
+  #pragma unroll
+      for (int it = 0; it < 64 / kRowsPerStore; ++it) {
+        const int r = it * kRowsPerStore + lane / kChunksPerRow, ch = lane % kChunksPerRow;
+        const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
+        const int64_t m = wrow0 + half * 64 + r, n = wcol0 + ch * 8;
+        if (m < a.m_pad && n < a.n) *(u32x4_t*)(a.d + m * a.n + n) = v;
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next half overwrites
+      asm volatile("" ::: "memory");
     }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
-    asm volatile("" ::: "memory");
-    // LDS -> global: lane L takes 8 columns of one row
+  } else {
+    // ---- fused epilogue: bias before the bf16 rounding, then the gated residual ----
+    // Each wave stages alpha * acc in fp32 in its quarter of the LDS, 32 rows at a
+    // time; lane L then owns 8 columns of one row: it adds the bias, rounds to bf16
+    // (D1), combines the residual, and stores 16 bytes.
+    const float alpha = (*a.ga) * (*a.gw);
+    constexpr int kWaveCols = FN * 32, kRowBytes = kWaveCols * 4 + 16;  // padded against bank conflicts
+    constexpr int kChunksPerRow = kWaveCols / 8, kRowsPerStore = 64 / kChunksPerRow;
+    constexpr int kIters = 32 / kRowsPerStore;
+    static_assert(32 * kRowBytes <= kStages * BigTile::StageBytes / kWaves, "staging fits the wave's LDS share");
+    unsigned char* stg = smem + wave * (kStages * BigTile::StageBytes / kWaves);
+    const int64_t wrow0 = m0 + wm * FM * 32, wcol0 = n0 + wn * FN * 32;
+    const int ch = lane % kChunksPerRow, rl = lane / kChunksPerRow;
+    const int64_t col = wcol0 + ch * 8;
+    const bool col_ok = col < a.n;
+    stage_barrier();  // every wave has finished reading the last K step's stage
+    // (loaded after the barrier so that they do not live through the K loop)
+    float bias8[8], gate8[8];
+    {
+      u32x4_t bv = {0u, 0u, 0u, 0u}, gv = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // gate 1.0
+      if (a.bias && col_ok) bv = *(const u32x4_t*)(a.bias + col);
+      if (a.gate && col_ok) gv = *(const u32x4_t*)(a.gate + col);
 #pragma unroll
-    for (int it = 0; it < 64 / kRowsPerStore; ++it) {
-      const int r = it * kRowsPerStore + lane / kChunksPerRow, ch = lane % kChunksPerRow;
-      const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
-      const int64_t m = wrow0 + half * 64 + r, n = wcol0 + ch * 8;
-      if (m < a.m_pad && n < a.n) *(u32x4_t*)(a.d + m * a.n + n) = v;
+      for (int e = 0; e < 8; ++e) {
+        bias8[e] = bf16_bits_to_float((bv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        gate8[e] = bf16_bits_to_float((gv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      }
     }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next half overwrites
-    asm volatile("" ::: "memory");
+    static_assert(FM <= 4, "fragment dispatch");
+#pragma nounroll
+    for (int i = 0; i < FM; ++i) {
+      // this fragment's residual rows, in flight while alpha * acc is staged
+      u32x4_t rv[kIters];
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int64_t m = wrow0 + i * 32 + it * kRowsPerStore + rl;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        rv[it] = (a.res && m < a.m_pad && col_ok) ? *(const u32x4_t*)(a.res + m * a.n + col) : z;
+      }
+      // registers -> LDS: fragment i holds rows 32 i .. 32 i + 31 of the wave's band
+      if (i == 0) stage_fragment_f32<0, FM, FN, kRowBytes>(acc, stg, alpha, lr, h);
+      if (FM > 1 && i == 1) stage_fragment_f32<(FM > 1 ? 1 : 0), FM, FN, kRowBytes>(acc, stg, alpha, lr, h);
+      if (FM > 2 && i == 2) stage_fragment_f32<(FM > 2 ? 2 : 0), FM, FN, kRowBytes>(acc, stg, alpha, lr, h);
+      if (FM > 3 && i == 3) stage_fragment_f32<(FM > 3 ? 3 : 0), FM, FN, kRowBytes>(acc, stg, alpha, lr, h);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int r = it * kRowsPerStore + rl;
+        const int64_t m = wrow0 + i * 32 + r;
+        const f32x4_t x0 = *(const f32x4_t*)(stg + r * kRowBytes + ch * 32);
+        const f32x4_t x1 = *(const f32x4_t*)(stg + r * kRowBytes + ch * 32 + 16);
+        // Each step is one fp32 sum rounded to bf16. gate * D1 (two bf16 values) is
+        // exact in fp32 above 2^-126; the sums round in fp32 before the bf16 rounding,
+        // which can move a result by one bf16 unit only when the exact sum lies within
+        // an fp32 unit of a bf16 midpoint, below the accumulation's own error.
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t d1 = bf16_bits_rn((e < 4 ? x0[e] : x1[e - 4]) + bias8[e]);
+          if (a.res) {
+            const float rr = bf16_bits_to_float((rv[it][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            o[e] = bf16_bits_rn(rr + gate8[e] * bf16_bits_to_float(d1));
+          } else {
+            o[e] = d1;
+          }
+        }
+        const u32x4_t v = {o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)};
+        if (m < a.m_pad && col_ok) *(u32x4_t*)(a.d + m * a.n + col) = v;
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next fragment overwrites
+      asm volatile("" ::: "memory");
+    }
   }
 }
 
+template <int EPI>
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // Tiles (256 x 256) are numbered m-band-major: band = 8 M-tiles, within a band M
@@ -471,23 +583,27 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
   const int tn = in_band / band_m;
   const int64_t m0 = (int64_t)tm * kTileBig, n0 = (int64_t)tn * kTileBig;
   if (quarter < 0) {
-    run_tile<4, 4>(a, m0, n0, smem);
+    run_tile<4, 4, EPI>(a, m0, n0, smem);
   } else {
     const int64_t qm0 = m0 + (quarter >> 1) * kTileQuarter, qn0 = n0 + (quarter & 1) * kTileQuarter;
     if (qm0 >= a.m_pad || qn0 >= a.n) return;  // a quarter wholly past the padded output
-    run_tile<2, 2>(a, qm0, qn0, smem);
+    run_tile<2, 2, EPI>(a, qm0, qn0, smem);
   }
 }
 
 // ---- host side -----------------------------------------------------------------------------
 
 size_t gemm_smem_bytes() { return (size_t)kStages * BigTile::StageBytes; }
-const void* gemm_kernel_ptr() { return (const void*)gemm_kernel; }
+const void* gemm_kernel_ptr(bool fused) { return fused ? (const void*)gemm_kernel<1> : (const void*)gemm_kernel<0>; }
 
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
-                       int cu_count, hipStream_t stream) {
+                       const uint16_t* bias, const uint16_t* gate, const uint16_t* res, bool fused, int cu_count,
+                       hipStream_t stream) {
   GemmArgs args;
+  args.bias = bias;
+  args.gate = gate;
+  args.res = res;
   args.aq = aq;
   args.as = as;
   args.ga = ga;
@@ -514,7 +630,10 @@ hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, co
   const int tail = cu_count > 0 ? ntiles % cu_count : 0;
   args.big_tiles = (tail > 0 && ntiles > cu_count && 4 * tail <= cu_count) ? ntiles - tail : ntiles;
   const int grid = args.big_tiles + 4 * (ntiles - args.big_tiles);
-  gemm_kernel<<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);
+  if (fused)
+    gemm_kernel<1><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);
+  else
+    gemm_kernel<0><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);
   return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@ GEMM tolerance (the oracle is exact and rounds once to bf16):
     over the checked set: one bf16 ulp, with a floor near zero where an FP32
     accumulation of thousands of terms cannot promise a relative bound;
   * ||D - D_ref||_F / ||D_ref||_F <= 2e-3.
+The fused epilogue's bounds follow from this one (see fused_compare).
 """
 from __future__ import annotations
 
@@ -53,6 +54,34 @@ def assert_gemm_close(got_bits: np.ndarray, ref_bits: np.ndarray, what: str = ""
     st = gemm_compare(got_bits, ref_bits)
     assert st["violations"] == 0 and st["rel_fro"] <= REL_FRO_TOL, f"{what} GEMM out of tolerance: {st}"
     return st
+
+
+def fused_compare(d1_got: np.ndarray, d1_ref: np.ndarray, plain_ref: np.ndarray,
+                  d_got: Optional[np.ndarray] = None, d_ref: Optional[np.ndarray] = None,
+                  gate: Optional[np.ndarray] = None) -> Dict[str, float]:
+    """Tolerance of the fused epilogue, derived from the GEMM bar:
+      * D1 = RN_bf16(X + bias): |D1 - D1_ref| <= ulp_bf16(max(|D1_ref|, tau)) with
+        tau = 2^-8 max |X_ref| (X_ref: the unbiased output, plain_ref), the FP32
+        accumulation floor of the plain GEMM, independent of the bias magnitude;
+      * D = RN_bf16(res + gate D1): a D1 error e1 moves the exact sum by |gate| e1,
+        and each side rounds once, so |D - D_ref| <= |gate| tol1 + ulp_bf16(max(|D|, |D_ref|)).
+    """
+    g1 = bf16_bits_to_f64(d1_got)
+    r1 = bf16_bits_to_f64(d1_ref)
+    x = bf16_bits_to_f64(plain_ref)
+    assert np.isfinite(g1).all(), "non-finite D1"
+    tau = 2.0 ** -8 * (float(np.abs(x).max()) if x.size else 0.0)
+    tol1 = ulp_bf16(np.maximum(np.abs(r1), tau))
+    out = {"checked": int(r1.size), "d1_violations": int((np.abs(g1 - r1) > tol1).sum()),
+           "d1_differing": int((d1_got != d1_ref).sum()), "tau": tau}
+    if d_got is not None:
+        gd = bf16_bits_to_f64(d_got)
+        rd = bf16_bits_to_f64(d_ref)
+        gv = np.ones(r1.shape[1]) if gate is None else bf16_bits_to_f64(gate)
+        tol = np.abs(gv)[None, :] * tol1 + ulp_bf16(np.maximum(np.abs(gd), np.abs(rd)))
+        out["d_violations"] = int((np.abs(gd - rd) > tol).sum())
+        out["d_differing"] = int((d_got != d_ref).sum())
+    return out
 
 
 def sample_rows(m: int, m_pad: int, count: int, seed: int) -> np.ndarray:

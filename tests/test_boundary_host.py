@@ -141,6 +141,25 @@ def test_gemm_validation(kw, status):
     assert call_gemm(**kw) == status
 
 
+def call_fused(**kw):
+    args = dict(aq=FAKE, as_=FAKE, ga=FAKE, wq=FAKE, ws=FAKE, gw=FAKE, d=FAKE, m=16, n=16, k=64, b=None, g=None,
+                r=None)
+    args.update(kw)
+    return nv.lib().nvfp4_gemm_bf16out_fused(args["aq"], args["as_"], args["ga"], args["wq"], args["ws"],
+                                             args["gw"], args["d"], args["m"], args["n"], args["k"], args["b"],
+                                             args["g"], args["r"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=FAKE), 1), (dict(b=FAKE + 8), 3), (dict(g=FAKE + 2, r=FAKE), 3), (dict(r=FAKE + 4), 3),
+    (dict(d=None), 1), (dict(m=8), 2), (dict(k=96), 2),
+])
+def test_fused_gemm_validation(kw, status):
+    """The fused GEMM validates like the plain one; a gate needs a residual, and bias,
+    gate and residual must be 16-byte aligned."""
+    assert call_fused(**kw) == status
+
+
 def test_silu_validation():
     assert nv.lib().nvfp4_silu_bf16(None, None, -1, None) == 1
     assert nv.lib().nvfp4_silu_bf16(None, FAKE, 4, None) == 1

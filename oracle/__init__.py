@@ -53,6 +53,8 @@ def _load():
                                            ctypes.c_int]),
         "oracle_quantize_amax": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, ctypes.c_double, _P, _P,
                                                 _P, ctypes.c_int]),
+        "oracle_modulate_bf16": (ctypes.c_uint16, [ctypes.c_uint16, ctypes.c_uint16, ctypes.c_uint16]),
+        "oracle_quantize_modulate": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_int]),
         "oracle_gemm_rows_ex": (ctypes.c_int, [_P, _P, _I64, ctypes.c_float, _P, _P, _I64, ctypes.c_float,
                                                _I64, _P, _I64, _P, _P, _P, _I64, _P, _P, ctypes.c_int]),
         "oracle_gemm_rows": (ctypes.c_int, [_P, _P, _I64, ctypes.c_float, _P, _P, _I64,
@@ -177,6 +179,34 @@ def quantize_amax(x: np.ndarray, up: Optional[np.ndarray], amax: float, m: Optio
                                       threads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle_quantize_amax failed ({rc})")
+    return qdata, scales, float(g[0])
+
+
+def modulate_bf16(x: int, scale: int, shift: int) -> int:
+    return int(_load().oracle_modulate_bf16(x, scale, shift))
+
+
+def quantize_modulate(x: np.ndarray, scale: np.ndarray, shift: np.ndarray, m: Optional[int] = None,
+                      return_y: bool = False, threads: Optional[int] = None):
+    """O13 + O3-O8: plain NVFP4 quantization of y = RN_bf16(fma_fp32(x, 1 + scale, shift))
+    (bf16 bits; scale, shift [k]). Returns (qdata, scales, g[, y])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    m = x.shape[0] if m is None else m
+    k = x.shape[1]
+    scale = np.ascontiguousarray(scale, dtype=np.uint16)
+    shift = np.ascontiguousarray(shift, dtype=np.uint16)
+    assert scale.shape == (k,) and shift.shape == (k,)
+    qdata = np.empty((padded_rows(m), k // 2), dtype=np.uint8)
+    scales = np.empty(scale_bytes(m, k), dtype=np.uint8)
+    g = np.zeros(1, dtype=np.float32)
+    y = np.empty((m, k), dtype=np.uint16) if return_y else None
+    rc = _load().oracle_quantize_modulate(x.ctypes.data, k, m, k, scale.ctypes.data, shift.ctypes.data,
+                                          qdata.ctypes.data, scales.ctypes.data, g.ctypes.data,
+                                          None if y is None else y.ctypes.data, threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_modulate failed ({rc})")
+    if return_y:
+        return qdata, scales, float(g[0]), y
     return qdata, scales, float(g[0])
 
 

@@ -31,6 +31,8 @@
  *                     evaluated exactly in integers
  *   O11 given amax    O4-O8 with amax supplied by the caller (single-read
  *                     producer); a block above v(126) * 6 * g saturates
+ *   O13 modulation    y = RN_bf16(fma_fp32(x, RN_fp32(1 + scale[k]), shift[k]))
+ *                     feeding O3-O8 (plain quantization of the modulated input)
  *   O12 epilogue      D1 = RN_bf16(O10's exact value + bias[n]); with a residual,
  *                     D = RN_bf16(res[m,n] + gate[n] * D1): the unfused chain of a
  *                     bf16 GEMM output followed by a gated residual add, each
@@ -225,9 +227,23 @@ int64_t oracle_scale_offset(int64_t r, int64_t c, int64_t cpad) {
  *   *g_out the fp32 global scale
  * y_out (optional, [m, k] bf16 bits) receives y for inspection.
  */
+/*
+ * O13: the modulated activation. m = RN_fp32(1 + scale[c]) and
+ * y = RN_bf16(fma_fp32(x, m, shift[c])): one fp32 rounding of the exact x * m + shift
+ * (fmaf is correctly rounded), then one bf16 rounding. The precision is fp32 because
+ * y decides integer codes and both sides must take that decision identically; the
+ * pages fix no precision for the modulation.
+ */
+uint16_t oracle_modulate_bf16(uint16_t x, uint16_t scale, uint16_t shift) {
+  const float xf = (float)bf16_to_double(x);
+  const float mf = 1.0f + (float)bf16_to_double(scale);
+  const float y = fmaf(xf, mf, (float)bf16_to_double(shift));
+  return oracle_rn_bf16((double)y);
+}
+
 static int quantize_core(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t ldu, int64_t m,
-                         int64_t k, const double* amax_given, uint8_t* qdata, uint8_t* scales, float* g_out,
-                         uint16_t* y_out, int nthreads) {
+                         int64_t k, const double* amax_given, const uint16_t* mod_scale, const uint16_t* mod_shift,
+                         uint8_t* qdata, uint8_t* scales, float* g_out, uint16_t* y_out, int nthreads) {
   if (!x || !qdata || !scales || !g_out || m < 0 || k <= 0 || k % 16 != 0 || ldx < k ||
       (up && ldu < k))
     return OR_EINVAL;
@@ -257,6 +273,9 @@ static int quantize_core(const uint16_t* x, int64_t ldx, const uint16_t* up, int
         uint16_t uv = up[r * ldu + c];
         if (!bf16_is_finite(xv) || !bf16_is_finite(uv)) bad = 1;
         yv = oracle_swiglu_bf16(xv, uv, tab);
+      } else if (mod_scale) {
+        if (!bf16_is_finite(xv) || !bf16_is_finite(mod_scale[c]) || !bf16_is_finite(mod_shift[c])) bad = 1;
+        yv = oracle_modulate_bf16(xv, mod_scale[c], mod_shift[c]);
       } else {
         yv = xv;
       }
@@ -332,7 +351,15 @@ static int quantize_core(const uint16_t* x, int64_t ldx, const uint16_t* up, int
 int oracle_quantize(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t ldu, int64_t m,
                     int64_t k, uint8_t* qdata, uint8_t* scales, float* g_out, uint16_t* y_out,
                     int nthreads) {
-  return quantize_core(x, ldx, up, ldu, m, k, NULL, qdata, scales, g_out, y_out, nthreads);
+  return quantize_core(x, ldx, up, ldu, m, k, NULL, NULL, NULL, qdata, scales, g_out, y_out, nthreads);
+}
+
+/* O13 + O3-O8: plain quantization of the modulated x. */
+int oracle_quantize_modulate(const uint16_t* x, int64_t ldx, int64_t m, int64_t k, const uint16_t* scale,
+                             const uint16_t* shift, uint8_t* qdata, uint8_t* scales, float* g_out, uint16_t* y_out,
+                             int nthreads) {
+  if (!scale || !shift) return OR_EINVAL;
+  return quantize_core(x, ldx, NULL, 0, m, k, NULL, scale, shift, qdata, scales, g_out, y_out, nthreads);
 }
 
 /*
@@ -345,7 +372,7 @@ int oracle_quantize(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t 
 int oracle_quantize_amax(const uint16_t* x, int64_t ldx, const uint16_t* up, int64_t ldu, int64_t m,
                          int64_t k, double amax, uint8_t* qdata, uint8_t* scales, float* g_out,
                          int nthreads) {
-  return quantize_core(x, ldx, up, ldu, m, k, &amax, qdata, scales, g_out, NULL, nthreads);
+  return quantize_core(x, ldx, up, ldu, m, k, &amax, NULL, NULL, qdata, scales, g_out, NULL, nthreads);
 }
 
 /* ---------- GEMM ------------------------------------------------------------- */

@@ -248,12 +248,27 @@ def shapes(args, dev) -> int:
         torch.cuda.synchronize()
         t_prod = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs)
         t_gemm = statistics.fmean(e[1].elapsed_time(e[2]) for e in evs)
+        t_mod = None
+        if not w.swiglu:
+            # the same input with adaLN modulation fused into the quantizer
+            sc = (torch.randn(w.k, device=dev) * 0.3).bfloat16()
+            sh = (torch.randn(w.k, device=dev) * 0.5).bfloat16()
+            nv.nvfp4_quantize_modulate(x, sc, sh, out=a)
+            torch.cuda.synchronize()
+            evm = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            for e in evm:
+                e[0].record(stream)
+                nv.nvfp4_quantize_modulate(x, sc, sh, out=a)
+                e[1].record(stream)
+            torch.cuda.synchronize()
+            t_mod = statistics.fmean(e[0].elapsed_time(e[1]) for e in evm)
         tflops = w.gemm_flops / (t_gemm * 1e-3) / 1e12
         pbytes = producer_bytes(w.m, w.k, w.swiglu)
         print(json.dumps({"mode": "shapes", "workload": name, "m": w.m, "n": w.n, "k": w.k,
                           "producer": "swiglu" if w.swiglu else "plain", "producer_ms": round(t_prod, 4),
                           "producer_gbs": round(pbytes / (t_prod * 1e-3) / 1e9, 1), "gemm_ms": round(t_gemm, 4),
                           "gemm_tflops": round(tflops, 2), "gemm_frac_of_peak": round(tflops / PEAK_MFMA_TFLOPS, 4),
+                          "producer_modulate_ms": None if t_mod is None else round(t_mod, 4),
                           "steps": args.steps}), flush=True)
         del x, u, wt, a, wq, d
         torch.cuda.empty_cache()

@@ -126,6 +126,23 @@ int nvfp4_quantize(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, voi
                    void* scales_dev, float* global_scale_dev, void* workspace_dev, void* stream);
 
 /*
+ * Modulated plain quantization: NVFP4 of the adaLN-modulated activation
+ *   y = RN_bf16(fma_fp32(x, RN_fp32(1 + scale[c]), shift[c]))
+ * in one launch, for the QKV and FC1 inputs (the pages list a fused modulation at
+ * those NVFP4 boundaries, next to the SwiGLU fusion of FC2). The modulation is
+ * evaluated in fp32 (one correctly rounded fused multiply-add) and rounded once to
+ * bf16, and y then goes through the nvfp4_quantize contract exactly.
+ *
+ * scale_dev, shift_dev : bf16 [k] (one sample's modulation vectors), 16-byte
+ *                        aligned, finite. Read only.
+ * Every other argument, layout and output as nvfp4_quantize; rows past the logical
+ * rows are zero (padding), not the shift.
+ */
+int nvfp4_quantize_modulate(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, const void* scale_dev,
+                            const void* shift_dev, void* qdata_dev, void* scales_dev, float* global_scale_dev,
+                            void* workspace_dev, void* stream);
+
+/*
  * Single-read producer: nvfp4_quantize_swiglu with the tensor amax supplied by the
  * caller, so every input byte is read once. The component-2 summary's conclusions
  * name the global scale as the dependency an exact fused producer must synchronize

@@ -51,6 +51,7 @@ SIGNATURES = {
     "nvfp4_init": (_INT, []),
     "nvfp4_quantize_swiglu": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_quantize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "nvfp4_quantize_modulate": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "nvfp4_quantize_swiglu_amax": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_quantize_amax": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_gemm_bf16out": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
@@ -233,6 +234,24 @@ def nvfp4_quantize(x, out: Optional[Nvfp4Tensor] = None, rows: Optional[int] = N
     ws = _workspace(x.device, sh) if workspace is None else workspace
     _call("nvfp4_quantize", x.data_ptr(), x.stride(0), rows, k, out.qdata.data_ptr(), out.scales.data_ptr(),
           out.global_scale.data_ptr(), ws.data_ptr(), sh)
+    return out
+
+
+def nvfp4_quantize_modulate(x, scale, shift, out: Optional[Nvfp4Tensor] = None, rows: Optional[int] = None,
+                            workspace=None, stream=None) -> Nvfp4Tensor:
+    """NVFP4 of y = RN_bf16(fma_fp32(x, 1 + scale, shift)) (scale, shift: bf16 [k])."""
+    import torch
+    _bf16_2d(x, "x")
+    rows = x.shape[0] if rows is None else rows
+    k = x.shape[1]
+    for name, t in (("scale", scale), ("shift", shift)):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (k,) or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor of shape ({k},)")
+    out = empty_nvfp4(rows, k, x.device) if out is None else out
+    sh = _stream_handle(stream)
+    ws = _workspace(x.device, sh) if workspace is None else workspace
+    _call("nvfp4_quantize_modulate", x.data_ptr(), x.stride(0), rows, k, scale.data_ptr(), shift.data_ptr(),
+          out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(), sh)
     return out
 
 

@@ -18,13 +18,14 @@ namespace nvfp4 {
 hipError_t silu_table_address(const uint16_t** p);
 hipError_t launch_silu_table_init(hipStream_t stream);
 hipError_t launch_silu_apply(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t stream);
-size_t producer_smem_bytes(bool swiglu);
-const void* producer_kernel_ptr(bool swiglu, bool given);
+// producer modes: 0 plain, 1 SwiGLU, 2 modulated plain
+size_t producer_smem_bytes(int mode);
+const void* producer_kernel_ptr(int mode, bool given);
 int producer_block_threads();
-hipError_t launch_producer(bool swiglu, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
-                           int64_t m, int64_t k, uint8_t* qdata, uint8_t* scales, float* gout,
-                           const float* amax_in, void* workspace, const uint16_t* silu_table, int max_blocks,
-                           hipStream_t stream);
+hipError_t launch_producer(int mode, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
+                           const uint16_t* mod_scale, const uint16_t* mod_shift, int64_t m, int64_t k,
+                           uint8_t* qdata, uint8_t* scales, float* gout, const float* amax_in, void* workspace,
+                           const uint16_t* silu_table, int max_blocks, hipStream_t stream);
 size_t gemm_smem_bytes();
 const void* gemm_kernel_ptr(bool fused);
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
@@ -41,8 +42,7 @@ constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;  // 32-bit buffer offsets 
 struct DeviceState {
   bool ready = false;
   const uint16_t* silu_table = nullptr;
-  int producer_blocks_swiglu = 0;
-  int producer_blocks_plain = 0;
+  int producer_blocks[3] = {0, 0, 0};  // persistent grid per producer mode
   int cu_count = 0;
   char arch[64] = {0};
 };
@@ -93,19 +93,19 @@ int ensure_device(DeviceState** out) {
   if (!prop.cooperativeLaunch) return fail(NVFP4_ERR_NO_DEVICE, "device %d lacks cooperative launch", dev);
 
   // kernels with more than 64 KiB of dynamic LDS must opt in
-  for (int sw = 0; sw < 2; ++sw) {
+  for (int mode = 0; mode < 3; ++mode) {
     for (int given = 0; given < 2; ++given) {
-      e = hipFuncSetAttribute(nvfp4::producer_kernel_ptr(sw != 0, given != 0),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)nvfp4::producer_smem_bytes(sw != 0));
+      e = hipFuncSetAttribute(nvfp4::producer_kernel_ptr(mode, given != 0),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)nvfp4::producer_smem_bytes(mode));
       if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer LDS attribute: %s", hipGetErrorString(e));
     }
     int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nvfp4::producer_kernel_ptr(sw != 0, false),
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nvfp4::producer_kernel_ptr(mode, false),
                                                      nvfp4::producer_block_threads(),
-                                                     nvfp4::producer_smem_bytes(sw != 0));
+                                                     nvfp4::producer_smem_bytes(mode));
     if (e != hipSuccess || per_cu < 1)
       return fail(NVFP4_ERR_LAUNCH, "producer occupancy query: %s (%d)", hipGetErrorString(e), per_cu);
-    (sw ? st.producer_blocks_swiglu : st.producer_blocks_plain) = per_cu * st.cu_count;
+    st.producer_blocks[mode] = per_cu * st.cu_count;
   }
   for (int fused = 0; fused < 2; ++fused) {
     e = hipFuncSetAttribute(nvfp4::gemm_kernel_ptr(fused != 0), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -175,18 +175,24 @@ int nvfp4_init(void) {
   return rc == NVFP4_OK ? ok() : rc;
 }
 
-static int quantize_common(bool swiglu, bool given, const void* x, int64_t ldx, const void* u, int64_t ldu,
-                           int64_t m, int64_t k, void* qdata, void* scales, float* g, const float* amax, void* ws,
-                           void* stream) {
+static int quantize_common(int mode, bool given, const void* x, int64_t ldx, const void* u, int64_t ldu,
+                           const void* mod_scale, const void* mod_shift, int64_t m, int64_t k, void* qdata,
+                           void* scales, float* g, const float* amax, void* ws, void* stream) {
+  const bool swiglu = mode == 1;
   int rc = check_quant_args(x, ldx, u, ldu, swiglu, m, k, qdata, scales, g, given ? (const void*)amax : ws, given);
   if (rc != NVFP4_OK) return rc;
+  if (mode == 2) {
+    if (!mod_scale || !mod_shift) return fail(NVFP4_ERR_INVALID_ARG, "null modulation scale or shift");
+    if (!aligned16(mod_scale) || !aligned16(mod_shift))
+      return fail(NVFP4_ERR_MISALIGNED, "modulation scale and shift must be 16-byte aligned");
+  }
   DeviceState* st = nullptr;
   rc = ensure_device(&st);
   if (rc != NVFP4_OK) return rc;
-  hipError_t e = nvfp4::launch_producer(swiglu, (const uint16_t*)x, ldx, (const uint16_t*)u, ldu, m, k,
+  hipError_t e = nvfp4::launch_producer(mode, (const uint16_t*)x, ldx, (const uint16_t*)u, ldu,
+                                        (const uint16_t*)mod_scale, (const uint16_t*)mod_shift, m, k,
                                         (uint8_t*)qdata, (uint8_t*)scales, g, amax, ws, st->silu_table,
-                                        swiglu ? st->producer_blocks_swiglu : st->producer_blocks_plain,
-                                        (hipStream_t)stream);
+                                        st->producer_blocks[mode], (hipStream_t)stream);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -194,27 +200,34 @@ static int quantize_common(bool swiglu, bool given, const void* x, int64_t ldx, 
 int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up, int64_t m,
                           int64_t k, void* qdata_dev, void* scales_dev, float* global_scale_dev, void* workspace_dev,
                           void* stream) {
-  return quantize_common(true, false, gate_dev, ld_gate, up_dev, ld_up, m, k, qdata_dev, scales_dev, global_scale_dev,
-                         nullptr, workspace_dev, stream);
+  return quantize_common(1, false, gate_dev, ld_gate, up_dev, ld_up, nullptr, nullptr, m, k, qdata_dev, scales_dev,
+                         global_scale_dev, nullptr, workspace_dev, stream);
 }
 
 int nvfp4_quantize_swiglu_amax(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up, int64_t m,
                                int64_t k, const float* amax_dev, void* qdata_dev, void* scales_dev,
                                float* global_scale_dev, void* stream) {
-  return quantize_common(true, true, gate_dev, ld_gate, up_dev, ld_up, m, k, qdata_dev, scales_dev, global_scale_dev,
-                         amax_dev, nullptr, stream);
+  return quantize_common(1, true, gate_dev, ld_gate, up_dev, ld_up, nullptr, nullptr, m, k, qdata_dev, scales_dev,
+                         global_scale_dev, amax_dev, nullptr, stream);
 }
 
 int nvfp4_quantize(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, void* qdata_dev, void* scales_dev,
                    float* global_scale_dev, void* workspace_dev, void* stream) {
-  return quantize_common(false, false, x_dev, ld_x, nullptr, 0, rows, k, qdata_dev, scales_dev, global_scale_dev,
-                         nullptr, workspace_dev, stream);
+  return quantize_common(0, false, x_dev, ld_x, nullptr, 0, nullptr, nullptr, rows, k, qdata_dev, scales_dev,
+                         global_scale_dev, nullptr, workspace_dev, stream);
+}
+
+int nvfp4_quantize_modulate(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, const void* scale_dev,
+                            const void* shift_dev, void* qdata_dev, void* scales_dev, float* global_scale_dev,
+                            void* workspace_dev, void* stream) {
+  return quantize_common(2, false, x_dev, ld_x, nullptr, 0, scale_dev, shift_dev, rows, k, qdata_dev, scales_dev,
+                         global_scale_dev, nullptr, workspace_dev, stream);
 }
 
 int nvfp4_quantize_amax(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, const float* amax_dev,
                         void* qdata_dev, void* scales_dev, float* global_scale_dev, void* stream) {
-  return quantize_common(false, true, x_dev, ld_x, nullptr, 0, rows, k, qdata_dev, scales_dev, global_scale_dev,
-                         amax_dev, nullptr, stream);
+  return quantize_common(0, true, x_dev, ld_x, nullptr, 0, nullptr, nullptr, rows, k, qdata_dev, scales_dev,
+                         global_scale_dev, amax_dev, nullptr, stream);
 }
 
 static int gemm_common(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,

@@ -67,6 +67,8 @@ struct ProducerArgs {
   uint8_t* scales;
   float* gout;
   const float* amax_in;  // caller-supplied amax (single-pass variant), else unused
+  const uint16_t* mod_scale;  // modulation scale and shift, bf16 [k] (MODE kModulate)
+  const uint16_t* mod_shift;
   ProducerWorkspace* ws;
   const uint16_t* silu_table;
 };
@@ -195,13 +197,32 @@ __device__ __noinline__ Y8 block_y_fix(u32x4_t g0, u32x4_t g1, u32x4_t u0, u32x4
   return yb;
 }
 
-// y for the 16 elements of one block, as 8 packed bf16 pairs. Products are formed in
-// fp32 (exact whenever the result is a normal fp32 number); the caller detects blocks
-// that may hold a rounded subnormal product and repairs them with block_y_fix.
-template <bool SWIGLU>
-__device__ __forceinline__ void block_y(const u32x4_t (&gv)[2], const u32x4_t (&uv)[2], const uint16_t* tab,
-                                        uint32_t (&yb)[8]) {
-  if (SWIGLU) {
+// What y is: x itself, RN_bf16(silu_bf16(gate) * up), or the adaLN-modulated
+// RN_bf16(fma_fp32(x, RN_fp32(1 + scale), shift)).
+constexpr int kPlain = 0, kSwiglu = 1, kModulate = 2;
+
+// The modulated value of one bf16 element (as fp32 before the bf16 rounding).
+__device__ __forceinline__ float modulate_f32(uint32_t x16, uint32_t scale16, uint32_t shift16) {
+  const float m = 1.0f + bf16_bits_to_float(scale16);
+  return __builtin_fmaf(bf16_bits_to_float(x16), m, bf16_bits_to_float(shift16));
+}
+
+// y for the 16 elements of one block, as 8 packed bf16 pairs. For kSwiglu, uv holds
+// up; for kModulate, the item's scale (mv[0]) and shift (mv[1]) of the lane's 16
+// columns. Products are formed in fp32 (exact whenever the result is a normal fp32
+// number); the caller detects blocks that may hold a rounded subnormal product and
+// repairs them with block_y_fix.
+template <int MODE>
+__device__ __forceinline__ void block_y(const u32x4_t (&gv)[2], const u32x4_t (&uv)[2],
+                                        const u32x4_t (&mv)[2][2], const uint16_t* tab, uint32_t (&yb)[8]) {
+  if (MODE == kModulate) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t xw = gv[w >> 2][w & 3], sw = mv[0][w >> 2][w & 3], bw = mv[1][w >> 2][w & 3];
+      yb[w] = cvt_pk_bf16(modulate_f32(xw & 0xFFFFu, sw & 0xFFFFu, bw & 0xFFFFu),
+                          modulate_f32(xw >> 16, sw >> 16, bw >> 16));
+    }
+  } else if (MODE == kSwiglu) {
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const uint32_t gw = gv[w >> 2][w & 3], uw = uv[w >> 2][w & 3];
@@ -238,8 +259,9 @@ __device__ __forceinline__ void block_mag_range(const uint32_t (&yb)[8], uint32_
 
 // GIVEN: the tensor amax comes from the caller (a device float); pass 1 and the grid
 // barrier are skipped and the launch needs no co-residency.
-template <bool SWIGLU, bool GIVEN>
+template <int MODE, bool GIVEN>
 __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) {
+  constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint32_t* red = (uint32_t*)smem;                          // wave maxima + two broadcast slots
   uint16_t* tab = (uint16_t*)(smem + kRedBytes);            // 65,536 entries (SwiGLU only)
@@ -260,9 +282,22 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
 
   // the 16 bf16 values of this lane's block in each step of an item (zero outside
   // the logical rows and columns)
+  // For kModulate the up slots carry the item's modulation instead: uv[0] = the
+  // scale and uv[1] = the shift of the lane's 16 columns (kSteps == 2).
+  static_assert(kSteps == 2, "modulation vectors ride in the two up slots");
   auto load_item = [&](int item, u32x4_t (&gv)[kSteps][2], u32x4_t (&uv)[kSteps][2]) {
     const int rt = item / a.items_k, kt = item - rt * a.items_k;
     const int64_t col = (int64_t)kt * kItemCols + blk * 16;
+    if (MOD) {
+      const bool cok = col < a.k;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      const u32x4_t* ps = (const u32x4_t*)(a.mod_scale + col);
+      const u32x4_t* pb = (const u32x4_t*)(a.mod_shift + col);
+      uv[0][0] = cok ? ps[0] : z;
+      uv[0][1] = cok ? ps[1] : z;
+      uv[1][0] = cok ? pb[0] : z;
+      uv[1][1] = cok ? pb[1] : z;
+    }
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const int64_t row = (int64_t)rt * kItemRows + s * kRowsPerStep + wave * kWaveRows + r4;
@@ -285,13 +320,22 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
   } else {
     // ---------------- pass 1: absmax ----------------
     uint32_t local_bits = 0;  // fp32 bits of a non-negative value
-    auto absmax_item = [&](const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
+    // rows past m read zeros; only the modulation would turn them into nonzero y
+    auto absmax_item = [&](int item, const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
+      const int64_t row0 = (int64_t)(item / a.items_k) * kItemRows + wave * kWaveRows + r4;
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
+        if (MOD && row0 + s * kRowsPerStep >= a.m) continue;
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
           const uint32_t gw = gv[s][w >> 2][w & 3];
-          if (SWIGLU) {
+          if (MOD) {
+            const uint32_t sw = uv[0][w >> 2][w & 3], bw = uv[1][w >> 2][w & 3];
+            const float p0 = fabsf(modulate_f32(gw & 0xFFFFu, sw & 0xFFFFu, bw & 0xFFFFu));
+            const float p1 = fabsf(modulate_f32(gw >> 16, sw >> 16, bw >> 16));
+            const uint32_t b = __float_as_uint(fmaxf(p0, p1));
+            local_bits = b > local_bits ? b : local_bits;
+          } else if (SWIGLU) {
             const uint32_t uw = uv[s][w >> 2][w & 3];
             const float s0 = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16);
             const float s1 = __uint_as_float((uint32_t)tab[gw >> 16] << 16);
@@ -315,12 +359,12 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
       while (item < nitems) {
         const int n1 = item + (int)gridDim.x;
         if (n1 < nitems) load_item(n1, gB, uB);
-        absmax_item(gA, uA);
+        absmax_item(item, gA, uA);
         item = n1;
         if (item >= nitems) break;
         const int n2 = item + (int)gridDim.x;
         if (n2 < nitems) load_item(n2, gA, uA);
-        absmax_item(gB, uB);
+        absmax_item(item, gB, uB);
         item = n2;
       }
     }
@@ -367,7 +411,7 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
       }
       __syncthreads();
       local_bits = red[kWaves];
-    } else if (SWIGLU) {
+    } else if (SWIGLU || MOD) {
       // RN_bf16 is monotone, so the rounded maximum is the maximum of the rounded values.
       local_bits = (cvt_pk_bf16(__uint_as_float(local_bits), 0.0f) & 0xFFFFu) << 16;
     }
@@ -414,7 +458,11 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
       const int lrow = s * kRowsPerStep + wave * kWaveRows + r4;
       const int64_t row = (int64_t)rt * kItemRows + lrow;
       uint32_t yb[8];
-      block_y<SWIGLU>(gv[s], uv[s], tab, yb);
+      block_y<MODE>(gv[s], uv[s], uv, tab, yb);
+      if (MOD && row >= a.m) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) yb[w] = 0u;  // padding rows are zero, not the shift
+      }
       // block maximum of |y| (bf16 magnitudes compare as integers)
       uint32_t mx, mn;
       block_mag_range(yb, mx, mn);
@@ -482,23 +530,26 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
 
 // ---- host side --------------------------------------------------------------------------------
 
-size_t producer_smem_bytes(bool swiglu) {
-  return kRedBytes + (swiglu ? 65536 * 2 : 0);
+size_t producer_smem_bytes(int mode) {
+  return kRedBytes + (mode == kSwiglu ? 65536 * 2 : 0);
 }
 
-const void* producer_kernel_ptr(bool swiglu, bool given) {
-  if (given) return swiglu ? (const void*)producer_kernel<true, true> : (const void*)producer_kernel<false, true>;
-  return swiglu ? (const void*)producer_kernel<true, false> : (const void*)producer_kernel<false, false>;
+const void* producer_kernel_ptr(int mode, bool given) {
+  if (mode == kSwiglu)
+    return given ? (const void*)producer_kernel<kSwiglu, true> : (const void*)producer_kernel<kSwiglu, false>;
+  if (mode == kModulate)
+    return given ? (const void*)producer_kernel<kModulate, true> : (const void*)producer_kernel<kModulate, false>;
+  return given ? (const void*)producer_kernel<kPlain, true> : (const void*)producer_kernel<kPlain, false>;
 }
 
 int producer_block_threads() { return kProdThreads; }
 
 // amax_in == nullptr: the two-pass producer (cooperative launch, workspace used);
 // otherwise the single-pass producer with the caller's amax (ordinary launch).
-hipError_t launch_producer(bool swiglu, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
-                           int64_t m, int64_t k, uint8_t* qdata, uint8_t* scales, float* gout,
-                           const float* amax_in, void* workspace, const uint16_t* silu_table, int max_blocks,
-                           hipStream_t stream) {
+hipError_t launch_producer(int mode, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
+                           const uint16_t* mod_scale, const uint16_t* mod_shift, int64_t m, int64_t k,
+                           uint8_t* qdata, uint8_t* scales, float* gout, const float* amax_in, void* workspace,
+                           const uint16_t* silu_table, int max_blocks, hipStream_t stream) {
   ProducerArgs args;
   args.x = x;
   args.u = u;
@@ -515,6 +566,8 @@ hipError_t launch_producer(bool swiglu, const uint16_t* x, int64_t ldx, const ui
   args.scales = scales;
   args.gout = gout;
   args.amax_in = amax_in;
+  args.mod_scale = mod_scale;
+  args.mod_shift = mod_shift;
   args.ws = (ProducerWorkspace*)workspace;
   args.silu_table = silu_table;
   const int64_t nitems = (int64_t)args.items_m * args.items_k;
@@ -522,10 +575,10 @@ hipError_t launch_producer(bool swiglu, const uint16_t* x, int64_t ldx, const ui
   if (blocks < 1) blocks = 1;
   void* kargs[] = {&args};
   if (amax_in)
-    return hipLaunchKernel(producer_kernel_ptr(swiglu, true), dim3(blocks), dim3(kProdThreads), kargs,
-                           producer_smem_bytes(swiglu), stream);
-  return hipLaunchCooperativeKernel(producer_kernel_ptr(swiglu, false), dim3(blocks), dim3(kProdThreads), kargs,
-                                    (unsigned)producer_smem_bytes(swiglu), stream);
+    return hipLaunchKernel(producer_kernel_ptr(mode, true), dim3(blocks), dim3(kProdThreads), kargs,
+                           producer_smem_bytes(mode), stream);
+  return hipLaunchCooperativeKernel(producer_kernel_ptr(mode, false), dim3(blocks), dim3(kProdThreads), kargs,
+                                    (unsigned)producer_smem_bytes(mode), stream);
 }
 
 }  // namespace nvfp4

@@ -141,6 +141,21 @@ def test_gemm_validation(kw, status):
     assert call_gemm(**kw) == status
 
 
+def call_modulate(**kw):
+    args = dict(x=FAKE, ld=64, rows=16, k=64, sc=FAKE, sh=FAKE, q=FAKE, s=FAKE, g=FAKE, ws=FAKE)
+    args.update(kw)
+    return nv.lib().nvfp4_quantize_modulate(args["x"], args["ld"], args["rows"], args["k"], args["sc"], args["sh"],
+                                            args["q"], args["s"], args["g"], args["ws"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sc=None), 1), (dict(sh=None), 1), (dict(sc=FAKE + 2), 3), (dict(sh=FAKE + 8), 3), (dict(ws=None), 4),
+    (dict(x=None), 1), (dict(k=96, ld=96), 2),
+])
+def test_modulate_validation(kw, status):
+    assert call_modulate(**kw) == status
+
+
 def call_fused(**kw):
     args = dict(aq=FAKE, as_=FAKE, ga=FAKE, wq=FAKE, ws=FAKE, gw=FAKE, d=FAKE, m=16, n=16, k=64, b=None, g=None,
                 r=None)

@@ -449,7 +449,7 @@ def main() -> int:
             "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
             "traffic": measured_gemm_traffic() if w.name == "fc2_canonical" else None,
             "traffic_summary": GEMM_TRAFFIC_SUMMARY,
-            "kernel": "nvfp4::gemm_kernel",
+            "kernel": "nvfp4::gemm_kernel<0>",
             "algorithmic_per_launch": f"{w.gemm_flops:.4e} FLOP (2*M*N*K, logical M)",
             "avg_launch_ms": round(t_gemm, 4),
         },

@@ -55,6 +55,8 @@ def _load():
                                                 _P, ctypes.c_int]),
         "oracle_modulate_bf16": (ctypes.c_uint16, [ctypes.c_uint16, ctypes.c_uint16, ctypes.c_uint16]),
         "oracle_quantize_modulate": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_int]),
+        "oracle_gemm_swiglu_rows": (ctypes.c_int, [_P, _P, _I64, ctypes.c_float, _P, _P, _I64, ctypes.c_float,
+                                                   _I64, _P, _I64, _P, _P, _P, _P, ctypes.c_int]),
         "oracle_gemm_rows_ex": (ctypes.c_int, [_P, _P, _I64, ctypes.c_float, _P, _P, _I64, ctypes.c_float,
                                                _I64, _P, _I64, _P, _P, _P, _I64, _P, _P, ctypes.c_int]),
         "oracle_gemm_rows": (ctypes.c_int, [_P, _P, _I64, ctypes.c_float, _P, _P, _I64,
@@ -259,6 +261,43 @@ def gemm_rows_ex(a_q: np.ndarray, a_s: np.ndarray, a_rows: int, ga: float, w_q: 
     if rc != 0:
         raise ValueError(f"oracle_gemm_rows_ex failed ({rc})")
     return d1, d
+
+
+def gemm_swiglu_rows(a_q: np.ndarray, a_s: np.ndarray, a_rows: int, ga: float, w_q: np.ndarray,
+                     w_s: np.ndarray, n_half: int, gw: float, k: int, rows: Sequence[int],
+                     bias: Optional[np.ndarray] = None, threads: Optional[int] = None):
+    """O14: (gate, up, ymax) for the selected activation rows: gate and up are bf16 bits
+    [len(rows), n_half], ymax float32 [len(rows)] (max |RN_bf16(silu(gate) * up)|).
+    The weight holds 2 n_half rows, gate and up interleaved in chunks of 8."""
+    a_q = np.ascontiguousarray(a_q, dtype=np.uint8)
+    a_s = np.ascontiguousarray(a_s, dtype=np.uint8)
+    w_q = np.ascontiguousarray(w_q, dtype=np.uint8)
+    w_s = np.ascontiguousarray(w_s, dtype=np.uint8)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+    if bias is not None:
+        assert bias.shape == (2 * n_half,)
+    gate = np.empty((rows.shape[0], n_half), dtype=np.uint16)
+    up = np.empty((rows.shape[0], n_half), dtype=np.uint16)
+    ymax = np.empty(rows.shape[0], dtype=np.float32)
+    rc = _load().oracle_gemm_swiglu_rows(a_q.ctypes.data, a_s.ctypes.data, a_rows, ga, w_q.ctypes.data,
+                                         w_s.ctypes.data, n_half, gw, k, rows.ctypes.data, rows.shape[0],
+                                         None if bias is None else bias.ctypes.data, gate.ctypes.data,
+                                         up.ctypes.data, ymax.ctypes.data, threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_swiglu_rows failed ({rc})")
+    return gate, up, ymax
+
+
+def interleave_swiglu_rows(gate_w: np.ndarray, up_w: np.ndarray) -> np.ndarray:
+    """The chunk-of-8 interleaving of O14: [n_half, k] gate and up rows -> [2 n_half, k]."""
+    n_half, k = gate_w.shape
+    assert up_w.shape == (n_half, k) and n_half % 8 == 0
+    out = np.empty((2 * n_half, k), dtype=gate_w.dtype)
+    v = out.reshape(n_half // 8, 2, 8, k)
+    v[:, 0] = gate_w.reshape(n_half // 8, 8, k)
+    v[:, 1] = up_w.reshape(n_half // 8, 8, k)
+    return out
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

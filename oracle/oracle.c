@@ -31,6 +31,9 @@
  *                     evaluated exactly in integers
  *   O11 given amax    O4-O8 with amax supplied by the caller (single-read
  *                     producer); a block above v(126) * 6 * g saturates
+ *   O14 SwiGLU pair   FC1 GEMM over chunk-of-8 interleaved gate/up weight rows:
+ *                     D1 split into gate and up, and the row maxima of
+ *                     |RN_bf16(silu_bf16(gate) * up)| (the FC2 quantizer's amax)
  *   O13 modulation    y = RN_bf16(fma_fp32(x, RN_fp32(1 + scale[k]), shift[k]))
  *                     feeding O3-O8 (plain quantization of the modulated input)
  *   O12 epilogue      D1 = RN_bf16(O10's exact value + bias[n]); with a residual,
@@ -609,6 +612,52 @@ int oracle_gemm_rows(const uint8_t* aq, const uint8_t* as, int64_t a_rows_total,
  * D1 = RN_bf16(g_a g_w sum ... + bias[j]); out receives D = RN_bf16(res + gate * D1)
  * when res is given, else D1. Gate without residual is rejected.
  */
+/*
+ * O14: the SwiGLU-pair GEMM. The weight's 2 n_half rows are the gate and up rows of
+ * the FC1 projection interleaved in chunks of 8: rows 16c .. 16c+7 are gate channels
+ * 8c .. 8c+7 and rows 16c+8 .. 16c+15 are up channels 8c .. 8c+7 (a layout choice of
+ * this library). For each selected row, D1 (O12 with the optional bias over the 2
+ * n_half columns) is split into gate[j] and up[j], j < n_half, and
+ * y = RN_bf16(silu_bf16(gate) * up) (O1-O2); ymax[i] = max_j |y| of that row.
+ */
+int oracle_gemm_swiglu_rows(const uint8_t* aq, const uint8_t* as, int64_t a_rows_total, float ga,
+                            const uint8_t* wq, const uint8_t* ws, int64_t n_half, float gw, int64_t k,
+                            const int64_t* rows, int64_t nrows, const uint16_t* bias, uint16_t* out_gate,
+                            uint16_t* out_up, float* out_ymax, int nthreads) {
+  if (n_half <= 0 || n_half % 8 != 0 || !out_gate || !out_up || !out_ymax) return OR_EINVAL;
+  const int64_t n = 2 * n_half;
+  uint16_t* d = (uint16_t*)malloc((size_t)(nrows ? nrows : 1) * (size_t)n * sizeof(uint16_t));
+  uint16_t* tab = (uint16_t*)malloc(65536 * sizeof(uint16_t));
+  if (!d || !tab) {
+    free(d);
+    free(tab);
+    return OR_ENOMEM;
+  }
+  int rc = gemm_rows_core(aq, as, a_rows_total, ga, wq, ws, n, gw, k, rows, nrows, bias, NULL, NULL, 0, NULL, d,
+                          nthreads);
+  if (rc != OR_OK) {
+    free(d);
+    free(tab);
+    return rc;
+  }
+  oracle_silu_table(tab);
+  for (int64_t i = 0; i < nrows; ++i) {
+    double ymax = 0.0;
+    for (int64_t j = 0; j < n_half; ++j) {
+      const int64_t c = j / 8, e = j % 8;
+      const uint16_t g = d[i * n + 16 * c + e], u = d[i * n + 16 * c + 8 + e];
+      out_gate[i * n_half + j] = g;
+      out_up[i * n_half + j] = u;
+      const double y = fabs(bf16_to_double(oracle_swiglu_bf16(g, u, tab)));
+      if (y > ymax) ymax = y;
+    }
+    out_ymax[i] = (float)ymax; /* a bf16 value: exact in float */
+  }
+  free(d);
+  free(tab);
+  return OR_OK;
+}
+
 int oracle_gemm_rows_ex(const uint8_t* aq, const uint8_t* as, int64_t a_rows_total, float ga,
                         const uint8_t* wq, const uint8_t* ws, int64_t n, float gw, int64_t k,
                         const int64_t* rows, int64_t nrows, const uint16_t* bias, const uint16_t* gate,

@@ -275,6 +275,91 @@ def shapes(args, dev) -> int:
     return 0
 
 
+def chain(args, dev) -> int:
+    """The MLP block with every fusion, on the FC1 and FC2 shapes (M = 37,810):
+      modulated quantize (f2) -> FC1 SwiGLU-pair GEMM emitting amax (f3)
+      -> single-read FC2 producer (f1) -> FC2 GEMM with bias + gated residual (f3),
+    against the unfused path on the same operands: plain quantize of the modulated
+    input, FC1 GEMM, two-pass FC2 producer, FC2 GEMM. Weights are quantized once,
+    outside the timing; the modulation and gate vectors are seeded."""
+    import statistics
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    import synth
+    from tests import parity
+    w1, w2 = synth.BY_NAME["fc1"], synth.FC2
+    m, k1, nh, n2 = w1.m, w1.k, w1.n // 2, w2.n
+    g = torch.Generator(device="cpu").manual_seed(5)
+    x = parity.to_device_bf16(w1.activations()[0], dev)
+    W1 = parity.to_device_bf16(w1.weight(), dev)
+    W1i = nv.interleave_swiglu_weight(W1[:nh], W1[nh:]).contiguous()
+    del W1
+    W2 = parity.to_device_bf16(w2.weight(), dev)
+    w1q = nv.nvfp4_quantize(W1i)
+    w2q = nv.nvfp4_quantize(W2)
+    del W1i, W2
+    sc = (torch.randn(k1, generator=g) * 0.3).bfloat16().to(dev)
+    sh = (torch.randn(k1, generator=g) * 0.5).bfloat16().to(dev)
+    bias2 = (torch.randn(n2, generator=g) * 0.1).bfloat16().to(dev)
+    gate2 = (torch.randn(n2, generator=g) * 0.7).bfloat16().to(dev)
+    m_pad = nv.nvfp4_padded_rows(m)
+    res = (torch.randn(m_pad, n2, generator=g) * 0.3).bfloat16().to(dev)
+    xm = torch.empty_like(x)  # the unfused path's modulated input
+    xm.copy_((x.float() * (1.0 + sc.float()) + sh.float()).bfloat16())
+    a1 = nv.empty_nvfp4(m, k1, dev)
+    a2 = nv.empty_nvfp4(m, nh, dev)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    gate_o = torch.empty((m_pad, nh), dtype=torch.bfloat16, device=dev)
+    up_o = torch.empty_like(gate_o)
+    d1 = torch.empty((m_pad, 2 * nh), dtype=torch.bfloat16, device=dev)
+    d2 = torch.empty((m_pad, n2), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fused(ev):
+        ev[0].record(stream)
+        nv.nvfp4_quantize_modulate(x, sc, sh, out=a1)
+        ev[1].record(stream)
+        amax.zero_()
+        nv.nvfp4_gemm_swiglu_pair(a1, w1q, amax=amax, amax_rows=m, gate_out=gate_o, up_out=up_o)
+        ev[2].record(stream)
+        nv.nvfp4_quantize_swiglu_amax(gate_o[:m], up_o[:m], amax, out=a2)
+        ev[3].record(stream)
+        nv.nvfp4_gemm_bf16out_fused(a2, w2q, bias=bias2, gate=gate2, residual=res, out=d2)
+        ev[4].record(stream)
+
+    def unfused(ev):
+        ev[0].record(stream)
+        nv.nvfp4_quantize(xm, out=a1)
+        ev[1].record(stream)
+        nv.nvfp4_gemm_bf16out(a1, w1q, out=d1)
+        ev[2].record(stream)
+        nv.nvfp4_quantize_swiglu(d1[:m, :nh], d1[:m, nh:], out=a2)
+        ev[3].record(stream)
+        nv.nvfp4_gemm_bf16out(a2, w2q, out=d2)
+        ev[4].record(stream)
+
+    names = ["quantize", "fc1_gemm", "fc2_producer", "fc2_gemm"]
+    out = {"mode": "chain", "m": m, "fc1": [2 * nh, k1], "fc2": [n2, nh], "steps": args.steps}
+    for label, fn in (("fused", fused), ("unfused", unfused)):
+        for _ in range(max(1, args.warmup)):
+            fn([torch.cuda.Event(enable_timing=True) for _ in range(5)])
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        for ev in evs:
+            fn(ev)
+        torch.cuda.synchronize()
+        parts = {nm: round(statistics.fmean(ev[i].elapsed_time(ev[i + 1]) for ev in evs), 4)
+                 for i, nm in enumerate(names)}
+        parts["total_ms"] = round(sum(parts[nm] for nm in names), 4)
+        out[label] = parts
+    out["fused_over_unfused"] = round(out["fused"]["total_ms"] / out["unfused"]["total_ms"], 4)
+    out["note"] = ("fused: modulate+quantize, FC1 SwiGLU-pair GEMM emitting amax, single-read FC2 producer, "
+                   "FC2 GEMM with bias and gated residual; unfused: the same GEMMs and quantizers without "
+                   "the fusions (its modulation, gate add and bias would be further kernels, not timed)")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +370,8 @@ def main() -> int:
     ap.add_argument("--only-gemm", action="store_true",
                     help="time the GEMM alone on seeded random NVFP4 operand bytes (no producer launch in "
                          "the process; used for profiler counter runs)")
+    ap.add_argument("--chain", action="store_true",
+                    help="the MLP block with every fusion against the unfused path, one JSON line")
     ap.add_argument("--shapes", action="store_true",
                     help="producer + GEMM on every projection shape, one JSON line each")
     ap.add_argument("--only-producer", action="store_true",
@@ -314,6 +401,8 @@ def main() -> int:
         return only_producer(w, args, dev)
     if args.shapes:
         return shapes(args, dev)
+    if args.chain:
+        return chain(args, dev)
 
     t0 = time.perf_counter()
     acts = w.activations()

@@ -218,6 +218,34 @@ int nvfp4_gemm_bf16out_fused(const void* a_qdata_dev, const void* a_scales_dev, 
                              void* d_dev, int64_t m_padded, int64_t n, int64_t k, const void* bias_dev,
                              const void* gate_dev, const void* residual_dev, void* stream);
 
+/*
+ * The SwiGLU-pair GEMM: the FC1 projection that also produces the FC2 quantizer's
+ * amax. The component-2 summary's conclusions put the global-scale dependency at
+ * the FC2 producer and point at removing traffic where two NVFP4 stages meet; here
+ * the stage that writes gate and up also reduces max |y| for
+ * nvfp4_quantize_swiglu_amax, which then reads each input byte once.
+ *
+ * w_*              : the FC1 weight, 2 n_half rows, as written by nvfp4_quantize,
+ *                    with gate and up rows interleaved in chunks of 8: rows
+ *                    16c .. 16c+7 are gate channels 8c .. 8c+7 and rows
+ *                    16c+8 .. 16c+15 the up channels 8c .. 8c+7.
+ * gate_dev, up_dev : out, bf16 [m_padded, n_half] row-major each, 16-byte aligned:
+ *                    D1 = RN_bf16(g_a g_w sum + bias) (as nvfp4_gemm_bf16out_fused)
+ *                    split back into the gate and up channels.
+ * bias_dev         : bf16 [2 n_half] in the interleaved order, or NULL.
+ * amax_dev         : device float or NULL. The kernel folds
+ *                    max |RN_bf16(silu_bf16(gate) * up)| over rows < amax_rows into
+ *                    it with an atomic max, so the caller sets it (to 0, or to a
+ *                    running maximum; a non-negative number) before the call;
+ *                    4-byte aligned. Calls that fold into one amax may overlap.
+ * amax_rows        : the logical rows, 0 <= amax_rows <= m_padded.
+ * n_half           : a positive multiple of 8. Other arguments as nvfp4_gemm_bf16out.
+ */
+int nvfp4_gemm_swiglu_pair(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
+                           const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
+                           void* gate_dev, void* up_dev, int64_t m_padded, int64_t n_half, int64_t k,
+                           const void* bias_dev, float* amax_dev, int64_t amax_rows, void* stream);
+
 /* ---- self-test hook ---------------------------------------------------------------------- */
 
 /* y[i] = silu_bf16(x[i]) for i < count, bf16 bit patterns, with the table the

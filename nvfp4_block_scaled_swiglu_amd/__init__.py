@@ -56,6 +56,7 @@ SIGNATURES = {
     "nvfp4_quantize_amax": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_gemm_bf16out": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "nvfp4_gemm_bf16out_fused": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "nvfp4_gemm_swiglu_pair": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P]),
     "nvfp4_silu_bf16": (_INT, [_P, _P, _I64, _P]),
     "nvfp4_status_string": (ctypes.c_char_p, [_INT]),
     "nvfp4_last_error": (ctypes.c_char_p, []),
@@ -328,6 +329,47 @@ def nvfp4_gemm_bf16out_fused(a: Nvfp4Tensor, w: Nvfp4Tensor, bias=None, gate=Non
           w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), out.data_ptr(), m_pad, n, a.k,
           ptr(bias), ptr(gate), ptr(residual), _stream_handle(stream))
     return out
+
+
+def interleave_swiglu_weight(w_gate, w_up):
+    """[n_half, k] gate and up weights -> [2 n_half, k] with rows interleaved in chunks
+    of 8 (the layout nvfp4_gemm_swiglu_pair expects)."""
+    n_half, k = w_gate.shape
+    if tuple(w_up.shape) != (n_half, k) or n_half % 8 != 0:
+        raise ValueError("gate and up weights must be [n_half, k] with n_half % 8 == 0")
+    return _torch_stack_chunks(w_gate, w_up)
+
+
+def _torch_stack_chunks(a, b):
+    import torch
+    n_half, k = a.shape
+    return torch.stack([a.reshape(n_half // 8, 8, k), b.reshape(n_half // 8, 8, k)], dim=1).reshape(2 * n_half, k)
+
+
+def nvfp4_gemm_swiglu_pair(a: Nvfp4Tensor, w: Nvfp4Tensor, bias=None, amax=None, amax_rows: Optional[int] = None,
+                           gate_out=None, up_out=None, stream=None):
+    """FC1 with the SwiGLU pair epilogue: returns (gate, up) bf16 [m_padded, n_half];
+    if amax (a float32 CUDA tensor, set by the caller) is given, max |silu(gate) * up|
+    over the logical rows is folded into it."""
+    import torch
+    if a.k != w.k or w.rows % 16 != 0:
+        raise ValueError("k mismatch or weight rows not a multiple of 16")
+    m_pad = a.padded_rows
+    n_half = w.rows // 2
+    dev = a.qdata.device
+    gate_out = torch.empty((m_pad, n_half), dtype=torch.bfloat16, device=dev) if gate_out is None else gate_out
+    up_out = torch.empty((m_pad, n_half), dtype=torch.bfloat16, device=dev) if up_out is None else up_out
+    for name, t in (("gate_out", gate_out), ("up_out", up_out)):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (m_pad, n_half) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 [m_padded, n_half] tensor")
+    if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (2 * n_half,)):
+        raise ValueError("bias must be bfloat16 [2 n_half] (interleaved order)")
+    _call("nvfp4_gemm_swiglu_pair", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
+          w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), gate_out.data_ptr(),
+          up_out.data_ptr(), m_pad, n_half, a.k, None if bias is None else bias.data_ptr(),
+          None if amax is None else _amax_ptr(amax), a.rows if amax_rows is None else amax_rows,
+          _stream_handle(stream))
+    return gate_out, up_out
 
 
 def nvfp4_silu_bf16(x, out=None, stream=None):

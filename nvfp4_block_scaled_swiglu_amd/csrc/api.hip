@@ -27,11 +27,10 @@ hipError_t launch_producer(int mode, const uint16_t* x, int64_t ldx, const uint1
                            uint8_t* qdata, uint8_t* scales, float* gout, const float* amax_in, void* workspace,
                            const uint16_t* silu_table, int max_blocks, hipStream_t stream);
 size_t gemm_smem_bytes();
-const void* gemm_kernel_ptr(bool fused);
+const void* gemm_kernel_ptr(int kind);
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
-                       const uint16_t* bias, const uint16_t* gate, const uint16_t* res, bool fused, int cu_count,
-                       hipStream_t stream);
+                       const GemmEpilogue& ep, int cu_count, hipStream_t stream);
 }  // namespace nvfp4
 
 namespace {
@@ -107,8 +106,8 @@ int ensure_device(DeviceState** out) {
       return fail(NVFP4_ERR_LAUNCH, "producer occupancy query: %s (%d)", hipGetErrorString(e), per_cu);
     st.producer_blocks[mode] = per_cu * st.cu_count;
   }
-  for (int fused = 0; fused < 2; ++fused) {
-    e = hipFuncSetAttribute(nvfp4::gemm_kernel_ptr(fused != 0), hipFuncAttributeMaxDynamicSharedMemorySize,
+  for (int kind = 0; kind < 3; ++kind) {
+    e = hipFuncSetAttribute(nvfp4::gemm_kernel_ptr(kind), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)nvfp4::gemm_smem_bytes());
     if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "gemm LDS attribute: %s", hipGetErrorString(e));
   }
@@ -232,8 +231,7 @@ int nvfp4_quantize_amax(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k
 
 static int gemm_common(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
                        const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev, void* d_dev,
-                       int64_t m_padded, int64_t n, int64_t k, const void* bias_dev, const void* gate_dev,
-                       const void* residual_dev, bool fused, void* stream) {
+                       int64_t m_padded, int64_t n, int64_t k, const nvfp4::GemmEpilogue& ep, void* stream) {
   if (!a_qdata_dev || !a_scales_dev || !a_global_dev || !w_qdata_dev || !w_scales_dev || !w_global_dev || !d_dev)
     return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
   if (m_padded < 0 || n <= 0 || k <= 0)
@@ -245,9 +243,14 @@ static int gemm_common(const void* a_qdata_dev, const void* a_scales_dev, const 
   if (!aligned16(a_qdata_dev) || !aligned16(a_scales_dev) || !aligned16(w_qdata_dev) || !aligned16(w_scales_dev) ||
       !aligned16(d_dev) || ((uintptr_t)a_global_dev & 3u) || ((uintptr_t)w_global_dev & 3u))
     return fail(NVFP4_ERR_MISALIGNED, "pointers must be 16-byte aligned (global scales 4-byte)");
-  if (gate_dev && !residual_dev) return fail(NVFP4_ERR_INVALID_ARG, "a gate needs a residual");
-  if (!aligned16(bias_dev) || !aligned16(gate_dev) || !aligned16(residual_dev))
-    return fail(NVFP4_ERR_MISALIGNED, "bias, gate and residual must be 16-byte aligned");
+  if (ep.gate && !ep.res) return fail(NVFP4_ERR_INVALID_ARG, "a gate needs a residual");
+  if (!aligned16(ep.bias) || !aligned16(ep.gate) || !aligned16(ep.res) || !aligned16(ep.gate_out) ||
+      !aligned16(ep.up_out) || ((uintptr_t)ep.amax & 3u))
+    return fail(NVFP4_ERR_MISALIGNED, "epilogue operands must be 16-byte aligned (amax 4-byte)");
+  if (ep.kind == 2 && (!ep.gate_out || !ep.up_out))
+    return fail(NVFP4_ERR_INVALID_ARG, "null gate or up output");
+  if (ep.kind == 2 && (ep.amax_rows < 0 || ep.amax_rows > m_padded))
+    return fail(NVFP4_ERR_INVALID_ARG, "amax_rows=%lld outside [0, m_padded]", (long long)ep.amax_rows);
   const int64_t mt = (m_padded + 255) / 256 * 256, nt = (n + 255) / 256 * 256;
   if (mt * (k / 2) >= kMaxBufferBytes || nt * (k / 2) >= kMaxBufferBytes ||
       (mt + 128) * nvfp4_scale_cols(k) >= kMaxBufferBytes || (nt + 128) * nvfp4_scale_cols(k) >= kMaxBufferBytes ||
@@ -257,11 +260,11 @@ static int gemm_common(const void* a_qdata_dev, const void* a_scales_dev, const 
   int rc = ensure_device(&st);
   if (rc != NVFP4_OK) return rc;
   if (m_padded == 0) return ok();
+  nvfp4::GemmEpilogue ep2 = ep;
+  ep2.silu_table = st->silu_table;
   hipError_t e = nvfp4::launch_gemm((const uint8_t*)a_qdata_dev, (const uint8_t*)a_scales_dev, a_global_dev,
                                     (const uint8_t*)w_qdata_dev, (const uint8_t*)w_scales_dev, w_global_dev,
-                                    (uint16_t*)d_dev, m_padded, n, k, (const uint16_t*)bias_dev,
-                                    (const uint16_t*)gate_dev, (const uint16_t*)residual_dev, fused, st->cu_count,
-                                    (hipStream_t)stream);
+                                    (uint16_t*)d_dev, m_padded, n, k, ep2, st->cu_count, (hipStream_t)stream);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -270,15 +273,38 @@ int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const 
                        const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev, void* d_dev,
                        int64_t m_padded, int64_t n, int64_t k, void* stream) {
   return gemm_common(a_qdata_dev, a_scales_dev, a_global_dev, w_qdata_dev, w_scales_dev, w_global_dev, d_dev,
-                     m_padded, n, k, nullptr, nullptr, nullptr, false, stream);
+                     m_padded, n, k, nvfp4::GemmEpilogue(), stream);
 }
 
 int nvfp4_gemm_bf16out_fused(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
                              const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
                              void* d_dev, int64_t m_padded, int64_t n, int64_t k, const void* bias_dev,
                              const void* gate_dev, const void* residual_dev, void* stream) {
+  nvfp4::GemmEpilogue ep;
+  ep.kind = 1;
+  ep.bias = (const uint16_t*)bias_dev;
+  ep.gate = (const uint16_t*)gate_dev;
+  ep.res = (const uint16_t*)residual_dev;
   return gemm_common(a_qdata_dev, a_scales_dev, a_global_dev, w_qdata_dev, w_scales_dev, w_global_dev, d_dev,
-                     m_padded, n, k, bias_dev, gate_dev, residual_dev, true, stream);
+                     m_padded, n, k, ep, stream);
+}
+
+int nvfp4_gemm_swiglu_pair(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
+                           const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
+                           void* gate_dev, void* up_dev, int64_t m_padded, int64_t n_half, int64_t k,
+                           const void* bias_dev, float* amax_dev, int64_t amax_rows, void* stream) {
+  if (n_half <= 0 || n_half % 8 != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "n_half=%lld must be a positive multiple of 8", (long long)n_half);
+  nvfp4::GemmEpilogue ep;
+  ep.kind = 2;
+  ep.bias = (const uint16_t*)bias_dev;
+  ep.gate_out = (uint16_t*)gate_dev;
+  ep.up_out = (uint16_t*)up_dev;
+  ep.amax = amax_dev;
+  ep.amax_rows = amax_rows;
+  // d is unused by this epilogue; the gate output stands in for the pointer checks
+  return gemm_common(a_qdata_dev, a_scales_dev, a_global_dev, w_qdata_dev, w_scales_dev, w_global_dev, gate_dev,
+                     m_padded, 2 * n_half, k, ep, stream);
 }
 
 int nvfp4_silu_bf16(const void* x_dev, void* y_dev, int64_t count, void* stream) {

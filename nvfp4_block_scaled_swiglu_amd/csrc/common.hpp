@@ -31,6 +31,25 @@ struct ProducerWorkspace {
 };
 static_assert(sizeof(ProducerWorkspace) == 256, "workspace layout");
 
+// What the GEMM does after its K loop (host -> launch_gemm).
+//   kind 0: D = RN_bf16(alpha * acc)
+//   kind 1: D1 = RN_bf16(alpha * acc + bias), D = RN_bf16(res + gate * D1)
+//   kind 2: the SwiGLU pair: D1 as in kind 1 over gate/up rows interleaved in
+//           chunks of 8, written to gate_out / up_out [m_pad, n / 2], and the
+//           maximum of |RN_bf16(silu_bf16(gate) * up)| over rows < amax_rows
+//           folded into *amax with an atomic max
+struct GemmEpilogue {
+  int kind = 0;
+  const uint16_t* bias = nullptr;
+  const uint16_t* gate = nullptr;
+  const uint16_t* res = nullptr;
+  uint16_t* gate_out = nullptr;
+  uint16_t* up_out = nullptr;
+  float* amax = nullptr;
+  int64_t amax_rows = 0;
+  const uint16_t* silu_table = nullptr;
+};
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }

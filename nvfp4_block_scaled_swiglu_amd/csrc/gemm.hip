@@ -95,24 +95,26 @@ struct GemmArgs {
   int big_tiles;                               // tiles [0, big_tiles) run whole; the rest as quarters
   int cgroups;                                 // scale column groups = C / 4
   int ksteps;
-  // fused epilogue (the EPI = 1 kernel): bias and gate bf16 [n] or null, residual
-  // bf16 [m_pad, n] (row stride n, may alias d) or null
-  const uint16_t* bias;
-  const uint16_t* gate;
-  const uint16_t* res;
+  GemmEpilogue ep;  // the epilogue's operands (kind 1 and 2 kernels)
 };
 
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
-// RN_bf16 of a float (ties to even), as a 16-bit pattern
-__device__ __forceinline__ uint32_t bf16_bits_rn(float v) {
+// the value of the other lane of an even/odd lane pair (DPP quad permutation 1,0,3,2)
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+// two floats rounded to bf16 (ties to even), packed: lo in bits 0-15
+__device__ __forceinline__ uint32_t cvt_pk_bf16_rn(float lo, float hi) {
   bf16x2_t c;
-  c[0] = (__bf16)v;
-  c[1] = (__bf16)0.0f;
+  c[0] = (__bf16)lo;
+  c[1] = (__bf16)hi;
   uint32_t r;
   __builtin_memcpy(&r, &c, 4);
-  return r & 0xFFFFu;
+  return r;
 }
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Position of 16-byte chunk c of code row r inside that row's 64 LDS bytes. The
@@ -211,26 +213,11 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// alpha * acc of fragment row I (rows 32 I .. 32 I + 31 of the wave's band) into the
-// wave's fp32 staging rows; I is a compile-time constant so that acc stays in registers.
-template <int I, int FM, int FN, int kRowBytes>
-__device__ __forceinline__ void stage_fragment_f32(const f32x16_t (&acc)[FN][FM], unsigned char* stg, float alpha,
-                                                   int lr, int h) {
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4_t v = {acc[j][I][q * 4 + 0] * alpha, acc[j][I][q * 4 + 1] * alpha, acc[j][I][q * 4 + 2] * alpha,
-                         acc[j][I][q * 4 + 3] * alpha};
-      *(f32x4_t*)(stg + lr * kRowBytes + (j * 32 + q * 8 + h * 4) * 4) = v;
-    }
-  }
-}
-
 // One output tile: the whole K loop and the epilogue for rows [m0, m0 + TM) and
 // columns [n0, n0 + TN), by the workgroup's 4 waves.
-// EPI = 0: D = RN_bf16(alpha * acc). EPI = 1: the fused epilogue, D1 = RN_bf16(alpha
-// * acc + bias[n]) and, with a residual, D = RN_bf16(res + gate[n] * D1).
+// EPI is the GemmEpilogue kind: 0, D = RN_bf16(alpha * acc); 1, D1 = RN_bf16(alpha *
+// acc + bias[n]) and, with a residual, D = RN_bf16(res + gate[n] * D1); 2, the SwiGLU
+// pair (D1 split into gate and up outputs, and the amax of silu(gate) * up).
 template <int FM, int FN, int EPI>
 __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, const int64_t n0, unsigned char* smem) {
   using T = TileShape<FM, FN>;
@@ -477,79 +464,168 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
       asm volatile("" ::: "memory");
     }
   } else {
-    // ---- fused epilogue: bias before the bf16 rounding, then the gated residual ----
-    // Each wave stages alpha * acc in fp32 in its quarter of the LDS, 32 rows at a
-    // time; lane L then owns 8 columns of one row: it adds the bias, rounds to bf16
-    // (D1), combines the residual, and stores 16 bytes.
+    // ---- fused epilogues (kind 1: bias + gated residual; kind 2: SwiGLU pair) ----
+    // The staging is the plain one (bf16 through LDS, 64 rows at a time); the bias
+    // enters the fp32 multiply-add that forms alpha * acc + bias before the one bf16
+    // rounding, and the rest happens on the bf16 row segments of the store phase.
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
     const float alpha = (*a.ga) * (*a.gw);
-    constexpr int kWaveCols = FN * 32, kRowBytes = kWaveCols * 4 + 16;  // padded against bank conflicts
+    constexpr int kWaveCols = FN * 32, kRowBytes = kWaveCols * 2 + 16;  // padded against bank conflicts
     constexpr int kChunksPerRow = kWaveCols / 8, kRowsPerStore = 64 / kChunksPerRow;
-    constexpr int kIters = 32 / kRowsPerStore;
-    static_assert(32 * kRowBytes <= kStages * BigTile::StageBytes / kWaves, "staging fits the wave's LDS share");
+    constexpr int kIts = 64 / kRowsPerStore;            // store iterations per 64-row half
+    constexpr int kBatch = kIts < 8 ? kIts : 8;          // residual rows / silu lookups in flight
+    static_assert(kIts % kBatch == 0, "whole batches");
+    static_assert(64 * kRowBytes <= kStages * BigTile::StageBytes / kWaves, "staging fits the wave's LDS share");
     unsigned char* stg = smem + wave * (kStages * BigTile::StageBytes / kWaves);
     const int64_t wrow0 = m0 + wm * FM * 32, wcol0 = n0 + wn * FN * 32;
     const int ch = lane % kChunksPerRow, rl = lane / kChunksPerRow;
-    const int64_t col = wcol0 + ch * 8;
+    const int64_t col = wcol0 + ch * 8;  // the 8 output columns of this lane in the store phase
     const bool col_ok = col < a.n;
     stage_barrier();  // every wave has finished reading the last K step's stage
-    // (loaded after the barrier so that they do not live through the K loop)
-    float bias8[8], gate8[8];
-    {
-      u32x4_t bv = {0u, 0u, 0u, 0u}, gv = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // gate 1.0
-      if (a.bias && col_ok) bv = *(const u32x4_t*)(a.bias + col);
-      if (a.gate && col_ok) gv = *(const u32x4_t*)(a.gate + col);
+    // bias of the lane's accumulator columns j*32 + q*8 + h*4 .. +3 (loaded after the
+    // barrier so that nothing lives through the K loop); zero without a bias
+    float bq[FN][4][4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bias8[e] = bf16_bits_to_float((bv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        gate8[e] = bf16_bits_to_float((gv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t c = wcol0 + j * 32 + q * 8 + h * 4;
+        u32x2_t bv = {0u, 0u};
+        if (a.ep.bias && c < a.n) bv = *(const u32x2_t*)(a.ep.bias + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bq[j][q][e] = bf16_bits_to_float((bv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
       }
     }
-    static_assert(FM <= 4, "fragment dispatch");
-#pragma nounroll
-    for (int i = 0; i < FM; ++i) {
-      // this fragment's residual rows, in flight while alpha * acc is staged
-      u32x4_t rv[kIters];
+    // kind 1: the gate of the lane's 8 store-phase columns (1.0 without a gate)
+    float gate8[8];
+    {
+      u32x4_t gv = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+      if (EPI == 1 && a.ep.gate && col_ok) gv = *(const u32x4_t*)(a.ep.gate + col);
 #pragma unroll
-      for (int it = 0; it < kIters; ++it) {
-        const int64_t m = wrow0 + i * 32 + it * kRowsPerStore + rl;
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-        rv[it] = (a.res && m < a.m_pad && col_ok) ? *(const u32x4_t*)(a.res + m * a.n + col) : z;
+      for (int e = 0; e < 8; ++e) gate8[e] = bf16_bits_to_float((gv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    }
+    // kind 2: the SwiGLU pair. Even chunks of 8 columns are gate channels j0 .. j0+7,
+    // odd chunks the same up channels (j0 = col / 16 * 8).
+    const bool is_up = (ch & 1) != 0;
+    const int64_t n_half = a.n >> 1, j0 = (col >> 4) << 3;
+    // The amax only needs the largest |y|. The value already in *amax (the caller's
+    // start, raised by tiles done so far) is a lower bound of the final one, and
+    // |y| <= max(|gate|, 0.28125) |up| (1 + 2^-8) bounds an element (|silu| <= |x| for
+    // x > 0 and <= 0.2785 for x < 0; one bf16 rounding of the product): elements
+    // whose bound is below the running maximum cannot raise it and skip the silu
+    // lookup. ymax is the running maximum as an fp32 value of a bf16.
+    float ymax = 0.0f;
+    if (EPI == 2 && a.ep.amax)
+      ymax = __uint_as_float(__hip_atomic_load((const uint32_t*)a.ep.amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int half = 0; half < FM / 2; ++half) {
+      // registers -> LDS: fragments i = 2 half, 2 half + 1 hold rows 64 half .. 64 half + 63
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * half + ii;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float* b = bq[j][q];
+            const u32x2_t v = {cvt_pk_bf16_rn(__builtin_fmaf(acc[j][i][q * 4 + 0], alpha, b[0]),
+                                              __builtin_fmaf(acc[j][i][q * 4 + 1], alpha, b[1])),
+                               cvt_pk_bf16_rn(__builtin_fmaf(acc[j][i][q * 4 + 2], alpha, b[2]),
+                                              __builtin_fmaf(acc[j][i][q * 4 + 3], alpha, b[3]))};
+            const int r = ii * 32 + lr, c = j * 32 + q * 8 + h * 4;
+            *(u32x2_t*)(stg + r * kRowBytes + c * 2) = v;
+          }
+        }
       }
-      // registers -> LDS: fragment i holds rows 32 i .. 32 i + 31 of the wave's band
-      if (i == 0) stage_fragment_f32<0, FM, FN, kRowBytes>(acc, stg, alpha, lr, h);
-      if (FM > 1 && i == 1) stage_fragment_f32<(FM > 1 ? 1 : 0), FM, FN, kRowBytes>(acc, stg, alpha, lr, h);
-      if (FM > 2 && i == 2) stage_fragment_f32<(FM > 2 ? 2 : 0), FM, FN, kRowBytes>(acc, stg, alpha, lr, h);
-      if (FM > 3 && i == 3) stage_fragment_f32<(FM > 3 ? 3 : 0), FM, FN, kRowBytes>(acc, stg, alpha, lr, h);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
       asm volatile("" ::: "memory");
+      // LDS -> global: lane L takes 8 columns of one row, kBatch rows at a time
 #pragma unroll
-      for (int it = 0; it < kIters; ++it) {
-        const int r = it * kRowsPerStore + rl;
-        const int64_t m = wrow0 + i * 32 + r;
-        const f32x4_t x0 = *(const f32x4_t*)(stg + r * kRowBytes + ch * 32);
-        const f32x4_t x1 = *(const f32x4_t*)(stg + r * kRowBytes + ch * 32 + 16);
-        // Each step is one fp32 sum rounded to bf16. gate * D1 (two bf16 values) is
-        // exact in fp32 above 2^-126; the sums round in fp32 before the bf16 rounding,
-        // which can move a result by one bf16 unit only when the exact sum lies within
-        // an fp32 unit of a bf16 midpoint, below the accumulation's own error.
-        uint32_t o[8];
+      for (int b0 = 0; b0 < kIts; b0 += kBatch) {
+        if constexpr (EPI == 1) {
+          u32x4_t rv[kBatch];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t d1 = bf16_bits_rn((e < 4 ? x0[e] : x1[e - 4]) + bias8[e]);
-          if (a.res) {
-            const float rr = bf16_bits_to_float((rv[it][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-            o[e] = bf16_bits_rn(rr + gate8[e] * bf16_bits_to_float(d1));
-          } else {
-            o[e] = d1;
+          for (int t = 0; t < kBatch; ++t) {
+            const int64_t m = wrow0 + half * 64 + (b0 + t) * kRowsPerStore + rl;
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+            rv[t] = (a.ep.res && m < a.m_pad && col_ok) ? *(const u32x4_t*)(a.ep.res + m * a.n + col) : z;
+          }
+#pragma unroll
+          for (int t = 0; t < kBatch; ++t) {
+            const int r = (b0 + t) * kRowsPerStore + rl;
+            const int64_t m = wrow0 + half * 64 + r;
+            u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
+            if (a.ep.res) {
+              // res + gate * D1 in fp32: the product of two bf16 values is exact, so
+              // the fused multiply-add is that sum rounded once
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                const float d0 = bf16_bits_to_float(v[w] & 0xFFFFu), d1 = __uint_as_float(v[w] & 0xFFFF0000u);
+                const float r0 = bf16_bits_to_float(rv[t][w] & 0xFFFFu);
+                const float r1 = __uint_as_float(rv[t][w] & 0xFFFF0000u);
+                v[w] = cvt_pk_bf16_rn(__builtin_fmaf(gate8[2 * w], d0, r0), __builtin_fmaf(gate8[2 * w + 1], d1, r1));
+              }
+            }
+            if (m < a.m_pad && col_ok) *(u32x4_t*)(a.d + m * a.n + col) = v;
+          }
+        } else {
+          // the pair trades halves: the gate lane keeps (gate, up) of channels j0 .. j0+3,
+          // the up lane those of j0+4 .. j0+7
+          uint32_t gpk[kBatch][2], upk[kBatch][2], sil[kBatch][4];
+          bool cand[kBatch][4];
+#pragma unroll
+          for (int t = 0; t < kBatch; ++t) {
+            const int r = (b0 + t) * kRowsPerStore + rl;
+            const int64_t m = wrow0 + half * 64 + r;
+            const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
+            if (m < a.m_pad && col_ok) *(u32x4_t*)((is_up ? a.ep.up_out : a.ep.gate_out) + m * n_half + j0) = v;
+            const uint32_t r0 = pair_swap(is_up ? v[0] : v[2]), r1 = pair_swap(is_up ? v[1] : v[3]);
+            gpk[t][0] = is_up ? r0 : v[0];
+            gpk[t][1] = is_up ? r1 : v[1];
+            upk[t][0] = is_up ? v[2] : r0;
+            upk[t][1] = is_up ? v[3] : r1;
+            const bool ok = m < a.ep.amax_rows && col_ok;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t g16 = (gpk[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+              const float gb = fmaxf(fabsf(bf16_bits_to_float(g16)), 0.28125f);
+              const float ub = fabsf(bf16_bits_to_float((upk[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+              cand[t][e] = ok && gb * ub * (1.0f + 0x1p-7f) + 0x1p-140f >= ymax;  // margin covers fp32 rounding
+              sil[t][e] = cand[t][e] ? a.ep.silu_table[g16] : 0u;  // the lookups of a batch fly together
+            }
+          }
+          // exact y = RN_bf16(silu(gate) * up) of the candidates: the product of two bf16
+          // values is exact in fp32 above 2^-126 (below, the fp64 product is)
+#pragma unroll
+          for (int t = 0; t < kBatch; ++t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (!cand[t][e]) continue;
+              const float sv = bf16_bits_to_float(sil[t][e]);
+              const float uv = bf16_bits_to_float((upk[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+              const float pr = fabsf(sv * uv);
+              uint32_t y = cvt_pk_bf16_rn(pr, 0.0f) & 0x7FFFu;
+              if (pr != 0.0f && pr < 0x1p-126f) y = rn_bf16_from_double(fabs((double)sv * (double)uv)) & 0x7FFFu;
+              ymax = fmaxf(ymax, __uint_as_float(y << 16));
+            }
           }
         }
-        const u32x4_t v = {o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)};
-        if (m < a.m_pad && col_ok) *(u32x4_t*)(a.d + m * a.n + col) = v;
       }
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next fragment overwrites
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next half overwrites
       asm volatile("" ::: "memory");
+    }
+    if constexpr (EPI == 2) {
+      // one atomic max per wave (non-negative fp32 bits order as integers)
+      uint32_t yb = __float_as_uint(ymax);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)yb, off, 64);
+        yb = yb > o ? yb : o;
+      }
+      if (a.ep.amax && lane == 0)
+        __hip_atomic_fetch_max((uint32_t*)a.ep.amax, yb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -594,16 +670,15 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
 // ---- host side -----------------------------------------------------------------------------
 
 size_t gemm_smem_bytes() { return (size_t)kStages * BigTile::StageBytes; }
-const void* gemm_kernel_ptr(bool fused) { return fused ? (const void*)gemm_kernel<1> : (const void*)gemm_kernel<0>; }
+const void* gemm_kernel_ptr(int kind) {
+  return kind == 2 ? (const void*)gemm_kernel<2> : kind == 1 ? (const void*)gemm_kernel<1> : (const void*)gemm_kernel<0>;
+}
 
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
-                       const uint16_t* bias, const uint16_t* gate, const uint16_t* res, bool fused, int cu_count,
-                       hipStream_t stream) {
+                       const GemmEpilogue& ep, int cu_count, hipStream_t stream) {
   GemmArgs args;
-  args.bias = bias;
-  args.gate = gate;
-  args.res = res;
+  args.ep = ep;
   args.aq = aq;
   args.as = as;
   args.ga = ga;
@@ -630,7 +705,9 @@ hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, co
   const int tail = cu_count > 0 ? ntiles % cu_count : 0;
   args.big_tiles = (tail > 0 && ntiles > cu_count && 4 * tail <= cu_count) ? ntiles - tail : ntiles;
   const int grid = args.big_tiles + 4 * (ntiles - args.big_tiles);
-  if (fused)
+  if (ep.kind == 2)
+    gemm_kernel<2><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);
+  else if (ep.kind == 1)
     gemm_kernel<1><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);
   else
     gemm_kernel<0><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);

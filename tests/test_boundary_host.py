@@ -175,6 +175,23 @@ def test_fused_gemm_validation(kw, status):
     assert call_fused(**kw) == status
 
 
+def call_pair(**kw):
+    args = dict(aq=FAKE, as_=FAKE, ga=FAKE, wq=FAKE, ws=FAKE, gw=FAKE, g=FAKE, u=FAKE, m=16, nh=16, k=64, b=None,
+                am=None, ar=16)
+    args.update(kw)
+    return nv.lib().nvfp4_gemm_swiglu_pair(args["aq"], args["as_"], args["ga"], args["wq"], args["ws"], args["gw"],
+                                           args["g"], args["u"], args["m"], args["nh"], args["k"], args["b"],
+                                           args["am"], args["ar"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nh=12), 2), (dict(nh=0), 2), (dict(u=None), 1), (dict(g=None), 1), (dict(am=FAKE + 2), 3),
+    (dict(ar=17), 1), (dict(ar=-1), 1), (dict(u=FAKE + 8), 3), (dict(b=FAKE + 4), 3),
+])
+def test_swiglu_pair_validation(kw, status):
+    assert call_pair(**kw) == status
+
+
 def test_silu_validation():
     assert nv.lib().nvfp4_silu_bf16(None, None, -1, None) == 1
     assert nv.lib().nvfp4_silu_bf16(None, FAKE, 4, None) == 1

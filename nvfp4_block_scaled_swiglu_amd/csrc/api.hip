@@ -26,7 +26,7 @@ hipError_t launch_producer(int mode, const uint16_t* x, int64_t ldx, const uint1
                            const uint16_t* mod_scale, const uint16_t* mod_shift, int64_t m, int64_t k,
                            uint8_t* qdata, uint8_t* scales, float* gout, const float* amax_in, void* workspace,
                            const uint16_t* silu_table, int max_blocks, hipStream_t stream);
-size_t gemm_smem_bytes();
+size_t gemm_smem_bytes(int kind);
 const void* gemm_kernel_ptr(int kind);
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
@@ -108,7 +108,7 @@ int ensure_device(DeviceState** out) {
   }
   for (int kind = 0; kind < 3; ++kind) {
     e = hipFuncSetAttribute(nvfp4::gemm_kernel_ptr(kind), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)nvfp4::gemm_smem_bytes());
+                            (int)nvfp4::gemm_smem_bytes(kind));
     if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "gemm LDS attribute: %s", hipGetErrorString(e));
   }
 

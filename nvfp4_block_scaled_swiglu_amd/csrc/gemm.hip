@@ -56,6 +56,7 @@ constexpr int kStages = 3;                       // LDS stages (loads run two K 
 constexpr int kBandM = 8;                        // M-tiles per traversal band
 constexpr int kTileBig = 256;                    // full tile edge
 constexpr int kTileQuarter = 128;                // tail tile edge
+constexpr int kCand = 1024;                      // SwiGLU-pair candidate list entries per wave (LDS)
 
 template <int FM_, int FN_>
 struct TileShape {
@@ -515,6 +516,41 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
     // whose bound is below the running maximum cannot raise it and skip the silu
     // lookup. ymax is the running maximum as an fp32 value of a bf16.
     float ymax = 0.0f;
+    // Candidates are queued per wave in LDS (past the pipeline stages) as
+    // gate | up << 16 and resolved together - their silu lookups in one batch - when
+    // the list fills and at the end of the tile. The count is wave-uniform.
+    uint32_t* clist = (uint32_t*)(smem + kStages * BigTile::StageBytes) + wave * kCand;
+    int ccount = 0;
+    auto flush = [&]() __attribute__((always_inline)) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's list writes are done
+      asm volatile("" ::: "memory");
+      // rounds of 4 entries per lane, their silu lookups in flight together
+#pragma nounroll
+      for (int base = 0; base < ccount; base += 256) {
+        uint32_t ent[4], sil[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ent[r] = (base + r * 64 + lane < ccount) ? clist[base + r * 64 + lane] : 0u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sil[r] = (base + r * 64 + lane < ccount) ? a.ep.silu_table[ent[r] & 0xFFFFu] : 0u;
+        // exact y = RN_bf16(silu(gate) * up): the product of two bf16 values is exact
+        // in fp32 above 2^-126 (below, the fp64 product is)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (base + r * 64 + lane < ccount) {
+            const float sv = bf16_bits_to_float(sil[r]), uv = bf16_bits_to_float(ent[r] >> 16);
+            const float pr = fabsf(sv * uv);
+            uint32_t y = cvt_pk_bf16_rn(pr, 0.0f) & 0x7FFFu;
+            if (pr != 0.0f && pr < 0x1p-126f) y = rn_bf16_from_double(fabs((double)sv * (double)uv)) & 0x7FFFu;
+            ymax = fmaxf(ymax, __uint_as_float(y << 16));
+          }
+        }
+      }
+      ccount = 0;
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the list reads are done before it is refilled
+      asm volatile("" ::: "memory");
+    };
     if (EPI == 2 && a.ep.amax)
       ymax = __uint_as_float(__hip_atomic_load((const uint32_t*)a.ep.amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 #pragma unroll
@@ -572,42 +608,34 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
         } else {
           // the pair trades halves: the gate lane keeps (gate, up) of channels j0 .. j0+3,
           // the up lane those of j0+4 .. j0+7
-          uint32_t gpk[kBatch][2], upk[kBatch][2], sil[kBatch][4];
-          bool cand[kBatch][4];
-#pragma unroll
+#pragma nounroll
           for (int t = 0; t < kBatch; ++t) {
+            if (ccount + 256 > kCand) flush();  // room for this row's 4 x 64 candidates
             const int r = (b0 + t) * kRowsPerStore + rl;
             const int64_t m = wrow0 + half * 64 + r;
             const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
             if (m < a.m_pad && col_ok) *(u32x4_t*)((is_up ? a.ep.up_out : a.ep.gate_out) + m * n_half + j0) = v;
             const uint32_t r0 = pair_swap(is_up ? v[0] : v[2]), r1 = pair_swap(is_up ? v[1] : v[3]);
-            gpk[t][0] = is_up ? r0 : v[0];
-            gpk[t][1] = is_up ? r1 : v[1];
-            upk[t][0] = is_up ? v[2] : r0;
-            upk[t][1] = is_up ? v[3] : r1;
+            const uint32_t gpk[2] = {is_up ? r0 : v[0], is_up ? r1 : v[1]};
+            const uint32_t upk[2] = {is_up ? v[2] : r0, is_up ? v[3] : r1};
             const bool ok = m < a.ep.amax_rows && col_ok;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const uint32_t g16 = (gpk[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+              const uint32_t g16 = (gpk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+              const uint32_t u16 = (upk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
               const float gb = fmaxf(fabsf(bf16_bits_to_float(g16)), 0.28125f);
-              const float ub = fabsf(bf16_bits_to_float((upk[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
-              cand[t][e] = ok && gb * ub * (1.0f + 0x1p-7f) + 0x1p-140f >= ymax;  // margin covers fp32 rounding
-              sil[t][e] = cand[t][e] ? a.ep.silu_table[g16] : 0u;  // the lookups of a batch fly together
-            }
-          }
-          // exact y = RN_bf16(silu(gate) * up) of the candidates: the product of two bf16
-          // values is exact in fp32 above 2^-126 (below, the fp64 product is)
-#pragma unroll
-          for (int t = 0; t < kBatch; ++t) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (!cand[t][e]) continue;
-              const float sv = bf16_bits_to_float(sil[t][e]);
-              const float uv = bf16_bits_to_float((upk[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-              const float pr = fabsf(sv * uv);
-              uint32_t y = cvt_pk_bf16_rn(pr, 0.0f) & 0x7FFFu;
-              if (pr != 0.0f && pr < 0x1p-126f) y = rn_bf16_from_double(fabs((double)sv * (double)uv)) & 0x7FFFu;
-              ymax = fmaxf(ymax, __uint_as_float(y << 16));
+              const float ub = fabsf(bf16_bits_to_float(u16));
+              const bool cand = ok && gb * ub * (1.0f + 0x1p-7f) + 0x1p-140f >= ymax;  // margin covers fp32 rounding
+              const uint64_t mask = __ballot(cand);
+              const int nc = __builtin_amdgcn_readfirstlane(__popcll(mask));
+              if (nc) {
+                if (cand) {
+                  const int off = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                  clist[ccount + off] = g16 | (u16 << 16);
+                }
+                ccount += nc;
+              }
             }
           }
         }
@@ -617,6 +645,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
       asm volatile("" ::: "memory");
     }
     if constexpr (EPI == 2) {
+      if (ccount) flush();
       // one atomic max per wave (non-negative fp32 bits order as integers)
       uint32_t yb = __float_as_uint(ymax);
 #pragma unroll
@@ -669,7 +698,9 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
 
 // ---- host side -----------------------------------------------------------------------------
 
-size_t gemm_smem_bytes() { return (size_t)kStages * BigTile::StageBytes; }
+size_t gemm_smem_bytes(int kind) {
+  return (size_t)kStages * BigTile::StageBytes + (kind == 2 ? (size_t)kWaves * kCand * 4 : 0);
+}
 const void* gemm_kernel_ptr(int kind) {
   return kind == 2 ? (const void*)gemm_kernel<2> : kind == 1 ? (const void*)gemm_kernel<1> : (const void*)gemm_kernel<0>;
 }
@@ -706,11 +737,11 @@ hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, co
   args.big_tiles = (tail > 0 && ntiles > cu_count && 4 * tail <= cu_count) ? ntiles - tail : ntiles;
   const int grid = args.big_tiles + 4 * (ntiles - args.big_tiles);
   if (ep.kind == 2)
-    gemm_kernel<2><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);
+    gemm_kernel<2><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(2), stream>>>(args);
   else if (ep.kind == 1)
-    gemm_kernel<1><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);
+    gemm_kernel<1><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(1), stream>>>(args);
   else
-    gemm_kernel<0><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(), stream>>>(args);
+    gemm_kernel<0><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(0), stream>>>(args);
   return hipGetLastError();
 }
 

@@ -16,6 +16,12 @@
 // The exact fp16 operands feed v_mfma_f32_32x32x16_f16 with fp32 accumulation;
 // the epilogue multiplies by g_a * g_w in fp32 and rounds to bf16 once.
 //
+// Epilogues (GemmEpilogue in common.hpp, one kernel instantiation each): the plain
+// store; kind 1 adds a bf16 bias inside the fp32 multiply-add before the rounding
+// and then a gated residual, res + gate[n] * D1; kind 2 is the SwiGLU pair of an
+// FC1 whose gate and up rows are interleaved in chunks of 8 - it writes gate and up
+// to separate tensors and folds max |silu(gate) * up| into the caller's amax.
+//
 // Tiling: a 256 x 256 output tile per workgroup of 4 waves (2 x 2), one wave per
 // SIMD, each wave 128 x 128 (4 x 4 MFMA tiles of 32 x 32, accumulators in the 256
 // AGPRs). A square wave tile needs the fewest dequantized fragments per MFMA: one
@@ -98,8 +104,6 @@ struct GemmArgs {
   int ksteps;
   GemmEpilogue ep;  // the epilogue's operands (kind 1 and 2 kernels)
 };
-
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 // the value of the other lane of an even/odd lane pair (DPP quad permutation 1,0,3,2)
 __device__ __forceinline__ uint32_t pair_swap(uint32_t v) {

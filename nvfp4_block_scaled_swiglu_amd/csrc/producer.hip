@@ -1,4 +1,4 @@
-// producer.hip - fused SwiGLU -> NVFP4 producer for gfx950 (one cooperative launch).
+// producer.hip - the NVFP4 producer for gfx950: SwiGLU, plain and modulated inputs.
 //
 // Operation (component-2 NSYS summary: the pre-fusion chain silu -> multiply ->
 // absmax_partial -> scale_finalize -> block_scale_zero -> activation_pack, whose
@@ -6,8 +6,10 @@
 // synchronisation design; "FC2 NVFP4 Scheduling Results", "Canonical Operation",
 // for the formats and the 37,810 -> 37,824 row padding):
 //
-//   y       = RN_bf16(silu_bf16(gate) * up)          (plain variant: y = x)
-//   amax    = max |y| over the logical rows
+//   y       = RN_bf16(silu_bf16(gate) * up)          (SwiGLU mode)
+//           = x                                      (plain mode)
+//           = RN_bf16(fma_fp32(x, RN_fp32(1 + scale[k]), shift[k]))   (modulate mode)
+//   amax    = max |y| over the logical rows, or the caller's value (GIVEN)
 //   g       = amax / 2688 rounded up to fp32          (2688 = 6 * 448)
 //   S[r,b]  = smallest UE4M3 byte with v(S) * 6 * g >= max_{16} |y|
 //   code    = E2M1 nearest to |y| / (v(S) g), ties to even, sign of y
@@ -23,7 +25,9 @@
 // (so the rows read last in pass 1, still in the memory-side cache, are read first),
 // recomputes y, and stores QDATA rows (32 lanes store one full 256-byte row segment)
 // and each scale byte at its place in its 512-byte tile. Pass 2 has no workgroup
-// barrier, so the 16 waves drift apart and hide each other's load latency.
+// barrier, so the 16 waves drift apart and hide each other's load latency. With
+// GIVEN (amax from the caller) pass 1 and the barrier are compiled out and the
+// launch is an ordinary one: every input byte is read once.
 //
 // Exactness: every rounding decision equals the exact one.
 //  - y: a product of two bf16 values is exact in fp32 when it is >= 2^-126; a block

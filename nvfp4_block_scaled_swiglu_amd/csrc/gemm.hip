@@ -44,7 +44,10 @@
 // Traversal: tiles are numbered m-band-major in bands of 8 M-tiles, and workgroup
 // ids (dispatched round-robin over the 8 XCDs) are remapped so that each XCD owns
 // one contiguous range of tiles; its 32 concurrent workgroups then share A row
-// bands and W panels in that XCD's L2.
+// bands and W panels in that XCD's L2. The plain kernel runs the whole tiles with
+// one persistent workgroup per CU that walks its XCD's range in the same order; the
+// first two K steps of its next tile are loaded while the current tile's epilogue
+// runs, staged through an LDS area of its own.
 #include "common.hpp"
 
 namespace nvfp4 {
@@ -100,6 +103,7 @@ struct GemmArgs {
   int a_qbytes, w_qbytes, a_sbytes, w_sbytes;  // buffer sizes for the range checks
   int tiles_m, tiles_n;                        // 256 x 256 tiles
   int big_tiles;                               // tiles [0, big_tiles) run whole; the rest as quarters
+  int persist_wgs;                             // > 0: workgroups [0, persist_wgs) loop over the whole tiles
   int cgroups;                                 // scale column groups = C / 4
   int ksteps;
   GemmEpilogue ep;  // the epilogue's operands (kind 1 and 2 kernels)
@@ -223,8 +227,23 @@ __device__ __forceinline__ void stage_barrier() {
 // EPI is the GemmEpilogue kind: 0, D = RN_bf16(alpha * acc); 1, D1 = RN_bf16(alpha *
 // acc + bias[n]) and, with a residual, D = RN_bf16(res + gate[n] * D1); 2, the SwiGLU
 // pair (D1 split into gate and up outputs, and the amax of silu(gate) * up).
-template <int FM, int FN, int EPI>
-__device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, const int64_t n0, unsigned char* smem) {
+// The origin of whole tile t: tiles are numbered m-band-major (bands of kBandM M-tiles,
+// M first within a band).
+__device__ __forceinline__ void tile_origin(const GemmArgs& a, int t, int64_t& m0, int64_t& n0) {
+  const int band = t / (kBandM * a.tiles_n);
+  const int in_band = t - band * kBandM * a.tiles_n;
+  const int band_m = (a.tiles_m - band * kBandM) < kBandM ? (a.tiles_m - band * kBandM) : kBandM;
+  m0 = (int64_t)(band * kBandM + in_band % band_m) * kTileBig;
+  n0 = (int64_t)(in_band / band_m) * kTileBig;
+}
+
+// PERSIST (plain epilogue, whole tiles): after tile (m0, n0) the workgroup goes on with
+// tiles t_next, t_next + t_stride, ... < t_end. The first two K steps of the next
+// tile are loaded while the current tile's epilogue runs; that epilogue stages
+// through its own LDS area, past the pipeline stages.
+template <int FM, int FN, int EPI, bool PERSIST = false>
+__device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t n0, unsigned char* smem,
+                                         int t_next = 0, int t_stride = 0, int t_end = 0) {
   using T = TileShape<FM, FN>;
   constexpr int kStageBytes = T::StageBytes, kCodesA = T::CodesA, kCodesW = T::CodesW, kScaleA = T::ScaleA;
   constexpr int kLoads = T::Loads;
@@ -311,12 +330,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
   };
 
   f32x16_t acc[FN][FM];
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
   // Software pipeline. K step ks lives in LDS stage ks % 3, loaded two K steps
   // ahead; the loads of step ks + 2 are spread over the first K16 steps of step ks
@@ -330,16 +343,31 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
   // at kk = 7. The body is instantiated without branches: the last two K steps are
   // peeled.
   const int nks = a.ksteps;
+  // g_a * g_w, read before any load of the pipeline so that waiting for it never
+  // waits for those (the persistent epilogue overlaps the next tile's first loads)
+  float alpha_p = 0.0f;
+  if constexpr (PERSIST) alpha_p = (*a.ga) * (*a.gw);
+  // the loads of the first two K steps of the current tile
+  auto prologue = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int idx = 0; idx < kLoads; ++idx) issue_one(0, 0, idx);
-  if (nks > 1) {
+    for (int idx = 0; idx < kLoads; ++idx) issue_one(0, 0, idx);
+    if (nks > 1) {
 #pragma unroll
-    for (int idx = 0; idx < kLoads; ++idx) issue_one(1, 1, idx);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);  // vmcnt(kLoads): step 0 has landed
-  } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  }
+      for (int idx = 0; idx < kLoads; ++idx) issue_one(1, 1, idx);
+    }
+  };
+  prologue();
+  if (nks > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);  // vmcnt(kLoads): step 0 has landed
+  else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+
+  for (;;) {  // one pass without PERSIST
   stage_barrier();
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
   u32x4_t ca[2][FM], cw[2][FN];
   uint32_t sa[FM], sw[FN], nsa[FM], nsw[FN];
@@ -416,7 +444,53 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
   }
   kstep(ks, stage, false, false);
 
-  if constexpr (EPI == 0) {
+  // the epilogue's tile; PERSIST moves (m0, n0) on to the next tile and starts its loads
+  const int64_t em0 = m0, en0 = n0;
+  bool more = false;
+  if constexpr (PERSIST) {
+    more = t_next < t_end;
+    stage_barrier();  // every wave has finished reading the last K step's stage
+    if (more) {
+      tile_origin(a, t_next, m0, n0);
+      prologue();
+    }
+  }
+  if constexpr (EPI == 0 && PERSIST) {
+    // ---- epilogue: D[m, n] = RN_bf16(alpha * acc), staged 32 rows at a time in the
+    // wave's area past the stages (the next tile's loads are landing in the stages) ----
+    const float alpha = alpha_p;
+    constexpr int kWaveCols = FN * 32, kRowBytes = kWaveCols * 2 + 16;  // padded against bank conflicts
+    constexpr int kChunksPerRow = kWaveCols / 8, kRowsPerStore = 64 / kChunksPerRow;
+    unsigned char* stg = smem + kStages * BigTile::StageBytes + wave * (32 * kRowBytes);
+    const int64_t wrow0 = em0 + wm * FM * 32, wcol0 = en0 + wn * FN * 32;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+          const u32x2_t v = {cvt_pk_bf16_rn(acc[j][i][q * 4 + 0] * alpha, acc[j][i][q * 4 + 1] * alpha),
+                             cvt_pk_bf16_rn(acc[j][i][q * 4 + 2] * alpha, acc[j][i][q * 4 + 3] * alpha)};
+          *(u32x2_t*)(stg + lr * kRowBytes + (j * 32 + q * 8 + h * 4) * 2) = v;
+        }
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+      asm volatile("" ::: "memory");
+      // LDS -> global: lane L takes 8 columns of one row
+#pragma unroll
+      for (int it = 0; it < 32 / kRowsPerStore; ++it) {
+        const int r = it * kRowsPerStore + lane / kChunksPerRow, ch = lane % kChunksPerRow;
+        const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
+        const int64_t m = wrow0 + i * 32 + r, n = wcol0 + ch * 8;
+        if (m < a.m_pad && n < a.n) *(u32x4_t*)(a.d + m * a.n + n) = v;
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next fragment overwrites
+      asm volatile("" ::: "memory");
+    }
+  } else if constexpr (EPI == 0) {
     // ---- epilogue: D[m, n] = RN_bf16(alpha * acc), alpha = g_a * g_w ----
     // Each wave stages its tile in its own quarter of the (now idle) LDS, 64 rows at a
     // time, then stores whole row segments: a store instruction writes 4 rows x 256 B
@@ -426,7 +500,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
     constexpr int kChunksPerRow = kWaveCols / 8, kRowsPerStore = 64 / kChunksPerRow;
     static_assert(64 * kRowBytes <= kStages * BigTile::StageBytes / kWaves, "staging fits the wave's LDS share");
     unsigned char* stg = smem + wave * (kStages * BigTile::StageBytes / kWaves);
-    const int64_t wrow0 = m0 + wm * FM * 32, wcol0 = n0 + wn * FN * 32;
+    const int64_t wrow0 = em0 + wm * FM * 32, wcol0 = en0 + wn * FN * 32;
     stage_barrier();  // every wave has finished reading the last K step's stage
   #pragma unroll
     for (int half = 0; half < FM / 2; ++half) {
@@ -482,7 +556,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
     static_assert(kIts % kBatch == 0, "whole batches");
     static_assert(64 * kRowBytes <= kStages * BigTile::StageBytes / kWaves, "staging fits the wave's LDS share");
     unsigned char* stg = smem + wave * (kStages * BigTile::StageBytes / kWaves);
-    const int64_t wrow0 = m0 + wm * FM * 32, wcol0 = n0 + wn * FN * 32;
+    const int64_t wrow0 = em0 + wm * FM * 32, wcol0 = en0 + wn * FN * 32;
     const int ch = lane % kChunksPerRow, rl = lane / kChunksPerRow;
     const int64_t col = wcol0 + ch * 8;  // the 8 output columns of this lane in the store phase
     const bool col_ok = col < a.n;
@@ -661,6 +735,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const int64_t m0, co
         __hip_atomic_fetch_max((uint32_t*)a.ep.amax, yb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  if (!more) break;
+  t_next += t_stride;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile's first steps have landed
+  }  // tiles
 }
 
 template <int EPI>
@@ -672,8 +750,29 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
   // contiguous range of tiles. Workgroups past that run the remaining tiles as
   // 128 x 128 quarters; they are dispatched last and fill the CUs that free up.
   const int b = blockIdx.x;
+  if constexpr (EPI == 0) {
+    if (b < a.persist_wgs) {
+      // persistent: workgroup b (on XCD b % 8) walks its XCD's tile range with a stride
+      // of the XCD's workgroup count, the order in which the non-persistent grid runs it
+      const int nb = a.big_tiles, slots = a.persist_wgs / 8;
+      const int per = nb / 8, rem = nb % 8;
+      const int xcd = b % 8, slot = b / 8;
+      const int t0 = xcd * per + (xcd < rem ? xcd : rem);
+      const int t_end = t0 + per + (xcd < rem ? 1 : 0);
+      const int t = t0 + slot;
+      if (t >= t_end) return;
+      int64_t m0, n0;
+      tile_origin(a, t, m0, n0);
+      run_tile<4, 4, 0, true>(a, m0, n0, smem, t + slots, slots, t_end);
+      return;
+    }
+  }
   int t, quarter = -1;
-  if (b < a.big_tiles) {
+  if (a.persist_wgs > 0 && b >= a.persist_wgs) {
+    const int q = b - a.persist_wgs;
+    t = a.big_tiles + q / 4;
+    quarter = q % 4;
+  } else if (b < a.big_tiles) {
     const int nb = a.big_tiles;
     const int per = nb / 8, rem = nb % 8;
     const int xcd = b % 8, idx = b / 8;
@@ -685,12 +784,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
   }
   const int ntiles = a.tiles_m * a.tiles_n;
   if (t >= ntiles) return;
-  const int band = t / (kBandM * a.tiles_n);
-  const int in_band = t - band * kBandM * a.tiles_n;
-  const int band_m = (a.tiles_m - band * kBandM) < kBandM ? (a.tiles_m - band * kBandM) : kBandM;
-  const int tm = band * kBandM + in_band % band_m;
-  const int tn = in_band / band_m;
-  const int64_t m0 = (int64_t)tm * kTileBig, n0 = (int64_t)tn * kTileBig;
+  int64_t m0, n0;
+  tile_origin(a, t, m0, n0);
   if (quarter < 0) {
     run_tile<4, 4, EPI>(a, m0, n0, smem);
   } else {
@@ -702,8 +797,11 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
 
 // ---- host side -----------------------------------------------------------------------------
 
+// the plain kernel's persistent workgroups stage their epilogue past the pipeline stages
+constexpr size_t kPersistStagingBytes = (size_t)kWaves * 32 * (BigTile::TN / WAVES_N * 2 + 16);
 size_t gemm_smem_bytes(int kind) {
-  return (size_t)kStages * BigTile::StageBytes + (kind == 2 ? (size_t)kWaves * kCand * 4 : 0);
+  return (size_t)kStages * BigTile::StageBytes +
+         (kind == 2 ? (size_t)kWaves * kCand * 4 : kind == 0 ? kPersistStagingBytes : 0);
 }
 const void* gemm_kernel_ptr(int kind) {
   return kind == 2 ? (const void*)gemm_kernel<2> : kind == 1 ? (const void*)gemm_kernel<1> : (const void*)gemm_kernel<0>;
@@ -739,7 +837,12 @@ hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, co
   // at most a quarter of the CUs' worth, its tiles run as 128 x 128 quarters.
   const int tail = cu_count > 0 ? ntiles % cu_count : 0;
   args.big_tiles = (tail > 0 && ntiles > cu_count && 4 * tail <= cu_count) ? ntiles - tail : ntiles;
-  const int grid = args.big_tiles + 4 * (ntiles - args.big_tiles);
+  // The plain kernel runs the whole tiles with persistent workgroups, a multiple of
+  // 8 of them (each XCD the same count), one per CU, when there are more tiles than
+  // that: the next tile's first loads then overlap the current tile's epilogue.
+  const int persist = cu_count - cu_count % 8;
+  args.persist_wgs = (ep.kind == 0 && persist >= 8 && args.big_tiles > persist) ? persist : 0;
+  const int grid = (args.persist_wgs > 0 ? args.persist_wgs : args.big_tiles) + 4 * (ntiles - args.big_tiles);
   if (ep.kind == 2)
     gemm_kernel<2><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(2), stream>>>(args);
   else if (ep.kind == 1)

@@ -82,6 +82,28 @@ def test_tail_quarter_tiles(gpu):
     run_path(w, gpu, None, 0)
 
 
+def test_persistent_tiles(gpu):
+    """The plain GEMM runs its whole tiles with persistent workgroups (a multiple of 8
+    of them, one per CU) when there are more whole tiles than that; each walks about
+    three tiles here, loading the next tile while the last one's epilogue runs, and the
+    leftover tiles run as quarters. M and N tails and a half K step; every output
+    element is compared."""
+    import torch
+    cu = torch.cuda.get_device_properties(gpu).multi_processor_count
+    persist = cu - cu % 8
+    tiles_n = 17
+    tiles_m = (3 * cu + cu // 16 + tiles_n - 1) // tiles_n
+    tiles = tiles_m * tiles_n
+    tail = tiles % cu
+    big = tiles - tail if (0 < tail and 4 * tail <= cu) else tiles
+    assert big > persist and big < tiles, (cu, tiles, tail)
+    m = tiles_m * 256 - 96
+    n = tiles_n * 256 - 16
+    w = synth.Workload(f"persistent_{m}x{n}", m=m, n=n, k=192, seed=23, swiglu=True)
+    _say(f"[persistent] {cu} CUs: {tiles} tiles, {big} whole over {persist} workgroups, {tiles - big} as quarters")
+    run_path(w, gpu, None, 0)
+
+
 def test_subnormal_scales(gpu):
     """Operands whose block scales are UE4M3 subnormals (E = 0) on both sides."""
     import torch

@@ -84,6 +84,75 @@ def measured_gemm_traffic():
         return None
 
 
+def percentiles(xs) -> dict:
+    """p10 / p50 / p90 of per-launch durations (ms), nearest-rank."""
+    v = sorted(xs)
+    pick = lambda q: v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {"p10": round(pick(0.1), 4), "p50": round(pick(0.5), 4), "p90": round(pick(0.9), 4)}
+
+
+def ceilings(dev, stream) -> dict:
+    """Context for the two rooflines, measured on this device: the dense fp16 MFMA rate
+    with nothing but MFMAs in flight (one wave per SIMD on every CU) and the shader
+    clock during it, and a plain device-to-device copy's HBM rate (read + write)."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 16384
+    nv.nvfp4_mfma_ceiling(cu, 256)
+    best, clocks = 0.0, []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        out = nv.nvfp4_mfma_ceiling(cu, iters)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = max(best, cu * 4 * iters * 4 * 2.0 * 32 * 32 * 16 / (ms * 1e-3) / 1e12)
+        o = out.cpu().double()
+        clocks += (o[:, 0] / (o[:, 1] / 100e6) / 1e9).tolist()
+    clocks.sort()
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+    return {"mfma_f16_tflops": round(best, 1), "mfma_clock_ghz_p50": round(clocks[len(clocks) // 2], 3),
+            "hbm_copy_gbs": round(copy_gbs, 1),
+            "note": "MFMA-only kernel (4 independent v_mfma_f32_32x32x16_f16 chains per wave, one wave per "
+                    "SIMD), clock from s_memtime over s_memrealtime; copy of 1 GiB, read + write bytes"}
+
+
+def cold_times(run_gemm, run_producer, dev, stream, reps: int) -> dict:
+    """Per-launch times with the caches cold: 1 GiB of scratch is rewritten before each
+    timed launch, which evicts the 4 MB L2s and the 256 MB MALL."""
+    import torch
+    scratch = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    out = {}
+    for name, fn in (("gemm", run_gemm), ("producer", run_producer)):
+        ts = []
+        for i in range(reps):
+            scratch.fill_(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        out[name + "_ms"] = percentiles(ts)
+    del scratch
+    out["reps"] = reps
+    return out
+
+
 def cpu_baseline(w, threads: int) -> dict:
     """The CPU oracle timed on a bounded sample of the same workload (about 10-15 s
     of CPU work on 16 cores): the exact GEMM on 16,384 evenly spaced rows (all N
@@ -496,6 +565,16 @@ def main() -> int:
 
     prod_ms = [e[0].elapsed_time(e[1]) for e in evs]
     gemm_ms = [e[1].elapsed_time(e[2]) for e in evs]
+
+    def producer_once():
+        if w.swiglu:
+            nv.nvfp4_quantize_swiglu(x, u, out=a)
+        else:
+            nv.nvfp4_quantize(x, out=a)
+
+    cold = cold_times(lambda: nv.nvfp4_gemm_bf16out(a, wq, out=d), producer_once, dev, stream,
+                      min(args.steps, 10))
+    ceil = ceilings(dev, stream)
     import statistics
     t_prod = statistics.fmean(prod_ms)
     t_gemm = statistics.fmean(gemm_ms)
@@ -570,6 +649,10 @@ def main() -> int:
         },
         "producer_ms": round(t_prod, 4),
         "gemm_ms": round(t_gemm, 4),
+        "warm_ms": {"gemm": percentiles(gemm_ms), "producer": percentiles(prod_ms)},
+        "cold_ms": cold,
+        "ceilings": dict(ceil, gemm_frac_of_mfma_ceiling=round(tflops / ceil["mfma_f16_tflops"], 4),
+                         producer_frac_of_copy=round(prod_gbs / ceil["hbm_copy_gbs"], 4)),
         "step_tflops": round(w.gemm_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "weight_quantize_ms": round(ev_w0.elapsed_time(ev_w1), 4),
         "gemm_distinct_bytes": gemm_bytes(w.m, w.n, w.k),

@@ -253,6 +253,20 @@ int nvfp4_gemm_swiglu_pair(const void* a_qdata_dev, const void* a_scales_dev, co
  * inputs). x_dev, y_dev: 2-byte aligned device arrays of count elements. */
 int nvfp4_silu_bf16(const void* x_dev, void* y_dev, int64_t count, void* stream);
 
+/* ---- measurement aid ---------------------------------------------------------------------- */
+
+/* Not a step of the method: the dense fp16 matrix-core rate the device sustains and
+ * its shader clock meanwhile, the ceiling beside which the GEMM's rate is read.
+ * Launches `workgroups` workgroups of 4 waves; each wave issues iters x 4 independent
+ * v_mfma_f32_32x32x16_f16 (32,768 FLOP each) and nothing else in its loop. For wave w
+ * of workgroup b, out[(4 b + w) * 2] receives its shader-clock cycles and
+ * out[(4 b + w) * 2 + 1] its 100 MHz real-time ticks over the loop (uint64 each).
+ * workgroups in [1, 65536]; iters in [1, 2^24]; out_dev: 8-byte aligned device memory
+ * of at least nvfp4_mfma_ceiling_out_bytes(workgroups) bytes, owned by the caller.
+ * Time the call with events on `stream` for the rate. */
+int64_t nvfp4_mfma_ceiling_out_bytes(int64_t workgroups);
+int nvfp4_mfma_ceiling(int64_t workgroups, int64_t iters, void* out_dev, int64_t out_bytes, void* stream);
+
 /* ---- diagnostics -------------------------------------------------------------------------- */
 
 /* Static text for a status code. */

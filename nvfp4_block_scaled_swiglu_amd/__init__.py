@@ -58,6 +58,8 @@ SIGNATURES = {
     "nvfp4_gemm_bf16out_fused": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_gemm_swiglu_pair": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P]),
     "nvfp4_silu_bf16": (_INT, [_P, _P, _I64, _P]),
+    "nvfp4_mfma_ceiling_out_bytes": (_I64, [_I64]),
+    "nvfp4_mfma_ceiling": (_INT, [_I64, _I64, _P, _I64, _P]),
     "nvfp4_status_string": (ctypes.c_char_p, [_INT]),
     "nvfp4_last_error": (ctypes.c_char_p, []),
     "nvfp4_build_info": (ctypes.c_char_p, []),
@@ -370,6 +372,18 @@ def nvfp4_gemm_swiglu_pair(a: Nvfp4Tensor, w: Nvfp4Tensor, bias=None, amax=None,
           None if amax is None else _amax_ptr(amax), a.rows if amax_rows is None else amax_rows,
           _stream_handle(stream))
     return gate_out, up_out
+
+
+def nvfp4_mfma_ceiling(workgroups: int, iters: int, stream=None):
+    """Run the matrix-core ceiling kernel once (a measurement aid, not a step of the
+    method). Returns the per-wave uint64 tensor [workgroups * 4, 2] of (shader-clock
+    cycles, 100 MHz ticks); time the call with events for the rate. Each wave issues
+    iters * 4 MFMAs of 2 * 32 * 32 * 16 FLOP."""
+    import torch
+    nbytes = lib().nvfp4_mfma_ceiling_out_bytes(workgroups)
+    out = torch.zeros((max(nbytes, 16) // 8,), dtype=torch.int64, device=torch.cuda.current_device())
+    _call("nvfp4_mfma_ceiling", workgroups, iters, out.data_ptr(), nbytes, _stream_handle(stream))
+    return out.view(-1, 2)
 
 
 def nvfp4_silu_bf16(x, out=None, stream=None):

@@ -31,6 +31,7 @@ const void* gemm_kernel_ptr(int kind);
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
                        const GemmEpilogue& ep, int cu_count, hipStream_t stream);
+hipError_t launch_mfma_ceiling(uint64_t* out, int64_t workgroups, int64_t iters, hipStream_t stream);
 }  // namespace nvfp4
 
 namespace {
@@ -316,6 +317,24 @@ int nvfp4_silu_bf16(const void* x_dev, void* y_dev, int64_t count, void* stream)
   if (rc != NVFP4_OK) return rc;
   hipError_t e = nvfp4::launch_silu_apply((const uint16_t*)x_dev, (uint16_t*)y_dev, count, (hipStream_t)stream);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "silu launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int64_t nvfp4_mfma_ceiling_out_bytes(int64_t workgroups) { return workgroups > 0 ? workgroups * 4 * 16 : 0; }
+
+int nvfp4_mfma_ceiling(int64_t workgroups, int64_t iters, void* out_dev, int64_t out_bytes, void* stream) {
+  if (workgroups < 1 || workgroups > 65536) return fail(NVFP4_ERR_INVALID_ARG, "workgroups must be in [1, 65536]");
+  if (iters < 1 || iters > ((int64_t)1 << 24)) return fail(NVFP4_ERR_INVALID_ARG, "iters must be in [1, 2^24]");
+  if (!out_dev) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if ((uintptr_t)out_dev & 7u) return fail(NVFP4_ERR_MISALIGNED, "out must be 8-byte aligned");
+  if (out_bytes < nvfp4_mfma_ceiling_out_bytes(workgroups))
+    return fail(NVFP4_ERR_INVALID_ARG, "out holds %lld bytes; %lld needed", (long long)out_bytes,
+                (long long)nvfp4_mfma_ceiling_out_bytes(workgroups));
+  DeviceState* st = nullptr;
+  int rc = ensure_device(&st);
+  if (rc != NVFP4_OK) return rc;
+  hipError_t e = nvfp4::launch_mfma_ceiling((uint64_t*)out_dev, workgroups, iters, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "ceiling launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -198,6 +198,19 @@ def test_silu_validation():
     assert nv.lib().nvfp4_silu_bf16(FAKE + 1, FAKE, 4, None) == 3
 
 
+def test_mfma_ceiling_validation():
+    l = nv.lib()
+    assert l.nvfp4_mfma_ceiling_out_bytes(3) == 3 * 4 * 16
+    assert l.nvfp4_mfma_ceiling_out_bytes(0) == 0
+    assert l.nvfp4_mfma_ceiling(0, 10, FAKE, 1 << 20, None) == 1
+    assert l.nvfp4_mfma_ceiling(65537, 10, FAKE, 1 << 30, None) == 1
+    assert l.nvfp4_mfma_ceiling(4, 0, FAKE, 1 << 20, None) == 1
+    assert l.nvfp4_mfma_ceiling(4, (1 << 24) + 1, FAKE, 1 << 20, None) == 1
+    assert l.nvfp4_mfma_ceiling(4, 10, None, 1 << 20, None) == 1
+    assert l.nvfp4_mfma_ceiling(4, 10, FAKE + 4, 1 << 20, None) == 3
+    assert l.nvfp4_mfma_ceiling(4, 10, FAKE, 4 * 4 * 16 - 1, None) == 1
+
+
 def test_status_strings():
     for s in range(7):
         assert nv.nvfp4_status_string(s) not in ("", "unknown status")

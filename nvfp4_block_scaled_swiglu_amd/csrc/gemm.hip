@@ -625,39 +625,143 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
         }
       }
       ccount = 0;
+      // every lane continues from the wave's maximum (non-negative fp32 bits order as integers)
+      uint32_t yb = __float_as_uint(ymax);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)yb, off, 64);
+        yb = yb > o ? yb : o;
+      }
+      ymax = __uint_as_float(yb);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(0xC07F);  // the list reads are done before it is refilled
       asm volatile("" ::: "memory");
     };
     if (EPI == 2 && a.ep.amax)
       ymax = __uint_as_float(__hip_atomic_load((const uint32_t*)a.ep.amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    // Kind 2 first screens each 64-row half in registers, on the fp32 values before
+    // their bf16 rounding: for a gate g and up u of one channel, with G = max(|g|,
+    // 0.28125), s = G |u| + G 2^-130 (one multiply, one fused multiply-add) satisfies
+    // |silu_bf16(RN(g)) RN(u)| <= (1 + 2^-6) s for ymax >= 2^-100: (1 + 2^-8) per bf16
+    // rounding, the fp32 roundings, and the subnormal-u term covered by G 2^-130. A half
+    // whose largest s (rows below amax_rows) is at most T = ymax (1 - 2^-6) holds no
+    // product above ymax, so it skips the exact scan. T is capped at 2^125 so that a
+    // product that overflows bf16 is always scanned, and is 0 while ymax < 2^-100.
+    auto threshold = [&]() -> float { return ymax < 0x1p-100f ? 0.0f : fminf(ymax * 0.984375f, 0x1p125f); };
+    // the exact scan of the staged half: elements of rows < amax_rows whose bound on
+    // the bf16 values reaches the running maximum go to the candidate list
+    auto scan_half = [&](int half) __attribute__((always_inline)) {
+      // seed: each lane's largest-bound element of the half is resolved first, so that
+      // a half scanned while ymax is still low (the first tiles) queues few candidates
+      float bbest = -1.0f;
+      uint32_t best = 0;
+#pragma nounroll
+      for (int t = 0; t < kIts; ++t) {
+        const int r = t * kRowsPerStore + rl;
+        const int64_t m = wrow0 + half * 64 + r;
+        const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
+        const uint32_t r0 = pair_swap(is_up ? v[0] : v[2]), r1 = pair_swap(is_up ? v[1] : v[3]);
+        const uint32_t gpk[2] = {is_up ? r0 : v[0], is_up ? r1 : v[1]};
+        const uint32_t upk[2] = {is_up ? v[2] : r0, is_up ? v[3] : r1};
+        const bool ok = m < a.ep.amax_rows && col_ok;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t g16 = (gpk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          const uint32_t u16 = (upk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          const float bnd = fmaxf(fabsf(bf16_bits_to_float(g16)), 0.28125f) * fabsf(bf16_bits_to_float(u16));
+          if (ok && bnd > bbest) {
+            bbest = bnd;
+            best = g16 | (u16 << 16);
+          }
+        }
+      }
+      if (ccount + 64 > kCand) flush();
+      {
+        const bool has = bbest >= 0.0f;
+        const uint64_t mask = __ballot(has);
+        if (has) {
+          const int off = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+          clist[ccount + off] = best;
+        }
+        ccount += __builtin_amdgcn_readfirstlane(__popcll(mask));
+      }
+      flush();
+      // the pair trades halves: the gate lane keeps (gate, up) of channels j0 .. j0+3,
+      // the up lane those of j0+4 .. j0+7
+#pragma nounroll
+      for (int t = 0; t < kIts; ++t) {
+        if (ccount + 256 > kCand) flush();  // room for this row's 4 x 64 candidates
+        const int r = t * kRowsPerStore + rl;
+        const int64_t m = wrow0 + half * 64 + r;
+        const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
+        const uint32_t r0 = pair_swap(is_up ? v[0] : v[2]), r1 = pair_swap(is_up ? v[1] : v[3]);
+        const uint32_t gpk[2] = {is_up ? r0 : v[0], is_up ? r1 : v[1]};
+        const uint32_t upk[2] = {is_up ? v[2] : r0, is_up ? v[3] : r1};
+        const bool ok = m < a.ep.amax_rows && col_ok;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t g16 = (gpk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          const uint32_t u16 = (upk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          const float gb = fmaxf(fabsf(bf16_bits_to_float(g16)), 0.28125f);
+          const float ub = fabsf(bf16_bits_to_float(u16));
+          const bool cand = ok && gb * ub * (1.0f + 0x1p-7f) + 0x1p-140f >= ymax;  // margin covers fp32 rounding
+          const uint64_t mask = __ballot(cand);
+          const int nc = __builtin_amdgcn_readfirstlane(__popcll(mask));
+          if (nc) {
+            if (cand) {
+              const int off = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+              clist[ccount + off] = g16 | (u16 << 16);
+            }
+            ccount += nc;
+          }
+        }
+      }
+    };
 #pragma unroll
     for (int half = 0; half < FM / 2; ++half) {
       // registers -> LDS: fragments i = 2 half, 2 half + 1 hold rows 64 half .. 64 half + 63
+      float smax = 0.0f;  // kind 2: the half's largest screening bound s (rows < amax_rows)
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
         const int i = 2 * half + ii;
+        float smax_ii = 0.0f;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
+          float f[4][4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[q][e] = __builtin_fmaf(acc[j][i][q * 4 + e], alpha, bq[j][q][e]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float* b = bq[j][q];
-            const u32x2_t v = {cvt_pk_bf16_rn(__builtin_fmaf(acc[j][i][q * 4 + 0], alpha, b[0]),
-                                              __builtin_fmaf(acc[j][i][q * 4 + 1], alpha, b[1])),
-                               cvt_pk_bf16_rn(__builtin_fmaf(acc[j][i][q * 4 + 2], alpha, b[2]),
-                                              __builtin_fmaf(acc[j][i][q * 4 + 3], alpha, b[3]))};
+            const u32x2_t v = {cvt_pk_bf16_rn(f[q][0], f[q][1]), cvt_pk_bf16_rn(f[q][2], f[q][3])};
             const int r = ii * 32 + lr, c = j * 32 + q * 8 + h * 4;
             *(u32x2_t*)(stg + r * kRowBytes + c * 2) = v;
           }
+          if constexpr (EPI == 2) {
+            // accumulator chunks q = 0, 2 are gate channels, q = 1, 3 the same up channels
+#pragma unroll
+            for (int pq = 0; pq < 4; pq += 2)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float G = fmaxf(fabsf(f[pq][e]), 0.28125f);
+                smax_ii = fmaxf(smax_ii, __builtin_fmaf(G, 0x1p-130f, G * fabsf(f[pq + 1][e])));
+              }
+          }
+        }
+        if constexpr (EPI == 2) {
+          const int64_t m = wrow0 + half * 64 + ii * 32 + lr;
+          smax = m < a.ep.amax_rows ? fmaxf(smax, smax_ii) : smax;
         }
       }
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
       asm volatile("" ::: "memory");
-      // LDS -> global: lane L takes 8 columns of one row, kBatch rows at a time
+      if constexpr (EPI == 1) {
+        // LDS -> global: lane L takes 8 columns of one row, kBatch rows at a time
 #pragma unroll
-      for (int b0 = 0; b0 < kIts; b0 += kBatch) {
-        if constexpr (EPI == 1) {
+        for (int b0 = 0; b0 < kIts; b0 += kBatch) {
           u32x4_t rv[kBatch];
 #pragma unroll
           for (int t = 0; t < kBatch; ++t) {
@@ -683,40 +787,18 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
             }
             if (m < a.m_pad && col_ok) *(u32x4_t*)(a.d + m * a.n + col) = v;
           }
-        } else {
-          // the pair trades halves: the gate lane keeps (gate, up) of channels j0 .. j0+3,
-          // the up lane those of j0+4 .. j0+7
-#pragma nounroll
-          for (int t = 0; t < kBatch; ++t) {
-            if (ccount + 256 > kCand) flush();  // room for this row's 4 x 64 candidates
-            const int r = (b0 + t) * kRowsPerStore + rl;
-            const int64_t m = wrow0 + half * 64 + r;
-            const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
-            if (m < a.m_pad && col_ok) *(u32x4_t*)((is_up ? a.ep.up_out : a.ep.gate_out) + m * n_half + j0) = v;
-            const uint32_t r0 = pair_swap(is_up ? v[0] : v[2]), r1 = pair_swap(is_up ? v[1] : v[3]);
-            const uint32_t gpk[2] = {is_up ? r0 : v[0], is_up ? r1 : v[1]};
-            const uint32_t upk[2] = {is_up ? v[2] : r0, is_up ? v[3] : r1};
-            const bool ok = m < a.ep.amax_rows && col_ok;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t g16 = (gpk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-              const uint32_t u16 = (upk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-              const float gb = fmaxf(fabsf(bf16_bits_to_float(g16)), 0.28125f);
-              const float ub = fabsf(bf16_bits_to_float(u16));
-              const bool cand = ok && gb * ub * (1.0f + 0x1p-7f) + 0x1p-140f >= ymax;  // margin covers fp32 rounding
-              const uint64_t mask = __ballot(cand);
-              const int nc = __builtin_amdgcn_readfirstlane(__popcll(mask));
-              if (nc) {
-                if (cand) {
-                  const int off = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-                  clist[ccount + off] = g16 | (u16 << 16);
-                }
-                ccount += nc;
-              }
-            }
-          }
         }
+      } else {
+        // LDS -> global: gate and up row segments to their own tensors
+#pragma unroll
+        for (int t = 0; t < kIts; ++t) {
+          const int r = t * kRowsPerStore + rl;
+          const int64_t m = wrow0 + half * 64 + r;
+          const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
+          if (m < a.m_pad && col_ok) *(u32x4_t*)((is_up ? a.ep.up_out : a.ep.gate_out) + m * n_half + j0) = v;
+        }
+        const float T = threshold();
+        if (__ballot(smax > T) != 0) scan_half(half);
       }
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next half overwrites

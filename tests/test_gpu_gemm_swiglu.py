@@ -104,6 +104,32 @@ def test_amax_accumulates_and_excludes_padding(gpu):
     assert float(big.item()) == np.float32(1e30)
 
 
+@pytest.mark.parametrize("log2_scale", [-60, -66, -72, 0, 63, 66])
+def test_amax_extreme_magnitudes(gpu, log2_scale):
+    """The amax stays exactly max |y| of the kernel's own outputs when the outputs are
+    scaled by a power of two (through the activation's global scale): products in the
+    bf16 subnormal range or underflowing to zero (where the register screen's threshold
+    is 0 and every half is scanned exactly), and products that overflow bf16 to inf."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    m, n_half, k = 300, 256, 320
+    _say(f"[swiglu-pair] outputs scaled by 2^{log2_scale}")
+    a, wt, _ = make_operands(m, n_half, k, 11, gpu)
+    a.global_scale.mul_(2.0 ** log2_scale)
+    amax = torch.zeros(1, dtype=torch.float32, device=gpu)
+    g, u = nv.nvfp4_gemm_swiglu_pair(a, wt, amax=amax)
+    torch.cuda.synchronize(gpu)
+    gb, ub = parity.tensor_bits(g), parity.tensor_bits(u)
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = swiglu_abs_max(gb[:m], ub[:m])
+    got = float(amax.item())
+    assert np.float32(got) == np.float32(want), (got, want)
+    if log2_scale == 66:
+        assert np.isinf(got)
+    if log2_scale == -66:
+        assert 0.0 < got < 2.0 ** -120
+
+
 def test_chain_small(gpu):
     """FC1 pair GEMM -> amax -> single-read producer equals the two-pass producer and
     the oracle, byte for byte."""

@@ -552,8 +552,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
     constexpr int kWaveCols = FN * 32, kRowBytes = kWaveCols * 2 + 16;  // padded against bank conflicts
     constexpr int kChunksPerRow = kWaveCols / 8, kRowsPerStore = 64 / kChunksPerRow;
     constexpr int kIts = 64 / kRowsPerStore;            // store iterations per 64-row half
-    constexpr int kBatch = kIts < 8 ? kIts : 8;          // residual rows / silu lookups in flight
-    static_assert(kIts % kBatch == 0, "whole batches");
     static_assert(64 * kRowBytes <= kStages * BigTile::StageBytes / kWaves, "staging fits the wave's LDS share");
     unsigned char* stg = smem + wave * (kStages * BigTile::StageBytes / kWaves);
     const int64_t wrow0 = em0 + wm * FM * 32, wcol0 = en0 + wn * FN * 32;
@@ -562,8 +560,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
     const bool col_ok = col < a.n;
     stage_barrier();  // every wave has finished reading the last K step's stage
     // bias of the lane's accumulator columns j*32 + q*8 + h*4 .. +3 (loaded after the
-    // barrier so that nothing lives through the K loop); zero without a bias
-    float bq[FN][4][4];
+    // barrier so that nothing lives through the K loop); zero without a bias. Kept as
+    // bf16 pairs and widened where used.
+    u32x2_t bq[FN][4];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -571,8 +570,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
         const int64_t c = wcol0 + j * 32 + q * 8 + h * 4;
         u32x2_t bv = {0u, 0u};
         if (a.ep.bias && c < a.n) bv = *(const u32x2_t*)(a.ep.bias + c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bq[j][q][e] = bf16_bits_to_float((bv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        bq[j][q] = bv;
       }
     }
     // kind 1: the gate of the lane's 8 store-phase columns (1.0 without a gate)
@@ -720,6 +718,17 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
     };
 #pragma unroll
     for (int half = 0; half < FM / 2; ++half) {
+      // kind 1: the residual row segments of this half, issued before its staging so
+      // that their latency overlaps it
+      u32x4_t rv[kIts];
+      if constexpr (EPI == 1) {
+#pragma unroll
+        for (int t = 0; t < kIts; ++t) {
+          const int64_t m = wrow0 + half * 64 + t * kRowsPerStore + rl;
+          const u32x4_t z = {0u, 0u, 0u, 0u};
+          rv[t] = (a.ep.res && m < a.m_pad && col_ok) ? *(const u32x4_t*)(a.ep.res + m * a.n + col) : z;
+        }
+      }
       // registers -> LDS: fragments i = 2 half, 2 half + 1 hold rows 64 half .. 64 half + 63
       float smax = 0.0f;  // kind 2: the half's largest screening bound s (rows < amax_rows)
 #pragma unroll
@@ -732,7 +741,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) f[q][e] = __builtin_fmaf(acc[j][i][q * 4 + e], alpha, bq[j][q][e]);
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t bw = bq[j][q][e >> 1];
+              const float b = (e & 1) ? __uint_as_float(bw & 0xFFFF0000u) : __uint_as_float(bw << 16);
+              f[q][e] = __builtin_fmaf(acc[j][i][q * 4 + e], alpha, b);
+            }
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const u32x2_t v = {cvt_pk_bf16_rn(f[q][0], f[q][1]), cvt_pk_bf16_rn(f[q][2], f[q][3])};
@@ -759,34 +772,24 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
       asm volatile("" ::: "memory");
       if constexpr (EPI == 1) {
-        // LDS -> global: lane L takes 8 columns of one row, kBatch rows at a time
+        // LDS -> global: lane L takes 8 columns of one row
 #pragma unroll
-        for (int b0 = 0; b0 < kIts; b0 += kBatch) {
-          u32x4_t rv[kBatch];
+        for (int t = 0; t < kIts; ++t) {
+          const int r = t * kRowsPerStore + rl;
+          const int64_t m = wrow0 + half * 64 + r;
+          u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
+          if (a.ep.res) {
+            // res + gate * D1 in fp32: the product of two bf16 values is exact, so
+            // the fused multiply-add is that sum rounded once
 #pragma unroll
-          for (int t = 0; t < kBatch; ++t) {
-            const int64_t m = wrow0 + half * 64 + (b0 + t) * kRowsPerStore + rl;
-            const u32x4_t z = {0u, 0u, 0u, 0u};
-            rv[t] = (a.ep.res && m < a.m_pad && col_ok) ? *(const u32x4_t*)(a.ep.res + m * a.n + col) : z;
-          }
-#pragma unroll
-          for (int t = 0; t < kBatch; ++t) {
-            const int r = (b0 + t) * kRowsPerStore + rl;
-            const int64_t m = wrow0 + half * 64 + r;
-            u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
-            if (a.ep.res) {
-              // res + gate * D1 in fp32: the product of two bf16 values is exact, so
-              // the fused multiply-add is that sum rounded once
-#pragma unroll
-              for (int w = 0; w < 4; ++w) {
-                const float d0 = bf16_bits_to_float(v[w] & 0xFFFFu), d1 = __uint_as_float(v[w] & 0xFFFF0000u);
-                const float r0 = bf16_bits_to_float(rv[t][w] & 0xFFFFu);
-                const float r1 = __uint_as_float(rv[t][w] & 0xFFFF0000u);
-                v[w] = cvt_pk_bf16_rn(__builtin_fmaf(gate8[2 * w], d0, r0), __builtin_fmaf(gate8[2 * w + 1], d1, r1));
-              }
+            for (int w = 0; w < 4; ++w) {
+              const float d0 = bf16_bits_to_float(v[w] & 0xFFFFu), d1 = __uint_as_float(v[w] & 0xFFFF0000u);
+              const float r0 = bf16_bits_to_float(rv[t][w] & 0xFFFFu);
+              const float r1 = __uint_as_float(rv[t][w] & 0xFFFF0000u);
+              v[w] = cvt_pk_bf16_rn(__builtin_fmaf(gate8[2 * w], d0, r0), __builtin_fmaf(gate8[2 * w + 1], d1, r1));
             }
-            if (m < a.m_pad && col_ok) *(u32x4_t*)(a.d + m * a.n + col) = v;
           }
+          if (m < a.m_pad && col_ok) *(u32x4_t*)(a.d + m * a.n + col) = v;
         }
       } else {
         // LDS -> global: gate and up row segments to their own tensors

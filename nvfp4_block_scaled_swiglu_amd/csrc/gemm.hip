@@ -574,13 +574,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
       }
     }
     // kind 1: the gate of the lane's 8 store-phase columns (1.0 without a gate)
-    float gate8[8];
-    {
-      u32x4_t gv = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-      if (EPI == 1 && a.ep.gate && col_ok) gv = *(const u32x4_t*)(a.ep.gate + col);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gate8[e] = bf16_bits_to_float((gv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-    }
+    // (bf16 pairs, widened where used)
+    u32x4_t gate8 = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    if (EPI == 1 && a.ep.gate && col_ok) gate8 = *(const u32x4_t*)(a.ep.gate + col);
     // kind 2: the SwiGLU pair. Even chunks of 8 columns are gate channels j0 .. j0+7,
     // odd chunks the same up channels (j0 = col / 16 * 8).
     const bool is_up = (ch & 1) != 0;
@@ -722,11 +718,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
       // that their latency overlaps it
       u32x4_t rv[kIts];
       if constexpr (EPI == 1) {
+        const int64_t m0r = wrow0 + half * 64 + rl;
+        const uint16_t* rp = a.ep.res ? a.ep.res + m0r * a.n + col : nullptr;
+        const int64_t rstride = (int64_t)kRowsPerStore * a.n;
 #pragma unroll
         for (int t = 0; t < kIts; ++t) {
-          const int64_t m = wrow0 + half * 64 + t * kRowsPerStore + rl;
           const u32x4_t z = {0u, 0u, 0u, 0u};
-          rv[t] = (a.ep.res && m < a.m_pad && col_ok) ? *(const u32x4_t*)(a.ep.res + m * a.n + col) : z;
+          rv[t] = (a.ep.res && m0r + t * kRowsPerStore < a.m_pad && col_ok) ? *(const u32x4_t*)(rp + t * rstride) : z;
         }
       }
       // registers -> LDS: fragments i = 2 half, 2 half + 1 hold rows 64 half .. 64 half + 63
@@ -786,7 +784,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
               const float d0 = bf16_bits_to_float(v[w] & 0xFFFFu), d1 = __uint_as_float(v[w] & 0xFFFF0000u);
               const float r0 = bf16_bits_to_float(rv[t][w] & 0xFFFFu);
               const float r1 = __uint_as_float(rv[t][w] & 0xFFFF0000u);
-              v[w] = cvt_pk_bf16_rn(__builtin_fmaf(gate8[2 * w], d0, r0), __builtin_fmaf(gate8[2 * w + 1], d1, r1));
+              const float g0 = __uint_as_float(gate8[w] << 16), g1 = __uint_as_float(gate8[w] & 0xFFFF0000u);
+              v[w] = cvt_pk_bf16_rn(__builtin_fmaf(g0, d0, r0), __builtin_fmaf(g1, d1, r1));
             }
           }
           if (m < a.m_pad && col_ok) *(u32x4_t*)(a.d + m * a.n + col) = v;

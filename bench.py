@@ -59,20 +59,27 @@ def gemm_bytes(m: int, n: int, k: int) -> int:
 
 GEMM_SOURCES = ("nvfp4_block_scaled_swiglu_amd/csrc/gemm.hip", "nvfp4_block_scaled_swiglu_amd/csrc/common.hpp")
 GEMM_TRAFFIC_SUMMARY = "profiles/gemm_fc2_hbm_traffic.md"
+PRODUCER_SOURCES = ("nvfp4_block_scaled_swiglu_amd/csrc/producer.hip",
+                    "nvfp4_block_scaled_swiglu_amd/csrc/common.hpp")
+SINGLE_READ_TRAFFIC_SUMMARY = "profiles/producer_single_read_fc2_hbm_traffic.md"
 
 
 def measured_gemm_traffic():
-    """HBM bytes per GEMM launch from the committed counter summary (FETCH_SIZE and
+    return measured_traffic(GEMM_TRAFFIC_SUMMARY, GEMM_SOURCES)
+
+
+def measured_traffic(summary: str, sources):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE and
     WRITE_SIZE, each scaled by a copy kernel of known size), or None when the summary
     was taken on a different kernel source than the one built here."""
     import hashlib
     try:
         h = hashlib.sha256()
-        for f in GEMM_SOURCES:
+        for f in sources:
             with open(os.path.join(ROOT, f), "rb") as fh:
                 h.update(fh.read())
         vals = {}
-        with open(os.path.join(ROOT, GEMM_TRAFFIC_SUMMARY)) as fh:
+        with open(os.path.join(ROOT, summary)) as fh:
             for line in fh:
                 if ":" in line and not line.startswith(("#", "|", "`")):
                     k, _, v = line.partition(":")
@@ -216,29 +223,36 @@ def only_gemm(w, args, dev) -> int:
            "tflops": round(tflops, 2), "frac_of_peak": round(tflops / PEAK_MFMA_TFLOPS, 4), "steps": args.steps,
            "gemm_distinct_bytes": gemm_bytes(w.m, w.n, w.k)}
     if args.copy_bytes > 0:
-        # calibration for the profiler's byte counters: a plain elementwise pass that
-        # reads copy_bytes and writes copy_bytes (int32 x | 0), launched `steps` times
-        n = args.copy_bytes // 4
-        src = torch.ones(n, dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        torch.bitwise_or(src, 0, out=dst)
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        for _ in range(args.steps):
-            torch.bitwise_or(src, 0, out=dst)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        t_copy = c0.elapsed_time(c1) / args.steps
-        out["copy_bytes"] = 4 * n
-        out["copy_ms"] = round(t_copy, 4)
-        out["copy_gbs"] = round(2 * 4 * n / (t_copy * 1e-3) / 1e9, 1)
+        out.update(copy_calibration(args.copy_bytes, args.steps, dev, stream))
     print(json.dumps(out), flush=True)
     return 0
 
 
+def copy_calibration(nbytes: int, steps: int, dev, stream) -> dict:
+    """Calibration for the profiler's byte counters: a plain elementwise pass that reads
+    nbytes and writes nbytes (int32 x | 0), launched `steps` times."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.bitwise_or(src, 0, out=dst)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(steps):
+        torch.bitwise_or(src, 0, out=dst)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    t_copy = c0.elapsed_time(c1) / steps
+    return {"copy_bytes": 4 * n, "copy_ms": round(t_copy, 4), "copy_gbs": round(2 * 4 * n / (t_copy * 1e-3) / 1e9, 1)}
+
+
 def only_producer(w, args, dev) -> int:
-    """Producer-only timing on the workload's seeded inputs (no GEMM in the process)."""
+    """Producer-only timing on the workload's seeded inputs (no GEMM in the process).
+    With --single-read, the single-read producer alone, with the amax an upstream stage
+    would supply (set up with the library's silu, not timed); it is an ordinary launch,
+    so the profiler can trace and count it (the two-pass producer's cooperative launch
+    ends the profiler)."""
     import statistics
     import torch
     import nvfp4_block_scaled_swiglu_amd as nv
@@ -249,9 +263,23 @@ def only_producer(w, args, dev) -> int:
     del acts
     a = nv.empty_nvfp4(w.m, w.k, dev)
     stream = torch.cuda.current_stream()
+    amax = None
+    if args.single_read:
+        if w.swiglu:
+            sx = nv.nvfp4_silu_bf16(x.view(torch.int16)).view(torch.bfloat16)
+            amax = (sx.float() * u.float()).bfloat16().abs().max().float().reshape(1)
+            del sx
+        else:
+            amax = x.abs().max().float().reshape(1)
+        torch.cuda.synchronize()
 
     def run():
-        if w.swiglu:
+        if amax is not None:
+            if w.swiglu:
+                nv.nvfp4_quantize_swiglu_amax(x, u, amax, out=a)
+            else:
+                nv.nvfp4_quantize_amax(x, amax, out=a)
+        elif w.swiglu:
             nv.nvfp4_quantize_swiglu(x, u, out=a)
         else:
             nv.nvfp4_quantize(x, out=a)
@@ -266,10 +294,13 @@ def only_producer(w, args, dev) -> int:
         e[1].record(stream)
     torch.cuda.synchronize()
     t_prod = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs)
-    pbytes = producer_bytes(w.m, w.k, w.swiglu)
-    print(json.dumps({"mode": "only-producer", "workload": w.name, "producer_ms": round(t_prod, 4),
-                      "gbs": round(pbytes / (t_prod * 1e-3) / 1e9, 1), "algorithmic_bytes": pbytes,
-                      "steps": args.steps}), flush=True)
+    pbytes = (producer_single_read_bytes if args.single_read else producer_bytes)(w.m, w.k, w.swiglu)
+    out = {"mode": "only-producer" + (" (single read)" if args.single_read else ""), "workload": w.name,
+           "producer_ms": round(t_prod, 4), "gbs": round(pbytes / (t_prod * 1e-3) / 1e9, 1),
+           "algorithmic_bytes": pbytes, "steps": args.steps}
+    if args.copy_bytes > 0:
+        out.update(copy_calibration(args.copy_bytes, args.steps, dev, stream))
+    print(json.dumps(out), flush=True)
     return 0
 
 
@@ -445,9 +476,11 @@ def main() -> int:
                     help="producer + GEMM on every projection shape, one JSON line each")
     ap.add_argument("--only-producer", action="store_true",
                     help="time the producer alone on the workload's seeded inputs (no GEMM launch)")
+    ap.add_argument("--single-read", action="store_true",
+                    help="with --only-producer: time the single-read producer (amax supplied) instead")
     ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="with --only-gemm: also run a plain elementwise copy of this many bytes (read + "
-                         "write), the calibration kernel for the profiler's FETCH_SIZE / WRITE_SIZE")
+                    help="with --only-gemm or --only-producer: also run a plain elementwise copy of this many "
+                         "bytes (read + write), the calibration kernel for the profiler's FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path is single-GPU; see DESIGN.md for how it "
@@ -639,6 +672,9 @@ def main() -> int:
             "achieved_gbs": round(sbytes / (t_single * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(sbytes / (t_single * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "bytes_equal_two_pass": same_bytes,
+            "traffic": (measured_traffic(SINGLE_READ_TRAFFIC_SUMMARY, PRODUCER_SOURCES)
+                        if w.name == "fc2_canonical" else None),
+            "traffic_summary": SINGLE_READ_TRAFFIC_SUMMARY,
         },
         "gemm_fused_epilogue": {
             "entry": "nvfp4_gemm_bf16out_fused",

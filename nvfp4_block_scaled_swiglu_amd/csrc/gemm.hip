@@ -799,8 +799,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
           const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
           if (m < a.m_pad && col_ok) *(u32x4_t*)((is_up ? a.ep.up_out : a.ep.gate_out) + m * n_half + j0) = v;
         }
+        // (no amax pointer: nothing to fold, no scan)
         const float T = threshold();
-        if (__ballot(smax > T) != 0) scan_half(half);
+        if (a.ep.amax && __ballot(smax > T) != 0) scan_half(half);
       }
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next half overwrites

@@ -104,6 +104,20 @@ def test_amax_accumulates_and_excludes_padding(gpu):
     assert float(big.item()) == np.float32(1e30)
 
 
+def test_pair_without_amax(gpu):
+    """With no amax pointer the gate and up outputs are the same bytes."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    m, n_half, k = 300, 256, 320
+    a, wt, _ = make_operands(m, n_half, k, 13, gpu)
+    amax = torch.zeros(1, dtype=torch.float32, device=gpu)
+    g1, u1 = nv.nvfp4_gemm_swiglu_pair(a, wt, amax=amax)
+    g0, u0 = nv.nvfp4_gemm_swiglu_pair(a, wt)
+    torch.cuda.synchronize(gpu)
+    assert torch.equal(g0, g1) and torch.equal(u0, u1)
+    assert float(amax.item()) > 0.0
+
+
 @pytest.mark.parametrize("log2_scale", [-60, -66, -72, 0, 63, 66])
 def test_amax_extreme_magnitudes(gpu, log2_scale):
     """The amax stays exactly max |y| of the kernel's own outputs when the outputs are

@@ -669,7 +669,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
           }
         }
       }
-      if (ccount + 64 > kCand) flush();
+      // (the list is empty here: every scan ends with it flushed)
       {
         const bool has = bbest >= 0.0f;
         const uint64_t mask = __ballot(has);
@@ -679,12 +679,19 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
         }
         ccount += __builtin_amdgcn_readfirstlane(__popcll(mask));
       }
-      flush();
-      // the pair trades halves: the gate lane keeps (gate, up) of channels j0 .. j0+3,
-      // the up lane those of j0+4 .. j0+7
+      // Then every element whose bound reaches ymax. One flush site: the seeds first,
+      // then whenever a row's 4 x 64 candidates might not fit, and once at the end. The
+      // pair trades halves: the gate lane keeps (gate, up) of channels j0 .. j0+3, the
+      // up lane those of j0+4 .. j0+7.
+      bool pending = true;
+      int t = 0;
 #pragma nounroll
-      for (int t = 0; t < kIts; ++t) {
-        if (ccount + 256 > kCand) flush();  // room for this row's 4 x 64 candidates
+      for (;;) {
+        if (pending || ccount + 256 > kCand) {
+          flush();
+          pending = false;
+        }
+        if (t == kIts) break;
         const int r = t * kRowsPerStore + rl;
         const int64_t m = wrow0 + half * 64 + r;
         const u32x4_t v = *(const u32x4_t*)(stg + r * kRowBytes + ch * 16);
@@ -692,10 +699,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
         const uint32_t gpk[2] = {is_up ? r0 : v[0], is_up ? r1 : v[1]};
         const uint32_t upk[2] = {is_up ? v[2] : r0, is_up ? v[3] : r1};
         const bool ok = m < a.ep.amax_rows && col_ok;
-#pragma unroll
+#pragma nounroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t g16 = (gpk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          const uint32_t u16 = (upk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          const uint32_t g16 = ((e >> 1) ? gpk[1] : gpk[0]) >> (16 * (e & 1)) & 0xFFFFu;
+          const uint32_t u16 = ((e >> 1) ? upk[1] : upk[0]) >> (16 * (e & 1)) & 0xFFFFu;
           const float gb = fmaxf(fabsf(bf16_bits_to_float(g16)), 0.28125f);
           const float ub = fabsf(bf16_bits_to_float(u16));
           const bool cand = ok && gb * ub * (1.0f + 0x1p-7f) + 0x1p-140f >= ymax;  // margin covers fp32 rounding
@@ -710,6 +717,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
             ccount += nc;
           }
         }
+        ++t;
+        if (t == kIts) pending = ccount != 0;
       }
     };
 #pragma unroll
@@ -808,7 +817,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
       asm volatile("" ::: "memory");
     }
     if constexpr (EPI == 2) {
-      if (ccount) flush();
+      // (the candidate list is empty: each scan ends with it flushed)
       // one atomic max per wave (non-negative fp32 bits order as integers)
       uint32_t yb = __float_as_uint(ymax);
 #pragma unroll

@@ -180,14 +180,23 @@ def cpu_baseline(w, threads: int) -> dict:
     t0 = time.perf_counter()
     oracle.gemm_rows(aq, as_, w.m, ga, wq, ws, w.n, gw, w.k, sel, threads=threads)
     t_gemm = time.perf_counter() - t0
+    # one thread on a smaller evenly spaced sample
+    rows1 = min(128, w.m)
+    sel1 = np.arange(rows1) * (w.m // rows1)
+    t0 = time.perf_counter()
+    oracle.gemm_rows(aq, as_, w.m, ga, wq, ws, w.n, gw, w.k, sel1, threads=1)
+    t_gemm1 = time.perf_counter() - t0
     return {
         "value": 2.0 * rows * w.n * w.k / t_gemm / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"exact int64 GEMM of {rows} rows (every {w.m // rows}th of {w.m}) x {w.n} x {w.k} "
-                  f"({t_gemm:.2f} s); exact producer over all {w.m} x {w.k}: "
-                  f"{producer_bytes(w.m, w.k, w.swiglu) / t_prod / 1e9:.3f} GB/s ({t_prod:.2f} s)",
+                  f"({t_gemm:.2f} s; all {w.m} rows extrapolated: {t_gemm * w.m / rows:.1f} s); exact producer "
+                  f"over all {w.m} x {w.k}: {producer_bytes(w.m, w.k, w.swiglu) / t_prod / 1e9:.3f} GB/s "
+                  f"({t_prod:.2f} s)",
+        "single_thread": {"value": 2.0 * rows1 * w.n * w.k / t_gemm1 / 1e12, "unit": "TFLOP/s",
+                          "sample": f"exact GEMM of {rows1} evenly spaced rows on 1 thread ({t_gemm1:.2f} s)"},
     }
 
 

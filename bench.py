@@ -492,8 +492,8 @@ def main() -> int:
                          "bytes (read + write), the calibration kernel for the profiler's FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the path is single-GPU; see DESIGN.md for how it "
-              f"would shard); got --gpus {args.gpus}", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the path runs on a single GPU (one GPU's share of an "
+              f"M-sharded job); got --gpus {args.gpus}", file=sys.stderr)
         return 2
 
     import torch

@@ -32,7 +32,35 @@ M = {
  'gemm_scale_wrong_block': ('total += (int64_t)dot * (sa[b] * sw[b]);', 'total += (int64_t)dot * (sa[b] * sw[(b+1)%nb]);'),
  'gemm_code_table': ('static const int MAG2[8] = {0, 1, 2, 3, 4, 6, 8, 12};', 'static const int MAG2[8] = {0, 1, 2, 3, 4, 5, 8, 12};'),
  'gemm_nibble': ('A[i * k + c] = (int8_t)q2_of_code((c & 1) ? (byte >> 4) : (byte & 15));', 'A[i * k + c] = (int8_t)q2_of_code((c & 1) ? (byte & 15) : (byte >> 4));'),
+ # O11: quantization with a given amax
+ 'amax_sat_127': ('if (s == 0xFF) s = 126;', 'if (s == 0xFF) s = 127;'),
+ 'amax_given_abs': ('amax = *amax_given;', 'amax = fabs(*amax_given);'),
+ # O12: bias and gated residual in the GEMM epilogue
+ 'bias_after_round': ('uint16_t d1 = bias ? rn_bf16_sum_exact(neg, P, Ebase, bias[j]) : rn_bf16_exact(neg, P, Ebase);',
+                      'uint16_t d1 = bias ? rn_bf16_pair((long double)bf16_to_double(rn_bf16_exact(neg, P, Ebase)), (long double)bf16_to_double(bias[j])) : rn_bf16_exact(neg, P, Ebase);'),
+ 'gate_on_residual': ('d = rn_bf16_pair((long double)bf16_to_double(res[j]), prod);',
+                      'd = rn_bf16_pair(gv * (long double)bf16_to_double(res[j]), (long double)bf16_to_double(d1));'),
+ 'residual_sign': ('d = rn_bf16_pair((long double)bf16_to_double(res[j]), prod);',
+                   'd = rn_bf16_pair(-(long double)bf16_to_double(res[j]), prod);'),
+ # O13: adaLN modulation
+ 'mod_no_one': ('const float mf = 1.0f + (float)bf16_to_double(scale);', 'const float mf = (float)bf16_to_double(scale);'),
+ 'mod_shift_first': ('const float y = fmaf(xf, mf, (float)bf16_to_double(shift));',
+                     'const float y = (xf + (float)bf16_to_double(shift)) * mf;'),
+ 'mod_unfused': ('const float y = fmaf(xf, mf, (float)bf16_to_double(shift));',
+                 'volatile float pm = xf * mf; const float y = pm + (float)bf16_to_double(shift);'),
+ 'mod_scale_bf16': ('const float mf = 1.0f + (float)bf16_to_double(scale);',
+                    'const float mf = (float)bf16_to_double(oracle_rn_bf16(1.0 + bf16_to_double(scale)));'),
+ # O14: the SwiGLU pair split and its row maxima
+ 'pair_swap_gate_up': ('const uint16_t g = d[i * n + 16 * c + e], u = d[i * n + 16 * c + 8 + e];',
+                       'const uint16_t u = d[i * n + 16 * c + e], g = d[i * n + 16 * c + 8 + e];'),
+ 'pair_chunk4': ('const int64_t c = j / 8, e = j % 8;\n      const uint16_t g = d[i * n + 16 * c + e], u = d[i * n + 16 * c + 8 + e];',
+                 'const int64_t c = j / 4, e = j % 4;\n      const uint16_t g = d[i * n + 8 * c + e], u = d[i * n + 8 * c + 4 + e];'),
+ 'pair_ymax_signed': ('const double y = fabs(bf16_to_double(oracle_swiglu_bf16(g, u, tab)));',
+                      'const double y = bf16_to_double(oracle_swiglu_bf16(g, u, tab));'),
 }
+TESTS = ['tests/test_oracle_silu.py', 'tests/test_oracle_quant.py', 'tests/test_oracle_layout.py',
+         'tests/test_oracle_gemm.py', 'tests/test_oracle_amax.py', 'tests/test_oracle_epilogue.py',
+         'tests/test_oracle_modulate.py', 'tests/test_oracle_swiglu_pair.py']
 tmpd=tempfile.mkdtemp()
 res={}
 only=sys.argv[1:] 
@@ -44,7 +72,7 @@ for name,(a,b) in M.items():
     open(cpath,'w').write(msrc)
     subprocess.run(['gcc','-O2','-fopenmp','-fPIC','-shared','-std=gnu11',cpath,'-o',lib,'-lm'],check=True)
     env=dict(os.environ, NVFP4_ORACLE_LIB=lib)
-    r=subprocess.run([sys.executable,'-m','pytest','-x','-q','tests/test_oracle_silu.py','tests/test_oracle_quant.py','tests/test_oracle_layout.py','tests/test_oracle_gemm.py','-k','not exhaustive_against_decimal or silu'],cwd=ROOT,env=env,capture_output=True,text=True,timeout=900)
+    r=subprocess.run([sys.executable,'-m','pytest','-x','-q']+TESTS+['-k','not exhaustive_against_decimal or silu'],cwd=ROOT,env=env,capture_output=True,text=True,timeout=900)
     caught = r.returncode!=0
     last=[l for l in r.stdout.splitlines() if 'FAILED' in l or 'passed' in l or 'failed' in l]
     print(f'{name:25s} caught={caught} {last[:1]}',flush=True)

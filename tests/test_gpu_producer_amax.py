@@ -88,6 +88,33 @@ def test_empty_rows(gpu):
     assert float(t.global_scale.item()) == 2.0
 
 
+def test_strided_inputs(gpu):
+    """Row strides larger than k, different for gate and up (the FC1 pair GEMM's gate
+    and up outputs are read this way when a caller slices a wider buffer)."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    m, k = 150, 448
+    gate_full = synth.normal_bf16(m, k + 64, seed=23, tag=1, sigma=1.0)
+    up_full = synth.normal_bf16(m, k + 192, seed=23, tag=2, sigma=1.0)
+    gate, up = np.ascontiguousarray(gate_full[:, :k]), np.ascontiguousarray(up_full[:, :k])
+    amax = true_amax(gate, up)
+    _say(f"[producer-amax] strided m={m} k={k}")
+    g_t = parity.to_device_bf16(gate_full, gpu)[:, :k]
+    u_t = parity.to_device_bf16(up_full, gpu)[:, :k]
+    a = torch.tensor([amax], dtype=torch.float32, device=gpu)
+    t = nv.nvfp4_quantize_swiglu_amax(g_t, u_t, a)
+    x_t = parity.to_device_bf16(gate_full, gpu)[:, :k]
+    ax = torch.tensor([true_amax(gate, None)], dtype=torch.float32, device=gpu)
+    t2 = nv.nvfp4_quantize_amax(x_t, ax)
+    torch.cuda.synchronize(gpu)
+    rq, rs, rg = oracle.quantize_amax(gate, up, amax)
+    assert (t.qdata.cpu().numpy() == rq).all() and (t.scales.cpu().numpy() == rs).all()
+    assert np.float32(t.global_scale.item()) == np.float32(rg)
+    rq2, rs2, rg2 = oracle.quantize_amax(gate, None, true_amax(gate, None))
+    assert (t2.qdata.cpu().numpy() == rq2).all() and (t2.scales.cpu().numpy() == rs2).all()
+    assert np.float32(t2.global_scale.item()) == np.float32(rg2)
+
+
 def test_mid_and_outliers(gpu):
     w = synth.BY_NAME["mid_fc2_slice"]
     gate, up = w.activations()

@@ -174,6 +174,17 @@ __device__ __noinline__ uint32_t e2m1_code_exact(uint32_t y16, uint32_t s, float
   return sign | idx;
 }
 
+// Magnitude index il or il + 1 for a bf16 y whose |y| / unit lies next to the
+// rounding boundary between E2M1 magnitudes il and il + 1: the exact comparison of
+// |y| with that boundary times unit (exact in fp64), a tie going to the even index.
+__device__ __forceinline__ uint32_t e2m1_step_exact(uint32_t y16, uint32_t s, float g, uint32_t il) {
+  const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  const double a = (double)bf16_bits_to_float(y16 & 0x7FFFu);
+  const double t = mid[il] * ue4m3_to_double(s) * (double)g;  // exact
+  const bool up = (il & 1u) ? (a >= t) : (a > t);
+  return up ? il + 1u : il;
+}
+
 // ---- the kernel ------------------------------------------------------------------------------
 
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
@@ -498,17 +509,35 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
       fp4_pair<1>(clo1, chi1, yb[5], rlo, rhi);
       fp4_pair<2>(clo1, chi1, yb[6], rlo, rhi);
       fp4_pair<3>(clo1, chi1, yb[7], rlo, rhi);
-      if (clo0 != chi0 || clo1 != chi1 || exact_block) {
+      if (exact_block) {
         uint32_t c[2] = {0u, 0u};
         for (int j = 0; j < 16; ++j) {
           const uint32_t y16 = (yb[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-          const uint32_t lo = j < 8 ? clo0 : clo1, hi = j < 8 ? chi0 : chi1;
-          const uint32_t nib_lo = (lo >> (4 * (j & 7))) & 15u, nib_hi = (hi >> (4 * (j & 7))) & 15u;
-          const uint32_t code = (nib_lo == nib_hi && !exact_block) ? nib_lo : e2m1_code_exact(y16, S, g);
-          c[j >> 3] |= code << (4 * (j & 7));
+          c[j >> 3] |= e2m1_code_exact(y16, S, g) << (4 * (j & 7));
         }
         clo0 = c[0];
         clo1 = c[1];
+      } else if ((clo0 ^ chi0) | (clo1 ^ chi1)) {
+        // The two bracket codes differ only where |y| / unit lies within the bracket of
+        // an E2M1 rounding boundary: there the code is one of two neighbours, decided
+        // by one exact comparison with that boundary (the other elements keep theirs).
+        uint64_t d = ((uint64_t)(clo1 ^ chi1) << 32) | (clo0 ^ chi0);
+        while (d) {
+          const int j = (int)(__builtin_ctzll(d) >> 2);  // element 0..15
+          d &= ~(0xFull << (4 * j));
+          const uint32_t y16 = (yb[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+          const uint32_t sh = 4 * (j & 7);
+          const uint32_t nl = ((j < 8 ? clo0 : clo1) >> sh) & 15u, nh = ((j < 8 ? chi0 : chi1) >> sh) & 15u;
+          const uint32_t il = nl & 7u, ih = nh & 7u;
+          uint32_t code;
+          if (ih == il + 1u) {
+            code = ((y16 >> 15) << 3) | e2m1_step_exact(y16, S, g, il);
+          } else {
+            code = e2m1_code_exact(y16, S, g);
+          }
+          if (j < 8) clo0 = (clo0 & ~(15u << sh)) | (code << sh);
+          else clo1 = (clo1 & ~(15u << sh)) | (code << sh);
+        }
       }
       if (row < a.m_pad && col < a.k) {
         const u32x2_t v = {clo0, clo1};

@@ -93,8 +93,9 @@ def measured_traffic(summary: str, sources):
 
 def percentiles(xs) -> dict:
     """p10 / p50 / p90 of per-launch durations (ms), nearest-rank."""
+    import math
     v = sorted(xs)
-    pick = lambda q: v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    pick = lambda q: v[min(len(v) - 1, max(0, math.ceil(q * len(v)) - 1))]
     return {"p10": round(pick(0.1), 4), "p50": round(pick(0.5), 4), "p90": round(pick(0.9), 4)}
 
 

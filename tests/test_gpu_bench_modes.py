@@ -1,0 +1,33 @@
+"""The bench's single-kernel modes (the ones the profiler commands run) on the tiny
+workload: each prints one JSON line with its timing fields."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_bench(*args):
+    print(f"[bench] {' '.join(args)}", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "2",
+                        "--warmup", "1", *args], capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout
+    return json.loads(lines[0])
+
+
+def test_only_gemm_with_copy_calibration(gpu):
+    d = run_bench("--only-gemm", "--copy-bytes", str(1 << 24))
+    assert d["gemm_ms"] > 0 and d["copy_bytes"] == 1 << 24 and d["copy_gbs"] > 0
+
+
+def test_only_producer_two_pass_and_single_read(gpu):
+    d2 = run_bench("--only-producer")
+    d1 = run_bench("--only-producer", "--single-read")
+    assert d2["producer_ms"] > 0 and d1["producer_ms"] > 0
+    assert d1["algorithmic_bytes"] < d2["algorithmic_bytes"]

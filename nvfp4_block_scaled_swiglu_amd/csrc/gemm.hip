@@ -590,7 +590,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
     float ymax = 0.0f;
     // Candidates are queued per wave in LDS (past the pipeline stages) as
     // gate | up << 16 and resolved together - their silu lookups in one batch - when
-    // the list fills and at the end of the tile. The count is wave-uniform.
+    // the list could fill and at the end of each scan. The count is wave-uniform.
     uint32_t* clist = (uint32_t*)(smem + kStages * BigTile::StageBytes) + wave * kCand;
     int ccount = 0;
     auto flush = [&]() __attribute__((always_inline)) {

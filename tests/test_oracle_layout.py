@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fc2_footprint.json")))
 
@@ -74,3 +75,70 @@ def test_regression_widths_are_exact_tilings():
     for k in GOLDEN["regression_widths"]["widths"]:
         assert (k // 16) % 4 == 0
         assert oracle.scale_cols(k) == k // 16
+
+
+# ---- the order inside a 128 x 4 tile, derived without the offset formula ----------------
+#
+# The component-2 summary names the layout only ("general 128-row by 4-scale-column
+# tiled offset", key native_pack_validation.fix). The reading taken is the tiled layout
+# documented publicly for block-scaled FP4 operands: the scale grid is cut into tiles of
+# 128 rows x 4 scale columns, stored one after another with the row tiles outermost;
+# inside a tile the 128 rows form 4 groups of 32, and the tile's bytes run over the row
+# within its group (outermost), then the group, then the column (innermost), so that
+# rows i, i+32, i+64, i+96 share one 16-byte chunk. The function below states that
+# storage order as reshapes and one transpose of a grid of element ids, and inverts the
+# resulting permutation; it contains no offset arithmetic of its own.
+
+def tiled_positions(rp: int, cp: int) -> np.ndarray:
+    """pos[r, c]: the byte of the scale buffer that holds scale (r, c)."""
+    ids = np.arange(rp * cp, dtype=np.int64).reshape(rp, cp)
+    # axes: row tile, row group (4), row within group (32), column tile, column (4)
+    cut = ids.reshape(rp // 128, 4, 32, cp // 4, 4)
+    stored = cut.transpose(0, 3, 2, 1, 4).reshape(-1)  # storage order, outermost first
+    pos = np.empty(rp * cp, dtype=np.int64)
+    pos[stored] = np.arange(rp * cp, dtype=np.int64)
+    return pos.reshape(rp, cp)
+
+
+def test_tiled_positions_structure():
+    """Sanity of the derivation itself on one tile: the first bytes of the tile hold row 0
+    columns 0-3, then rows 32, 64, 96; the second 16-byte chunk starts with row 1; the next
+    tile along the columns starts at byte 512."""
+    pos = tiled_positions(128, 8)
+    assert [int(pos[r, c]) for r, c in ((0, 0), (0, 1), (0, 3), (32, 0), (64, 0), (96, 3))] == [0, 1, 3, 4, 8, 15]
+    assert int(pos[1, 0]) == 16 and int(pos[31, 3]) == 31 * 16 + 3 and int(pos[127, 3]) == 511
+    assert int(pos[0, 4]) == 512
+    chunk = sorted(int(pos[r, c]) // 16 for r in (5, 37, 69, 101) for c in range(4))
+    assert chunk == [5] * 16
+
+
+@pytest.mark.parametrize("rows,k", [(256, 1024), (48, 96), (16, 64), (1, 64), (300, 448), (37824, 14336)])
+def test_oracle_swizzle_equals_tiled_positions(rows, k):
+    """The oracle's scale offset (step O8) against the permutation derived above, on
+    every (row, column) of the padded grid (a row sample for the full FC2 grid)."""
+    rp, cp = oracle.scale_rows(rows), oracle.scale_cols(k)
+    pos = tiled_positions(rp, cp)
+    rsel = np.arange(rp) if rp <= 512 else np.unique(np.concatenate(
+        [np.arange(0, 256), np.arange(rp - 256, rp), np.random.default_rng(8).choice(rp, 256, replace=False)]))
+    csel = np.arange(cp) if cp <= 64 else np.unique(np.concatenate(
+        [np.arange(0, 16), np.arange(cp - 16, cp), np.random.default_rng(9).choice(cp, 32, replace=False)]))
+    got = np.array([[oracle.scale_offset(int(r), int(c), cp) for c in csel] for r in rsel], dtype=np.int64)
+    np.testing.assert_array_equal(got, pos[np.ix_(rsel, csel)])
+
+
+def test_oracle_scale_buffer_through_tiled_positions():
+    """The whole scale buffer the oracle writes, read back through the derived layout:
+    every real byte is the block scale of its (row, block) (step O5, pinned separately by
+    brute force), and every byte outside the real rows and columns is zero."""
+    m, k = 200, 448  # padded rows 208 of 256 scale rows; 28 blocks of 28 scale columns
+    x = synth.normal_bf16(m, k, seed=41, tag=9, sigma=1.0)
+    qd, sc, g = oracle.quantize(x)
+    rp, cp = oracle.scale_rows(m), oracle.scale_cols(k)
+    grid = sc[tiled_positions(rp, cp)]
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bmax = np.abs(xf).reshape(m, k // 16, 16).max(axis=2)
+    want = np.zeros((rp, cp), dtype=np.uint8)
+    for r in range(m):
+        for b in range(k // 16):
+            want[r, b] = oracle.block_scale(float(bmax[r, b]), g)
+    np.testing.assert_array_equal(grid, want)

@@ -62,6 +62,7 @@ GEMM_TRAFFIC_SUMMARY = "profiles/gemm_fc2_hbm_traffic.md"
 PRODUCER_SOURCES = ("nvfp4_block_scaled_swiglu_amd/csrc/producer.hip",
                     "nvfp4_block_scaled_swiglu_amd/csrc/common.hpp")
 SINGLE_READ_TRAFFIC_SUMMARY = "profiles/producer_single_read_fc2_hbm_traffic.md"
+PRODUCER_TRAFFIC_SUMMARY = "profiles/producer_fc2_hbm_traffic.md"
 
 
 def measured_gemm_traffic():
@@ -133,10 +134,44 @@ def ceilings(dev, stream) -> dict:
     torch.cuda.synchronize()
     copy_gbs = 2 * n * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
+    stream_gbs = stream_ceilings(dev, stream)
     return {"mfma_f16_tflops": round(best, 1), "mfma_clock_ghz_p50": round(clocks[len(clocks) // 2], 3),
-            "hbm_copy_gbs": round(copy_gbs, 1),
+            "hbm_copy_gbs": round(copy_gbs, 1), **stream_gbs,
             "note": "MFMA-only kernel (4 independent v_mfma_f32_32x32x16_f16 chains per wave, one wave per "
-                    "SIMD), clock from s_memtime over s_memrealtime; copy of 1 GiB, read + write bytes"}
+                    "SIMD), clock from s_memtime over s_memrealtime; copy of 1 GiB, read + write bytes; "
+                    "streaming probe (nvfp4_hbm_stream_ceiling) over 2 GiB reading only, and writing "
+                    f"{QUANT_WRITE_SHARE:.4f} byte per byte read (the quantize launch's mix), read + write bytes"}
+
+
+# bytes the quantize launch writes per byte it reads at the canonical FC2 shape
+# (QDATA + padded scales over gate + up read once)
+QUANT_WRITE_SHARE = (37824 * 14336 // 2 + 37888 * 896) / (2 * 37810 * 14336 * 2)
+
+
+def stream_ceilings(dev, stream) -> dict:
+    """The streaming probe's HBM rate reading 2 GiB alone, and reading 2 GiB while
+    writing the quantize launch's share; best of 5 launches each."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    wbytes = int(nbytes * QUANT_WRITE_SHARE) // 16 * 16
+    dst = torch.empty(wbytes // 4 + 4, dtype=torch.int32, device=dev)
+    out = {}
+    for name, wb in (("hbm_read_only_gbs", 0), ("hbm_read_write_mix_gbs", wbytes)):
+        nv.nvfp4_hbm_stream_ceiling(src, nbytes, dst, wb)
+        torch.cuda.synchronize()
+        best = 0.0
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            written = nv.nvfp4_hbm_stream_ceiling(src, nbytes, dst, wb)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = max(best, (nbytes + written) / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        out[name] = round(best, 1)
+    del src, dst
+    return out
 
 
 def cold_times(run_gemm, run_producer, dev, stream, reps: int) -> dict:
@@ -161,43 +196,77 @@ def cold_times(run_gemm, run_producer, dev, stream, reps: int) -> dict:
     return out
 
 
-def cpu_baseline(w, threads: int) -> dict:
-    """The CPU oracle timed on a bounded sample of the same workload (about 10-15 s
-    of CPU work on 16 cores): the exact GEMM on 16,384 evenly spaced rows (all N
-    columns, full K), scaled to TFLOP/s, and the exact producer over the whole
-    activation. The oracle is an
-    exact-arithmetic correctness reference, not a tuned CPU GEMM."""
+def host_cpu() -> dict:
+    """What the CPU baseline runs on: logical CPUs of this process (nproc), the OS count,
+    and the CPU model name."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return {"nproc": nproc, "os_cpu_count": os.cpu_count(), "cpu_model": model}
+
+
+def baseline_threads() -> int:
+    """Threads for the CPU baseline: nproc, capped by OMP_NUM_THREADS when it is set (the
+    share of the host's cores a one-GPU job gets)."""
+    n = host_cpu()["nproc"]
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(omp))) if omp.isdigit() and int(omp) > 0 else max(1, n)
+
+
+def cpu_baseline(w, threads: int, reps: int = 3) -> dict:
+    """The CPU oracle, as it stands, timed on a bounded sample of the same workload:
+    the exact GEMM on 4,096 evenly spaced rows (all N columns, full K), scaled to
+    TFLOP/s, and the exact producer over the whole activation; the median of `reps`
+    runs each (about 10-20 s of CPU work on 16 threads), plus the GEMM on 128 rows with
+    one thread. The oracle is an exact-arithmetic correctness reference, not a tuned
+    CPU GEMM or quantizer."""
+    import statistics
     import numpy as np
     import oracle
-    rows = min(16384, w.m)
+    rows = min(4096, w.m)
     acts = w.activations(threads=threads)
-    t0 = time.perf_counter()
-    aq, as_, ga = oracle.quantize(acts[0], acts[1] if w.swiglu else None, threads=threads)
-    t_prod = time.perf_counter() - t0
+    t_prod = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        aq, as_, ga = oracle.quantize(acts[0], acts[1] if w.swiglu else None, threads=threads)
+        t_prod.append(time.perf_counter() - t0)
     del acts
     W = w.weight(threads=threads)
     wq, ws, gw = oracle.quantize(W, threads=threads)
     sel = np.arange(rows) * (w.m // rows)
-    t0 = time.perf_counter()
-    oracle.gemm_rows(aq, as_, w.m, ga, wq, ws, w.n, gw, w.k, sel, threads=threads)
-    t_gemm = time.perf_counter() - t0
-    # one thread on a smaller evenly spaced sample
+    t_gemm = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.gemm_rows(aq, as_, w.m, ga, wq, ws, w.n, gw, w.k, sel, threads=threads)
+        t_gemm.append(time.perf_counter() - t0)
     rows1 = min(128, w.m)
     sel1 = np.arange(rows1) * (w.m // rows1)
-    t0 = time.perf_counter()
-    oracle.gemm_rows(aq, as_, w.m, ga, wq, ws, w.n, gw, w.k, sel1, threads=1)
-    t_gemm1 = time.perf_counter() - t0
+    t_gemm1 = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.gemm_rows(aq, as_, w.m, ga, wq, ws, w.n, gw, w.k, sel1, threads=1)
+        t_gemm1.append(time.perf_counter() - t0)
+    tg, tp, tg1 = statistics.median(t_gemm), statistics.median(t_prod), statistics.median(t_gemm1)
     return {
-        "value": 2.0 * rows * w.n * w.k / t_gemm / 1e12,
+        "value": 2.0 * rows * w.n * w.k / tg / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"exact int64 GEMM of {rows} rows (every {w.m // rows}th of {w.m}) x {w.n} x {w.k} "
-                  f"({t_gemm:.2f} s; all {w.m} rows extrapolated: {t_gemm * w.m / rows:.1f} s); exact producer "
-                  f"over all {w.m} x {w.k}: {producer_bytes(w.m, w.k, w.swiglu) / t_prod / 1e9:.3f} GB/s "
-                  f"({t_prod:.2f} s)",
-        "single_thread": {"value": 2.0 * rows1 * w.n * w.k / t_gemm1 / 1e12, "unit": "TFLOP/s",
-                          "sample": f"exact GEMM of {rows1} evenly spaced rows on 1 thread ({t_gemm1:.2f} s)"},
+        "sample": f"median of {reps}: exact int64 GEMM of {rows} rows (every {w.m // rows}th of {w.m}) x {w.n} x "
+                  f"{w.k} ({tg:.2f} s; all {w.m} rows extrapolated: {tg * w.m / rows:.1f} s); exact producer over "
+                  f"all {w.m} x {w.k}: {producer_bytes(w.m, w.k, w.swiglu) / tp / 1e9:.3f} GB/s ({tp:.2f} s)",
+        "host": dict(host_cpu(), threads_used=threads),
+        "note": "the oracle is an exact-arithmetic correctness reference, not a tuned CPU GEMM or quantizer",
+        "single_thread": {"value": 2.0 * rows1 * w.n * w.k / tg1 / 1e12, "unit": "TFLOP/s",
+                          "sample": f"median of {reps}: exact GEMM of {rows1} evenly spaced rows on 1 thread "
+                                    f"({tg1:.2f} s)"},
     }
 
 
@@ -257,12 +326,66 @@ def copy_calibration(nbytes: int, steps: int, dev, stream) -> dict:
     return {"copy_bytes": 4 * n, "copy_ms": round(t_copy, 4), "copy_gbs": round(2 * 4 * n / (t_copy * 1e-3) / 1e9, 1)}
 
 
+def profile_step(w, args, dev) -> int:
+    """The bench's timed step alone: the producer and the GEMM on the workload's seeded
+    inputs (the weight quantized once before), warm-up and timed steps exactly as in the
+    default run, and nothing else launched afterwards except the optional copy
+    calibration. This is the command the profiler traces and counts, so that its
+    per-kernel averages describe the same launches as the bench line's `producer_ms`
+    and `gemm_ms`. Prints one JSON line with the HIP-event averages."""
+    import statistics
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    from tests import parity
+    acts = w.activations()
+    x = parity.to_device_bf16(acts[0], dev)
+    u = parity.to_device_bf16(acts[1], dev) if w.swiglu else None
+    del acts
+    wt = parity.to_device_bf16(w.weight(), dev)
+    a = nv.empty_nvfp4(w.m, w.k, dev)
+    wq = nv.empty_nvfp4(w.n, w.k, dev)
+    d = torch.empty((w.m_pad, w.n), dtype=torch.bfloat16, device=dev)
+    nv.nvfp4_quantize(wt, out=wq)
+    del wt
+    stream = torch.cuda.current_stream()
+
+    def producer():
+        if w.swiglu:
+            nv.nvfp4_quantize_swiglu(x, u, out=a)
+        else:
+            nv.nvfp4_quantize(x, out=a)
+
+    for _ in range(args.warmup):
+        producer()
+        nv.nvfp4_gemm_bf16out(a, wq, out=d)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record(stream)
+        producer()
+        e[1].record(stream)
+        nv.nvfp4_gemm_bf16out(a, wq, out=d)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    t_prod = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs)
+    t_gemm = statistics.fmean(e[1].elapsed_time(e[2]) for e in evs)
+    out = {"mode": "profile-step", "workload": w.name, "steps": args.steps, "warmup": args.warmup,
+           "producer_ms": round(t_prod, 4), "gemm_ms": round(t_gemm, 4),
+           "gemm_tflops": round(w.gemm_flops / (t_gemm * 1e-3) / 1e12, 2),
+           "producer_gbs": round(producer_bytes(w.m, w.k, w.swiglu) / (t_prod * 1e-3) / 1e9, 1),
+           "dispatches_per_kernel": args.warmup + args.steps,
+           "note": "the activation producer is two launches (absmax, then quantize); the weight's plain "
+                   "quantization (one absmax and one quantize launch of the plain kernels) runs once before"}
+    if args.copy_bytes > 0:
+        out.update(copy_calibration(args.copy_bytes, args.steps, dev, stream))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def only_producer(w, args, dev) -> int:
     """Producer-only timing on the workload's seeded inputs (no GEMM in the process).
     With --single-read, the single-read producer alone, with the amax an upstream stage
-    would supply (set up with the library's silu, not timed); it is an ordinary launch,
-    so the profiler can trace and count it (the two-pass producer's cooperative launch
-    ends the profiler)."""
+    would supply (set up with the library's silu, not timed)."""
     import statistics
     import torch
     import nvfp4_block_scaled_swiglu_amd as nv
@@ -488,8 +611,11 @@ def main() -> int:
                     help="time the producer alone on the workload's seeded inputs (no GEMM launch)")
     ap.add_argument("--single-read", action="store_true",
                     help="with --only-producer: time the single-read producer (amax supplied) instead")
+    ap.add_argument("--profile-step", action="store_true",
+                    help="the timed step alone (producer + GEMM), for profiler traces and counter runs")
     ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="with --only-gemm or --only-producer: also run a plain elementwise copy of this many "
+                    help="with --only-gemm, --only-producer or --profile-step: also run a plain elementwise copy "
+                         "of this many "
                          "bytes (read + write), the calibration kernel for the profiler's FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -511,6 +637,8 @@ def main() -> int:
         return only_gemm(w, args, dev)
     if args.only_producer:
         return only_producer(w, args, dev)
+    if args.profile_step:
+        return profile_step(w, args, dev)
     if args.shapes:
         return shapes(args, dev)
     if args.chain:
@@ -670,9 +798,13 @@ def main() -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(prod_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
-            "kernel": "nvfp4::producer_kernel<true>" if w.swiglu else "nvfp4::producer_kernel<false>",
-            "algorithmic_per_launch": f"{pbytes} B (inputs read twice, QDATA + padded scales written)",
+            "traffic": (measured_traffic(PRODUCER_TRAFFIC_SUMMARY, PRODUCER_SOURCES)
+                        if w.name == "fc2_canonical" else None),
+            "traffic_summary": PRODUCER_TRAFFIC_SUMMARY,
+            "kernel": ("nvfp4::producer_absmax_kernel<1> then nvfp4::producer_kernel<1, false>" if w.swiglu else
+                       "nvfp4::producer_absmax_kernel<0> then nvfp4::producer_kernel<0, false>"),
+            "algorithmic_per_launch": f"{pbytes} B per call of its two launches (inputs read twice, QDATA + "
+                                      f"padded scales written)",
             "avg_launch_ms": round(t_prod, 4),
         },
         "producer_single_read": {
@@ -708,7 +840,7 @@ def main() -> int:
         "build": nv.nvfp4_build_info(),
     }
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads = baseline_threads()
         try:
             line["cpu_baseline"] = cpu_baseline(w, threads)
         except Exception as e:  # the baseline is a report, not the product

@@ -65,29 +65,45 @@ int64_t nvfp4_padded_rows(int64_t rows);
  * with scale buffers padded this way. */
 int64_t nvfp4_scale_rows(int64_t rows);
 
-/* Scale columns: roundup(k / 16, 4). */
+/* Scale columns: roundup(k / 16, 4), whole 4-scale-column tiles (component-2
+ * summary, key native_pack_validation.fix: the "128-row by 4-scale-column tiled"
+ * scale offset). Returns -1 if k < 0. */
 int64_t nvfp4_scale_cols(int64_t k);
 
-/* QDATA bytes: nvfp4_padded_rows(rows) * k / 2. */
+/* QDATA bytes: nvfp4_padded_rows(rows) * k / 2, two E2M1 codes per byte over the
+ * padded rows ("FC2 NVFP4 Scheduling Results", "Traffic Attribution": the
+ * activation's one-pass footprint counts the 37,824 descriptor rows). Returns -1 if
+ * rows < 0 or k < 0. */
 int64_t nvfp4_qdata_bytes(int64_t rows, int64_t k);
 
-/* Block-scale buffer bytes: nvfp4_scale_rows(rows) * nvfp4_scale_cols(k). */
+/* Block-scale buffer bytes: nvfp4_scale_rows(rows) * nvfp4_scale_cols(k), one UE4M3
+ * byte per 16 elements in whole 128 x 4 tiles (component-2 summary, keys
+ * native_pack_validation.fix and
+ * intermediate_materialization_bytes_across_four_projections). Returns -1 if
+ * rows < 0 or k < 0. */
 int64_t nvfp4_scale_bytes(int64_t rows, int64_t k);
 
-/* Bytes of the producer workspace (the absmax slot and grid-barrier counters).
- * The caller allocates it on the device, zero-fills it once before the first
- * call, and never touches it afterwards: every producer call leaves it zeroed
- * again when it completes. Calls that may overlap in time (different streams)
- * need distinct workspaces. */
+/* Bytes of the two-pass producers' workspace: one partial absmax slot per
+ * workgroup of the absmax launch, read back by the quantize launch. The
+ * component-2 summary's "conclusion" names the global scale as the dependency
+ * that needs an explicit synchronisation design; this buffer carries it across
+ * the launch boundary. The caller allocates it on the device (16-byte aligned)
+ * and owns it; its contents need no initialisation, since every call writes the
+ * slots it reads. Calls that may overlap in time (different streams) need distinct
+ * workspaces. */
 int64_t nvfp4_quantize_workspace_bytes(void);
 
 /* ---- set-up -------------------------------------------------------------------------- */
 
 /* One-time set-up of the current device: checks that it is gfx950, builds the
  * producer's correctly rounded bf16 silu table in device memory and sizes the
- * producer's persistent grid. Synchronous; safe to call repeatedly and from
- * several threads. Called implicitly by the first producer call on a device;
- * call it explicitly before capturing producer calls into a HIP graph. */
+ * producer's persistent grid. "FC2 NVFP4 Scheduling Results", "Production
+ * Integration": production start-up prepares the extension and caches its
+ * compatibility result before inference; this is that step. Synchronous; safe to
+ * call repeatedly and from several threads. Called implicitly by the first call on
+ * a device (which therefore synchronises once); call it explicitly at start-up, and
+ * before capturing calls into a HIP graph. Errors: NVFP4_ERR_NO_DEVICE (no device,
+ * or not gfx950), NVFP4_ERR_LAUNCH (the silu table build failed). */
 int nvfp4_init(void);
 
 /* ---- stage P: producer ---------------------------------------------------------------- */
@@ -111,8 +127,10 @@ int nvfp4_init(void);
  * Every byte of qdata and scales is written, padding included. Block scale S is
  * the smallest UE4M3 byte with v(S) * 6 * g >= max |y| over its 16 elements; each
  * code is the E2M1 value nearest to |y| / (v(S) * g), ties to the even code, with
- * the sign of y (also on zero). One cooperative launch: absmax pass, grid-wide
- * barrier, pack-and-swizzle pass. Inputs must be finite and keep every
+ * the sign of y (also on zero). Two ordinary launches on `stream`: the absmax pass
+ * writes per-workgroup partial maxima into the workspace, and the
+ * pack-and-swizzle pass reduces them to the global scale (the launch boundary is
+ * the grid-wide synchronisation). Inputs must be finite and keep every
  * |silu(gate) * up| below 2^128.
  */
 int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up,
@@ -120,8 +138,10 @@ int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_
                           float* global_scale_dev, void* workspace_dev, void* stream);
 
 /* Plain NVFP4 quantization of x (y = x): the same contract as
- * nvfp4_quantize_swiglu with one bf16 [rows, k] input of row stride ld_x. Used for
- * the QKV / attention-output / FC1 activations and for weights. */
+ * nvfp4_quantize_swiglu with one bf16 [rows, k] input of row stride ld_x. The
+ * component-2 summary lists this generic producer (absmax_partial, scale_finalize,
+ * block_scale_zero, activation_pack) for the four NVFP4 projections of a block;
+ * used here for the QKV / attention-output / FC1 activations and for weights. */
 int nvfp4_quantize(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k, void* qdata_dev,
                    void* scales_dev, float* global_scale_dev, void* workspace_dev, void* stream);
 
@@ -267,16 +287,41 @@ int nvfp4_silu_bf16(const void* x_dev, void* y_dev, int64_t count, void* stream)
 int64_t nvfp4_mfma_ceiling_out_bytes(int64_t workgroups);
 int nvfp4_mfma_ceiling(int64_t workgroups, int64_t iters, void* out_dev, int64_t out_bytes, void* stream);
 
+/* Not a step of the method: the HBM rate of a plain streaming kernel for a given mix of
+ * reads and writes, the ceiling beside which the producer's two launches are read (the
+ * absmax launch only reads; the quantize launch writes about 0.14 byte per byte read).
+ * A persistent grid reads all read_bytes of src in chunks of
+ * nvfp4_hbm_stream_chunk_bytes() bytes, and chunk c writes dst bytes
+ * [c * w, (c + 1) * w) with w = 16 * floor(write_bytes / 16 / chunks), so
+ * 16 * chunks * floor(write_bytes / (16 * chunks)) bytes are written in all.
+ * src_dev: 16-byte aligned, read_bytes a positive multiple of the chunk size; dst_dev:
+ * 16-byte aligned, at least max(write_bytes, 16) bytes (its first word may be
+ * overwritten even when write_bytes is 0); write_bytes a multiple of 16, at most
+ * read_bytes. Both owned by the caller. Time the call with events on `stream`. */
+int64_t nvfp4_hbm_stream_chunk_bytes(void);
+int nvfp4_hbm_stream_ceiling(const void* src_dev, int64_t read_bytes, void* dst_dev, int64_t write_bytes,
+                             void* stream);
+
 /* ---- diagnostics -------------------------------------------------------------------------- */
 
-/* Static text for a status code. */
+/* Static text for a status code. The statuses are what a caller's guard tests
+ * before falling back ("FC2 NVFP4 Scheduling Results", "Production Integration": a
+ * load, check or execution failure falls back through the already produced NVFP4
+ * bytes, which a failed call leaves untouched). Unknown codes give
+ * "unknown status". */
 const char* nvfp4_status_string(int status);
 
-/* Detail of the last failing call on this host thread ("" if none). */
+/* Detail of the last failing call on this host thread ("" after a successful
+ * call): the failed check, or the HIP error of a refused launch (the failure
+ * record the guards of "Production Integration" keep). The text lives in
+ * thread-local storage until the thread's next call. */
 const char* nvfp4_last_error(void);
 
-/* Compile-time and run-time HIP versions, target architecture and the device
- * the library last initialised, as one line of text. */
+/* Compile-time and run-time HIP versions, target architecture and the current
+ * device's architecture once initialised, as one line of text ("FC2 NVFP4
+ * Scheduling Results", "Production Integration": compile-time versions alone are
+ * not runtime-ABI evidence, so both are recorded). The text lives in thread-local
+ * storage until the thread's next call. */
 const char* nvfp4_build_info(void);
 
 #ifdef __cplusplus

@@ -4,8 +4,10 @@ A thin ctypes layer over the C ABI in ``include/nvfp4.h`` (``libnvfp4.so``, buil
 in-tree by ``build.py``). Every step of the computation runs in the library's HIP
 kernels; this module only marshals torch tensors (device memory) and the current
 torch stream into the C calls, and allocates outputs with torch when the caller
-does not pass them. There is no fallback path: if the library is missing or a
-call fails, an exception is raised.
+does not pass them. There is no fallback computation: if the library is missing,
+the first call raises ImportError; if a call fails it raises (strict, the default)
+or returns None and counts a fallback (non-strict), leaving the caller's buffers as
+they were.
 
 Functions carry the C names:
 
@@ -60,6 +62,8 @@ SIGNATURES = {
     "nvfp4_silu_bf16": (_INT, [_P, _P, _I64, _P]),
     "nvfp4_mfma_ceiling_out_bytes": (_I64, [_I64]),
     "nvfp4_mfma_ceiling": (_INT, [_I64, _I64, _P, _I64, _P]),
+    "nvfp4_hbm_stream_chunk_bytes": (_I64, []),
+    "nvfp4_hbm_stream_ceiling": (_INT, [_P, _I64, _P, _I64, _P]),
     "nvfp4_status_string": (ctypes.c_char_p, [_INT]),
     "nvfp4_last_error": (ctypes.c_char_p, []),
     "nvfp4_build_info": (ctypes.c_char_p, []),
@@ -100,20 +104,51 @@ def _check(rc: int, where: str) -> None:
         raise Nvfp4Error(rc, where, detail)
 
 
-# ---- dispatch counters (attempts / successes / failures per entry point) ----------------
+# ---- dispatch policy and counters --------------------------------------------------------
+#
+# Strict (the default): a failing call raises Nvfp4Error. Non-strict: the call returns
+# None and counts a fallback. The library validates every argument before it enqueues
+# anything, so after a failure every buffer the caller passed, in particular NVFP4
+# bytes already produced, is as it was (the two-pass producer's workspace aside), and
+# the caller can fall back through them without quantizing twice ("FC2 NVFP4
+# Scheduling Results", "Production Integration": fallback through the produced bytes,
+# strict mode on request, dispatch and fallback counts per block). Nothing here
+# computes a result itself. NVFP4_STRICT=0 in the environment starts non-strict;
+# set_strict() changes the default, and each entry point takes strict= per call.
+STRICT = os.environ.get("NVFP4_STRICT", "1") != "0"
+
+# per entry point: attempts, successes, fallbacks (non-strict failures) and failures
+# (strict failures, raised)
 COUNTERS: Dict[str, Dict[str, int]] = {}
+# the status and detail of the most recent fallback per entry point
+LAST_FALLBACK: Dict[str, Tuple[int, str]] = {}
 
 
-def _count(name: str, ok: bool) -> None:
-    c = COUNTERS.setdefault(name, {"attempts": 0, "successes": 0, "failures": 0})
-    c["attempts"] += 1
-    c["successes" if ok else "failures"] += 1
+def set_strict(flag: bool) -> None:
+    global STRICT
+    STRICT = bool(flag)
 
 
-def _call(name: str, *args) -> None:
+def dispatch_counters() -> Dict[str, Dict[str, int]]:
+    """A copy of the per-entry-point counters."""
+    return {k: dict(v) for k, v in COUNTERS.items()}
+
+
+def _call(name: str, *args, strict: Optional[bool] = None) -> bool:
+    """Call entry point `name`; True on success. On failure raise (strict) or count a
+    fallback and return False (non-strict)."""
     rc = getattr(lib(), name)(*args)
-    _count(name, rc == NVFP4_OK)
-    _check(rc, name)
+    c = COUNTERS.setdefault(name, {"attempts": 0, "successes": 0, "fallbacks": 0, "failures": 0})
+    c["attempts"] += 1
+    if rc == NVFP4_OK:
+        c["successes"] += 1
+        return True
+    if STRICT if strict is None else strict:
+        c["failures"] += 1
+        _check(rc, name)
+    c["fallbacks"] += 1
+    LAST_FALLBACK[name] = (rc, lib().nvfp4_last_error().decode(errors="replace"))
+    return False
 
 
 # ---- sizes ---------------------------------------------------------------------------------
@@ -170,7 +205,7 @@ class Nvfp4Tensor:
         return nvfp4_padded_rows(self.rows)
 
 
-def empty_nvfp4(rows: int, k: int, device) -> Nvfp4Tensor:
+def empty_nvfp4(rows: int, k: int, device) -> Optional[Nvfp4Tensor]:
     import torch
     return Nvfp4Tensor(
         qdata=torch.empty((nvfp4_padded_rows(rows), k // 2), dtype=torch.uint8, device=device),
@@ -183,13 +218,13 @@ _workspaces: Dict[Tuple[int, int], "torch.Tensor"] = {}
 
 
 def _workspace(device, stream_handle: int):
-    """A zeroed producer workspace per (device, stream); the kernel leaves it zeroed."""
+    """A producer workspace per (device, stream), so that calls on different streams
+    never share one (its contents need no initialisation)."""
     import torch
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
     ws = _workspaces.get(key)
     if ws is None:
-        ws = torch.zeros((nvfp4_quantize_workspace_bytes(),), dtype=torch.uint8, device=device)
-        torch.cuda.synchronize(device)
+        ws = torch.empty((nvfp4_quantize_workspace_bytes(),), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -210,7 +245,7 @@ def _bf16_2d(t, name: str):
 
 
 def nvfp4_quantize_swiglu(gate, up, out: Optional[Nvfp4Tensor] = None, m: Optional[int] = None,
-                          workspace=None, stream=None) -> Nvfp4Tensor:
+                          workspace=None, stream=None, strict: Optional[bool] = None) -> Optional[Nvfp4Tensor]:
     """Fused y = RN_bf16(silu_bf16(gate) * up) -> NVFP4 (QDATA, 128x4-tiled scales, global scale)."""
     _bf16_2d(gate, "gate")
     _bf16_2d(up, "up")
@@ -221,13 +256,15 @@ def nvfp4_quantize_swiglu(gate, up, out: Optional[Nvfp4Tensor] = None, m: Option
     out = empty_nvfp4(m, k, gate.device) if out is None else out
     sh = _stream_handle(stream)
     ws = _workspace(gate.device, sh) if workspace is None else workspace
-    _call("nvfp4_quantize_swiglu", gate.data_ptr(), gate.stride(0), up.data_ptr(), up.stride(0), m, k,
-          out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(), sh)
+    if not _call("nvfp4_quantize_swiglu", gate.data_ptr(), gate.stride(0), up.data_ptr(), up.stride(0), m, k,
+                 out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(), sh,
+                 strict=strict):
+        return None
     return out
 
 
 def nvfp4_quantize(x, out: Optional[Nvfp4Tensor] = None, rows: Optional[int] = None, workspace=None,
-                   stream=None) -> Nvfp4Tensor:
+                   stream=None, strict: Optional[bool] = None) -> Optional[Nvfp4Tensor]:
     """Plain NVFP4 quantization of a bf16 [rows, k] tensor (y = x)."""
     _bf16_2d(x, "x")
     rows = x.shape[0] if rows is None else rows
@@ -235,13 +272,15 @@ def nvfp4_quantize(x, out: Optional[Nvfp4Tensor] = None, rows: Optional[int] = N
     out = empty_nvfp4(rows, k, x.device) if out is None else out
     sh = _stream_handle(stream)
     ws = _workspace(x.device, sh) if workspace is None else workspace
-    _call("nvfp4_quantize", x.data_ptr(), x.stride(0), rows, k, out.qdata.data_ptr(), out.scales.data_ptr(),
-          out.global_scale.data_ptr(), ws.data_ptr(), sh)
+    if not _call("nvfp4_quantize", x.data_ptr(), x.stride(0), rows, k, out.qdata.data_ptr(), out.scales.data_ptr(),
+                 out.global_scale.data_ptr(), ws.data_ptr(), sh,
+                 strict=strict):
+        return None
     return out
 
 
 def nvfp4_quantize_modulate(x, scale, shift, out: Optional[Nvfp4Tensor] = None, rows: Optional[int] = None,
-                            workspace=None, stream=None) -> Nvfp4Tensor:
+                            workspace=None, stream=None, strict: Optional[bool] = None) -> Optional[Nvfp4Tensor]:
     """NVFP4 of y = RN_bf16(fma_fp32(x, 1 + scale, shift)) (scale, shift: bf16 [k])."""
     import torch
     _bf16_2d(x, "x")
@@ -253,8 +292,10 @@ def nvfp4_quantize_modulate(x, scale, shift, out: Optional[Nvfp4Tensor] = None, 
     out = empty_nvfp4(rows, k, x.device) if out is None else out
     sh = _stream_handle(stream)
     ws = _workspace(x.device, sh) if workspace is None else workspace
-    _call("nvfp4_quantize_modulate", x.data_ptr(), x.stride(0), rows, k, scale.data_ptr(), shift.data_ptr(),
-          out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(), sh)
+    if not _call("nvfp4_quantize_modulate", x.data_ptr(), x.stride(0), rows, k, scale.data_ptr(), shift.data_ptr(),
+                 out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(), sh,
+                 strict=strict):
+        return None
     return out
 
 
@@ -266,7 +307,7 @@ def _amax_ptr(amax) -> int:
 
 
 def nvfp4_quantize_swiglu_amax(gate, up, amax, out: Optional[Nvfp4Tensor] = None, m: Optional[int] = None,
-                               stream=None) -> Nvfp4Tensor:
+                               stream=None, strict: Optional[bool] = None) -> Optional[Nvfp4Tensor]:
     """Single-read SwiGLU -> NVFP4 with the caller's tensor amax (a device float32 scalar)."""
     _bf16_2d(gate, "gate")
     _bf16_2d(up, "up")
@@ -275,25 +316,27 @@ def nvfp4_quantize_swiglu_amax(gate, up, amax, out: Optional[Nvfp4Tensor] = None
     if up.shape[1] != k or up.shape[0] < m or gate.shape[0] < m:
         raise ValueError("gate/up shapes disagree")
     out = empty_nvfp4(m, k, gate.device) if out is None else out
-    _call("nvfp4_quantize_swiglu_amax", gate.data_ptr(), gate.stride(0), up.data_ptr(), up.stride(0), m, k,
-          _amax_ptr(amax), out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(),
-          _stream_handle(stream))
+    if not _call("nvfp4_quantize_swiglu_amax", gate.data_ptr(), gate.stride(0), up.data_ptr(), up.stride(0), m, k,
+                 _amax_ptr(amax), out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(),
+                 _stream_handle(stream), strict=strict):
+        return None
     return out
 
 
 def nvfp4_quantize_amax(x, amax, out: Optional[Nvfp4Tensor] = None, rows: Optional[int] = None,
-                        stream=None) -> Nvfp4Tensor:
+                        stream=None, strict: Optional[bool] = None) -> Optional[Nvfp4Tensor]:
     """Single-read plain NVFP4 quantization with the caller's tensor amax."""
     _bf16_2d(x, "x")
     rows = x.shape[0] if rows is None else rows
     k = x.shape[1]
     out = empty_nvfp4(rows, k, x.device) if out is None else out
-    _call("nvfp4_quantize_amax", x.data_ptr(), x.stride(0), rows, k, _amax_ptr(amax), out.qdata.data_ptr(),
-          out.scales.data_ptr(), out.global_scale.data_ptr(), _stream_handle(stream))
+    if not _call("nvfp4_quantize_amax", x.data_ptr(), x.stride(0), rows, k, _amax_ptr(amax), out.qdata.data_ptr(),
+                 out.scales.data_ptr(), out.global_scale.data_ptr(), _stream_handle(stream), strict=strict):
+        return None
     return out
 
 
-def nvfp4_gemm_bf16out(a: Nvfp4Tensor, w: Nvfp4Tensor, out=None, stream=None):
+def nvfp4_gemm_bf16out(a: Nvfp4Tensor, w: Nvfp4Tensor, out=None, stream=None, strict: Optional[bool] = None):
     """D[m_padded, n] = RN_bf16(g_a g_w sum_k deq(A) deq(W)), FP32 accumulation."""
     import torch
     if a.k != w.k:
@@ -304,14 +347,15 @@ def nvfp4_gemm_bf16out(a: Nvfp4Tensor, w: Nvfp4Tensor, out=None, stream=None):
         out = torch.empty((m_pad, n), dtype=torch.bfloat16, device=a.qdata.device)
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != (m_pad, n) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bfloat16 [m_padded, n] tensor")
-    _call("nvfp4_gemm_bf16out", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
-          w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), out.data_ptr(), m_pad, n, a.k,
-          _stream_handle(stream))
+    if not _call("nvfp4_gemm_bf16out", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
+                 w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), out.data_ptr(), m_pad, n, a.k,
+                 _stream_handle(stream), strict=strict):
+        return None
     return out
 
 
 def nvfp4_gemm_bf16out_fused(a: Nvfp4Tensor, w: Nvfp4Tensor, bias=None, gate=None, residual=None, out=None,
-                             stream=None):
+                             stream=None, strict: Optional[bool] = None):
     """D = RN_bf16(residual + gate * RN_bf16(g_a g_w sum + bias)) (each term optional;
     without a residual D is the biased GEMM output). out may be residual (in place)."""
     import torch
@@ -327,9 +371,10 @@ def nvfp4_gemm_bf16out_fused(a: Nvfp4Tensor, w: Nvfp4Tensor, bias=None, gate=Non
         if t is not None and (t.dtype != torch.bfloat16 or tuple(t.shape) != shape or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous bfloat16 tensor of shape {shape}")
     ptr = lambda t: None if t is None else t.data_ptr()
-    _call("nvfp4_gemm_bf16out_fused", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
-          w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), out.data_ptr(), m_pad, n, a.k,
-          ptr(bias), ptr(gate), ptr(residual), _stream_handle(stream))
+    if not _call("nvfp4_gemm_bf16out_fused", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
+                 w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), out.data_ptr(), m_pad, n, a.k,
+                 ptr(bias), ptr(gate), ptr(residual), _stream_handle(stream), strict=strict):
+        return None
     return out
 
 
@@ -349,7 +394,7 @@ def _torch_stack_chunks(a, b):
 
 
 def nvfp4_gemm_swiglu_pair(a: Nvfp4Tensor, w: Nvfp4Tensor, bias=None, amax=None, amax_rows: Optional[int] = None,
-                           gate_out=None, up_out=None, stream=None):
+                           gate_out=None, up_out=None, stream=None, strict: Optional[bool] = None):
     """FC1 with the SwiGLU pair epilogue: returns (gate, up) bf16 [m_padded, n_half];
     if amax (a float32 CUDA tensor, set by the caller) is given, max |silu(gate) * up|
     over the logical rows is folded into it."""
@@ -366,11 +411,12 @@ def nvfp4_gemm_swiglu_pair(a: Nvfp4Tensor, w: Nvfp4Tensor, bias=None, amax=None,
             raise ValueError(f"{name} must be a contiguous bfloat16 [m_padded, n_half] tensor")
     if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (2 * n_half,)):
         raise ValueError("bias must be bfloat16 [2 n_half] (interleaved order)")
-    _call("nvfp4_gemm_swiglu_pair", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
-          w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), gate_out.data_ptr(),
-          up_out.data_ptr(), m_pad, n_half, a.k, None if bias is None else bias.data_ptr(),
-          None if amax is None else _amax_ptr(amax), a.rows if amax_rows is None else amax_rows,
-          _stream_handle(stream))
+    if not _call("nvfp4_gemm_swiglu_pair", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
+                 w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), gate_out.data_ptr(),
+                 up_out.data_ptr(), m_pad, n_half, a.k, None if bias is None else bias.data_ptr(),
+                 None if amax is None else _amax_ptr(amax), a.rows if amax_rows is None else amax_rows,
+                 _stream_handle(stream), strict=strict):
+        return None
     return gate_out, up_out
 
 
@@ -384,6 +430,19 @@ def nvfp4_mfma_ceiling(workgroups: int, iters: int, stream=None):
     out = torch.zeros((max(nbytes, 16) // 8,), dtype=torch.int64, device=torch.cuda.current_device())
     _call("nvfp4_mfma_ceiling", workgroups, iters, out.data_ptr(), nbytes, _stream_handle(stream))
     return out.view(-1, 2)
+
+
+def nvfp4_hbm_stream_ceiling(src, read_bytes: int, dst, write_bytes: int, stream=None) -> int:
+    """Run the HBM streaming probe once (a measurement aid, not a step of the method):
+    read read_bytes of the CUDA tensor src, write about write_bytes of dst. Returns the
+    bytes actually written; time the call with events for the rate."""
+    chunk = int(lib().nvfp4_hbm_stream_chunk_bytes())
+    if src.numel() * src.element_size() < read_bytes or dst.numel() * dst.element_size() < max(write_bytes, 16):
+        raise ValueError("src or dst smaller than the requested bytes")
+    _call("nvfp4_hbm_stream_ceiling", src.data_ptr(), read_bytes, dst.data_ptr(), write_bytes,
+          _stream_handle(stream))
+    chunks = read_bytes // chunk
+    return 16 * chunks * (write_bytes // (16 * chunks))
 
 
 def nvfp4_silu_bf16(x, out=None, stream=None):

@@ -6,6 +6,7 @@
 // per-thread message for nvfp4_last_error().
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -21,6 +22,7 @@ hipError_t launch_silu_apply(const uint16_t* x, uint16_t* y, int64_t n, hipStrea
 // producer modes: 0 plain, 1 SwiGLU, 2 modulated plain
 size_t producer_smem_bytes(int mode);
 const void* producer_kernel_ptr(int mode, bool given);
+const void* producer_absmax_kernel_ptr(int mode);
 int producer_block_threads();
 hipError_t launch_producer(int mode, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
                            const uint16_t* mod_scale, const uint16_t* mod_shift, int64_t m, int64_t k,
@@ -32,6 +34,9 @@ hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, co
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
                        const GemmEpilogue& ep, int cu_count, hipStream_t stream);
 hipError_t launch_mfma_ceiling(uint64_t* out, int64_t workgroups, int64_t iters, hipStream_t stream);
+hipError_t launch_hbm_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, int workgroups,
+                             hipStream_t stream);
+int64_t hbm_stream_chunk_bytes();
 }  // namespace nvfp4
 
 namespace {
@@ -39,8 +44,11 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;  // 32-bit buffer offsets in the kernels
 
+// A device's set-up. `ready` is published with release order after every other
+// field is written (under g_init_mutex) and read with acquire order, so a thread that
+// sees it set also sees the finished state without taking the lock.
 struct DeviceState {
-  bool ready = false;
+  std::atomic<bool> ready{false};
   const uint16_t* silu_table = nullptr;
   int producer_blocks[3] = {0, 0, 0};  // persistent grid per producer mode
   int cu_count = 0;
@@ -50,7 +58,7 @@ struct DeviceState {
 DeviceState g_dev[kMaxDevices];
 std::mutex g_init_mutex;
 thread_local char t_last_error[512] = "";
-char g_build_info[512] = "";
+thread_local char t_build_info[512] = "";
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -74,12 +82,12 @@ int ensure_device(DeviceState** out) {
   if (e != hipSuccess || dev < 0) return fail(NVFP4_ERR_NO_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
   if (dev >= kMaxDevices) return fail(NVFP4_ERR_NO_DEVICE, "device index %d out of range", dev);
   DeviceState& st = g_dev[dev];
-  if (st.ready) {
+  if (st.ready.load(std::memory_order_acquire)) {
     *out = &st;
     return NVFP4_OK;
   }
   std::lock_guard<std::mutex> lock(g_init_mutex);
-  if (st.ready) {
+  if (st.ready.load(std::memory_order_relaxed)) {
     *out = &st;
     return NVFP4_OK;
   }
@@ -90,7 +98,6 @@ int ensure_device(DeviceState** out) {
     return fail(NVFP4_ERR_NO_DEVICE, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
   snprintf(st.arch, sizeof(st.arch), "%s", prop.gcnArchName);
   st.cu_count = prop.multiProcessorCount;
-  if (!prop.cooperativeLaunch) return fail(NVFP4_ERR_NO_DEVICE, "device %d lacks cooperative launch", dev);
 
   // kernels with more than 64 KiB of dynamic LDS must opt in
   for (int mode = 0; mode < 3; ++mode) {
@@ -99,6 +106,9 @@ int ensure_device(DeviceState** out) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)nvfp4::producer_smem_bytes(mode));
       if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer LDS attribute: %s", hipGetErrorString(e));
     }
+    e = hipFuncSetAttribute(nvfp4::producer_absmax_kernel_ptr(mode), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)nvfp4::producer_smem_bytes(mode));
+    if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "absmax LDS attribute: %s", hipGetErrorString(e));
     int per_cu = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nvfp4::producer_kernel_ptr(mode, false),
                                                      nvfp4::producer_block_threads(),
@@ -106,6 +116,7 @@ int ensure_device(DeviceState** out) {
     if (e != hipSuccess || per_cu < 1)
       return fail(NVFP4_ERR_LAUNCH, "producer occupancy query: %s (%d)", hipGetErrorString(e), per_cu);
     st.producer_blocks[mode] = per_cu * st.cu_count;
+    if (st.producer_blocks[mode] > nvfp4::kMaxPartials) st.producer_blocks[mode] = nvfp4::kMaxPartials;
   }
   for (int kind = 0; kind < 3; ++kind) {
     e = hipFuncSetAttribute(nvfp4::gemm_kernel_ptr(kind), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -123,7 +134,7 @@ int ensure_device(DeviceState** out) {
   (void)hipStreamDestroy(s);
   if (e != hipSuccess || e2 != hipSuccess)
     return fail(NVFP4_ERR_LAUNCH, "silu table init: %s / %s", hipGetErrorString(e), hipGetErrorString(e2));
-  st.ready = true;
+  st.ready.store(true, std::memory_order_release);
   *out = &st;
   return NVFP4_OK;
 }
@@ -338,6 +349,26 @@ int nvfp4_mfma_ceiling(int64_t workgroups, int64_t iters, void* out_dev, int64_t
   return ok();
 }
 
+int64_t nvfp4_hbm_stream_chunk_bytes(void) { return nvfp4::hbm_stream_chunk_bytes(); }
+
+int nvfp4_hbm_stream_ceiling(const void* src_dev, int64_t read_bytes, void* dst_dev, int64_t write_bytes,
+                             void* stream) {
+  const int64_t chunk = nvfp4::hbm_stream_chunk_bytes();
+  if (!src_dev || !dst_dev) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (read_bytes <= 0 || read_bytes % chunk != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "read_bytes must be a positive multiple of %lld", (long long)chunk);
+  if (write_bytes < 0 || write_bytes > read_bytes || write_bytes % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "write_bytes must be a multiple of 16 in [0, read_bytes]");
+  if (!aligned16(src_dev) || !aligned16(dst_dev)) return fail(NVFP4_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  DeviceState* st = nullptr;
+  int rc = ensure_device(&st);
+  if (rc != NVFP4_OK) return rc;
+  hipError_t e = nvfp4::launch_hbm_stream(src_dev, read_bytes, dst_dev, write_bytes, st->cu_count * 8,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "stream probe launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";
@@ -359,11 +390,13 @@ const char* nvfp4_build_info(void) {
   (void)hipDriverGetVersion(&drv);
   int dev = -1;
   const char* arch = "";
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices && g_dev[dev].ready) arch = g_dev[dev].arch;
-  snprintf(g_build_info, sizeof(g_build_info),
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices &&
+      g_dev[dev].ready.load(std::memory_order_acquire))
+    arch = g_dev[dev].arch;
+  snprintf(t_build_info, sizeof(t_build_info),
            "nvfp4 gfx950; HIP compile %d.%d.%d; HIP runtime %d; driver %d; device arch %s", HIP_VERSION_MAJOR,
            HIP_VERSION_MINOR, HIP_VERSION_PATCH, rt, drv, arch[0] ? arch : "(not initialised)");
-  return g_build_info;
+  return t_build_info;
 }
 
 }  // extern "C"

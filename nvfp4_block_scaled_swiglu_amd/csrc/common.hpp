@@ -19,17 +19,15 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
-// Workspace of the producer: the tensor absmax (fp32 bits of a non-negative
-// bf16 value, so unsigned order is value order) and the grid-barrier counters.
-// All three are zero between calls.
-// Producer workspace: zero between calls (each launch returns it to zero).
+// Workspace of the two-pass producer: one partial maximum per absmax-pass
+// workgroup (fp32 bits of a non-negative bf16 value, so unsigned order is value
+// order). The absmax launch writes every slot the quantize launch then reads, so
+// the contents never need initialising.
+constexpr int kMaxPartials = 1024;
 struct ProducerWorkspace {
-  uint32_t amax_bits;  // max |y| (fp32 bits) over the grid
-  uint32_t arrived;    // grid barrier after pass 1
-  uint32_t departed;
-  uint32_t pad[61];
+  uint32_t partial[kMaxPartials];
 };
-static_assert(sizeof(ProducerWorkspace) == 256, "workspace layout");
+static_assert(sizeof(ProducerWorkspace) == 4096, "workspace layout");
 
 // What the GEMM does after its K loop (host -> launch_gemm).
 //   kind 0: D = RN_bf16(alpha * acc)

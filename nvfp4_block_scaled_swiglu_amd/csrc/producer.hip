@@ -16,18 +16,22 @@
 //   QDATA   = two codes per byte (even element low), rows [m, m_pad) zero
 //   scales  = 512-byte tiles of 128 rows x 4 scale columns, padding zero
 //
-// Structure: a persistent grid (co-resident through a cooperative launch, one
-// 16-wave workgroup per CU, the bf16 SiLU table in LDS) walks work items of 64 rows
-// x 512 columns; each lane owns one 16-element block of a row per step (a wave
-// covers 2 rows x 32 blocks). Pass 1 reduces |y| with the next item's loads in
-// flight (wavefront shuffles, LDS across waves, one agent-scope atomic max per
-// workgroup); a grid barrier publishes amax; pass 2 walks the items in reverse order
-// (so the rows read last in pass 1, still in the memory-side cache, are read first),
-// recomputes y, and stores QDATA rows (32 lanes store one full 256-byte row segment)
-// and each scale byte at its place in its 512-byte tile. Pass 2 has no workgroup
-// barrier, so the 16 waves drift apart and hide each other's load latency. With
-// GIVEN (amax from the caller) pass 1 and the barrier are compiled out and the
-// launch is an ordinary one: every input byte is read once.
+// Structure: two ordinary launches on the caller's stream. Each runs a persistent
+// grid (one 16-wave workgroup per CU, the bf16 SiLU table in LDS) over work items of
+// 64 rows x 512 columns; each lane owns one 16-element block of a row per step (a wave
+// covers 2 rows x 32 blocks).
+//  - The absmax launch reduces |y| with the next item's loads in flight (wavefront
+//    shuffles, then LDS across waves) and writes one partial maximum per workgroup
+//    into the caller's workspace.
+//  - The kernel boundary is the grid-wide synchronisation the global scale needs.
+//  - The quantize launch reduces the partials to amax, derives g, walks the items in
+//    reverse order (so the rows the absmax launch read last, still in the memory-side
+//    cache, are read first), recomputes y, and stores QDATA rows (32 lanes store one
+//    full 256-byte row segment) and each scale byte at its place in its 512-byte
+//    tile. It has no workgroup barrier, so the 16 waves drift apart and hide each
+//    other's load latency.
+// With GIVEN (amax from the caller) only the quantize launch runs: every input byte
+// is read once.
 //
 // Exactness: every rounding decision equals the exact one.
 //  - y: a product of two bf16 values is exact in fp32 when it is >= 2^-126; a block
@@ -56,7 +60,7 @@ constexpr int kLanesPerRow = kItemCols / 16;
 constexpr int kWaveRows = 64 / kLanesPerRow;
 constexpr int kRowsPerStep = kWaves * kWaveRows;
 constexpr int kItemRows = 2 * kRowsPerStep;
-constexpr int kRedBytes = 128;       // wave maxima and two broadcast slots
+constexpr int kRedBytes = 128;       // wave maxima and a broadcast slot
 constexpr int kSteps = kItemRows / kRowsPerStep;
 
 struct ProducerArgs {
@@ -66,14 +70,15 @@ struct ProducerArgs {
   int64_t m, k, m_pad;
   int64_t cpad;       // scale columns
   int items_m;        // scale row-tiles
-  int items_k;        // 256-column segments
+  int items_k;        // 512-column segments
   uint8_t* qdata;
   uint8_t* scales;
   float* gout;
   const float* amax_in;  // caller-supplied amax (single-pass variant), else unused
   const uint16_t* mod_scale;  // modulation scale and shift, bf16 [k] (MODE kModulate)
   const uint16_t* mod_shift;
-  ProducerWorkspace* ws;
+  uint32_t* partials;  // absmax launch: one slot per workgroup (the caller's workspace)
+  int npart;           // quantize launch: slots to reduce (the absmax launch's grid)
   const uint16_t* silu_table;
 };
 
@@ -272,13 +277,170 @@ __device__ __forceinline__ void block_mag_range(const uint32_t (&yb)[8], uint32_
   mn = lo.x < lo.y ? lo.x : lo.y;
 }
 
-// GIVEN: the tensor amax comes from the caller (a device float); pass 1 and the grid
-// barrier are skipped and the launch needs no co-residency.
+// The 16 bf16 values of this lane's block in each step of an item (zero outside the
+// logical rows and columns). For kModulate the up slots carry the item's modulation
+// instead: uv[0] = the scale and uv[1] = the shift of the lane's 16 columns.
+static_assert(kSteps == 2, "modulation vectors ride in the two up slots");
+template <int MODE>
+__device__ __forceinline__ void load_item(const ProducerArgs& a, int item, int wave, int r4, int blk,
+                                          u32x4_t (&gv)[kSteps][2], u32x4_t (&uv)[kSteps][2]) {
+  const int rt = item / a.items_k, kt = item - rt * a.items_k;
+  const int64_t col = (int64_t)kt * kItemCols + blk * 16;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  if (MODE == kModulate) {
+    const bool cok = col < a.k;
+    const u32x4_t* ps = (const u32x4_t*)(a.mod_scale + col);
+    const u32x4_t* pb = (const u32x4_t*)(a.mod_shift + col);
+    uv[0][0] = cok ? ps[0] : z;
+    uv[0][1] = cok ? ps[1] : z;
+    uv[1][0] = cok ? pb[0] : z;
+    uv[1][1] = cok ? pb[1] : z;
+  }
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int64_t row = (int64_t)rt * kItemRows + s * kRowsPerStep + wave * kWaveRows + r4;
+    const bool ok = row < a.m && col < a.k;
+    const u32x4_t* px = (const u32x4_t*)(a.x + row * a.ldx + col);
+    gv[s][0] = ok ? px[0] : z;
+    gv[s][1] = ok ? px[1] : z;
+    if (MODE == kSwiglu) {
+      const u32x4_t* pu = (const u32x4_t*)(a.u + row * a.ldu + col);
+      uv[s][0] = ok ? pu[0] : z;
+      uv[s][1] = ok ? pu[1] : z;
+    }
+  }
+}
+
+// The bf16 silu table into LDS (SwiGLU only).
+__device__ __forceinline__ void stage_silu_table(const uint16_t* src_tab, uint16_t* tab, int tid) {
+  const u32x4_t* src = (const u32x4_t*)src_tab;
+  u32x4_t* dst = (u32x4_t*)tab;
+  for (int i = tid; i < 65536 * 2 / 16; i += kProdThreads) dst[i] = src[i];
+  __syncthreads();
+}
+
+// Workgroup maximum of v (unsigned), returned to every thread. Uses red[0 .. kWaves].
+__device__ __forceinline__ uint32_t workgroup_max_u32(uint32_t v, uint32_t* red, int tid) {
+  const uint32_t wmax = wave_max_u32(v);
+  if ((tid & 63) == 0) red[tid >> 6] = wmax;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < kWaves; ++i) r = red[i] > r ? red[i] : r;
+    red[kWaves] = r;
+  }
+  __syncthreads();
+  const uint32_t r = red[kWaves];
+  __syncthreads();
+  return r;
+}
+
+// ---- pass 1: the tensor absmax ------------------------------------------------------------------
+//
+// Each workgroup reduces max |y| over its items (every gridDim.x-th item, the next
+// item's loads in flight while the current one is reduced) and writes it to its own
+// slot of the workspace: the bits of a bf16 magnitude shifted into fp32 position.
+// The quantize launch that follows on the same stream reduces the slots; the kernel
+// boundary between the two launches is the grid-wide synchronisation the global
+// scale needs.
+template <int MODE>
+__global__ void __launch_bounds__(kProdThreads) producer_absmax_kernel(ProducerArgs a) {
+  constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint32_t* red = (uint32_t*)smem;
+  uint16_t* tab = (uint16_t*)(smem + kRedBytes);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r4 = lane / kLanesPerRow;
+  const int blk = lane % kLanesPerRow;
+  const int nitems = a.items_m * a.items_k;
+  if (SWIGLU) stage_silu_table(a.silu_table, tab, tid);
+
+  uint32_t local_bits = 0;  // fp32 bits of a non-negative value
+  // rows past m read zeros; only the modulation would turn them into nonzero y
+  auto absmax_item = [&](int item, const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
+    const int64_t row0 = (int64_t)(item / a.items_k) * kItemRows + wave * kWaveRows + r4;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      if (MOD && row0 + s * kRowsPerStep >= a.m) continue;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const uint32_t gw = gv[s][w >> 2][w & 3];
+        if (MOD) {
+          const uint32_t sw = uv[0][w >> 2][w & 3], bw = uv[1][w >> 2][w & 3];
+          const float p0 = fabsf(modulate_f32(gw & 0xFFFFu, sw & 0xFFFFu, bw & 0xFFFFu));
+          const float p1 = fabsf(modulate_f32(gw >> 16, sw >> 16, bw >> 16));
+          const uint32_t b = __float_as_uint(fmaxf(p0, p1));
+          local_bits = b > local_bits ? b : local_bits;
+        } else if (SWIGLU) {
+          const uint32_t uw = uv[s][w >> 2][w & 3];
+          const float s0 = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16);
+          const float s1 = __uint_as_float((uint32_t)tab[gw >> 16] << 16);
+          const float p0 = fabsf(s0 * __uint_as_float(uw << 16));
+          const float p1 = fabsf(s1 * __uint_as_float(uw & 0xFFFF0000u));
+          const uint32_t b = __float_as_uint(fmaxf(p0, p1));
+          local_bits = b > local_bits ? b : local_bits;
+        } else {
+          const uint32_t m0 = gw & 0x7FFFu, m1 = (gw >> 16) & 0x7FFFu;
+          const uint32_t b = (m0 > m1 ? m0 : m1) << 16;
+          local_bits = b > local_bits ? b : local_bits;
+        }
+      }
+    }
+  };
+  {
+    u32x4_t gA[kSteps][2], uA[kSteps][2], gB[kSteps][2], uB[kSteps][2];
+    int item = blockIdx.x;
+    if (item < nitems) load_item<MODE>(a, item, wave, r4, blk, gA, uA);
+    while (item < nitems) {
+      const int n1 = item + (int)gridDim.x;
+      if (n1 < nitems) load_item<MODE>(a, n1, wave, r4, blk, gB, uB);
+      absmax_item(item, gA, uA);
+      item = n1;
+      if (item >= nitems) break;
+      const int n2 = item + (int)gridDim.x;
+      if (n2 < nitems) load_item<MODE>(a, n2, wave, r4, blk, gA, uA);
+      absmax_item(item, gB, uB);
+      item = n2;
+    }
+  }
+  // workgroup max of the unrounded |products| (SwiGLU) or of |x|
+  local_bits = workgroup_max_u32(local_bits, red, tid);
+  // A product below 2^-126 may have been rounded in fp32; if this workgroup's maximum
+  // is such a product, redo its elements exactly (never taken for inputs whose absmax
+  // is a normal number).
+  if (SWIGLU && local_bits != 0 && local_bits < 0x00800000u) {
+    uint32_t best = 0;  // bf16 magnitude bits
+    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+      u32x4_t gv[kSteps][2], uv[kSteps][2];
+      load_item<MODE>(a, item, wave, r4, blk, gv, uv);
+      for (int s = 0; s < kSteps; ++s)
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t g16 = (gv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
+          const uint32_t u16 = (uv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
+          const double p = (double)bf16_bits_to_float(tab[g16]) * (double)bf16_bits_to_float(u16);
+          const uint32_t y = rn_bf16_from_double(p) & 0x7FFFu;
+          best = y > best ? y : best;
+        }
+    }
+    local_bits = workgroup_max_u32(best, red, tid) << 16;
+  } else if (SWIGLU || MOD) {
+    // RN_bf16 is monotone, so the rounded maximum is the maximum of the rounded values.
+    local_bits = (cvt_pk_bf16(__uint_as_float(local_bits), 0.0f) & 0xFFFFu) << 16;
+  }
+  if (tid == 0) a.partials[blockIdx.x] = local_bits;
+}
+
+// ---- pass 2: scales, codes, pack, swizzle ---------------------------------------------------------
+//
+// GIVEN: the tensor amax comes from the caller (a device float). Otherwise it is the
+// maximum of the absmax launch's a.npart workgroup partials.
 template <int MODE, bool GIVEN>
 __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) {
   constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint32_t* red = (uint32_t*)smem;                          // wave maxima + two broadcast slots
+  uint32_t* red = (uint32_t*)smem;                          // wave maxima + a broadcast slot
   uint16_t* tab = (uint16_t*)(smem + kRedBytes);            // 65,536 entries (SwiGLU only)
 
   const int tid = threadIdx.x;
@@ -287,169 +449,18 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
   const int r4 = lane / kLanesPerRow;   // row within the wave's rows of a step
   const int blk = lane % kLanesPerRow;  // 16-column block of the item's column segment
   const int nitems = a.items_m * a.items_k;
-
-  if (SWIGLU) {
-    const u32x4_t* src = (const u32x4_t*)a.silu_table;
-    u32x4_t* dst = (u32x4_t*)tab;
-    for (int i = tid; i < 65536 * 2 / 16; i += kProdThreads) dst[i] = src[i];
-    __syncthreads();
-  }
-
-  // the 16 bf16 values of this lane's block in each step of an item (zero outside
-  // the logical rows and columns)
-  // For kModulate the up slots carry the item's modulation instead: uv[0] = the
-  // scale and uv[1] = the shift of the lane's 16 columns (kSteps == 2).
-  static_assert(kSteps == 2, "modulation vectors ride in the two up slots");
-  auto load_item = [&](int item, u32x4_t (&gv)[kSteps][2], u32x4_t (&uv)[kSteps][2]) {
-    const int rt = item / a.items_k, kt = item - rt * a.items_k;
-    const int64_t col = (int64_t)kt * kItemCols + blk * 16;
-    if (MOD) {
-      const bool cok = col < a.k;
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      const u32x4_t* ps = (const u32x4_t*)(a.mod_scale + col);
-      const u32x4_t* pb = (const u32x4_t*)(a.mod_shift + col);
-      uv[0][0] = cok ? ps[0] : z;
-      uv[0][1] = cok ? ps[1] : z;
-      uv[1][0] = cok ? pb[0] : z;
-      uv[1][1] = cok ? pb[1] : z;
-    }
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int64_t row = (int64_t)rt * kItemRows + s * kRowsPerStep + wave * kWaveRows + r4;
-      const bool ok = row < a.m && col < a.k;
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      const u32x4_t* px = (const u32x4_t*)(a.x + row * a.ldx + col);
-      gv[s][0] = ok ? px[0] : z;
-      gv[s][1] = ok ? px[1] : z;
-      if (SWIGLU) {
-        const u32x4_t* pu = (const u32x4_t*)(a.u + row * a.ldu + col);
-        uv[s][0] = ok ? pu[0] : z;
-        uv[s][1] = ok ? pu[1] : z;
-      }
-    }
-  };
+  if (SWIGLU) stage_silu_table(a.silu_table, tab, tid);
 
   float amax;
   if constexpr (GIVEN) {
     amax = a.amax_in[0];
   } else {
-    // ---------------- pass 1: absmax ----------------
-    uint32_t local_bits = 0;  // fp32 bits of a non-negative value
-    // rows past m read zeros; only the modulation would turn them into nonzero y
-    auto absmax_item = [&](int item, const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
-      const int64_t row0 = (int64_t)(item / a.items_k) * kItemRows + wave * kWaveRows + r4;
-#pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        if (MOD && row0 + s * kRowsPerStep >= a.m) continue;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const uint32_t gw = gv[s][w >> 2][w & 3];
-          if (MOD) {
-            const uint32_t sw = uv[0][w >> 2][w & 3], bw = uv[1][w >> 2][w & 3];
-            const float p0 = fabsf(modulate_f32(gw & 0xFFFFu, sw & 0xFFFFu, bw & 0xFFFFu));
-            const float p1 = fabsf(modulate_f32(gw >> 16, sw >> 16, bw >> 16));
-            const uint32_t b = __float_as_uint(fmaxf(p0, p1));
-            local_bits = b > local_bits ? b : local_bits;
-          } else if (SWIGLU) {
-            const uint32_t uw = uv[s][w >> 2][w & 3];
-            const float s0 = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16);
-            const float s1 = __uint_as_float((uint32_t)tab[gw >> 16] << 16);
-            const float p0 = fabsf(s0 * __uint_as_float(uw << 16));
-            const float p1 = fabsf(s1 * __uint_as_float(uw & 0xFFFF0000u));
-            const uint32_t b = __float_as_uint(fmaxf(p0, p1));
-            local_bits = b > local_bits ? b : local_bits;
-          } else {
-            const uint32_t m0 = gw & 0x7FFFu, m1 = (gw >> 16) & 0x7FFFu;
-            const uint32_t b = (m0 > m1 ? m0 : m1) << 16;
-            local_bits = b > local_bits ? b : local_bits;
-          }
-        }
-      }
-    };
-    {
-      // the next item's loads are in flight while the current item is reduced
-      u32x4_t gA[kSteps][2], uA[kSteps][2], gB[kSteps][2], uB[kSteps][2];
-      int item = blockIdx.x;
-      if (item < nitems) load_item(item, gA, uA);
-      while (item < nitems) {
-        const int n1 = item + (int)gridDim.x;
-        if (n1 < nitems) load_item(n1, gB, uB);
-        absmax_item(item, gA, uA);
-        item = n1;
-        if (item >= nitems) break;
-        const int n2 = item + (int)gridDim.x;
-        if (n2 < nitems) load_item(n2, gA, uA);
-        absmax_item(item, gB, uB);
-        item = n2;
-      }
+    uint32_t v = 0;
+    for (int i = tid; i < a.npart; i += kProdThreads) {
+      const uint32_t p = a.partials[i];
+      v = p > v ? p : v;
     }
-    // workgroup max of the unrounded |products| (SwiGLU) or of |x|
-    bool needs_exact = false;
-    {
-      uint32_t wmax = wave_max_u32(local_bits);
-      if (lane == 0) red[wave] = wmax;
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t v = 0;
-        for (int i = 0; i < kProdThreads / 64; ++i) v = red[i] > v ? red[i] : v;
-        red[kWaves] = v;
-      }
-      __syncthreads();
-      local_bits = red[kWaves];
-      // A product below 2^-126 may have been rounded in fp32; if this workgroup's
-      // maximum is such a product, redo its elements exactly (never taken for
-      // inputs whose absmax is a normal number).
-      needs_exact = SWIGLU && local_bits != 0 && local_bits < 0x00800000u;
-      __syncthreads();
-    }
-    if (SWIGLU && needs_exact) {
-      uint32_t best = 0;  // bf16 magnitude bits
-      for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-        u32x4_t gv[kSteps][2], uv[kSteps][2];
-        load_item(item, gv, uv);
-        for (int s = 0; s < kSteps; ++s)
-          for (int j = 0; j < 16; ++j) {
-            const uint32_t g16 = (gv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
-            const uint32_t u16 = (uv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
-            const double p = (double)bf16_bits_to_float(tab[g16]) * (double)bf16_bits_to_float(u16);
-            const uint32_t y = rn_bf16_from_double(p) & 0x7FFFu;
-            best = y > best ? y : best;
-          }
-      }
-      uint32_t wmax = wave_max_u32(best);
-      if (lane == 0) red[wave] = wmax;
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t v = 0;
-        for (int i = 0; i < kProdThreads / 64; ++i) v = red[i] > v ? red[i] : v;
-        red[kWaves] = v << 16;
-      }
-      __syncthreads();
-      local_bits = red[kWaves];
-    } else if (SWIGLU || MOD) {
-      // RN_bf16 is monotone, so the rounded maximum is the maximum of the rounded values.
-      local_bits = (cvt_pk_bf16(__uint_as_float(local_bits), 0.0f) & 0xFFFFu) << 16;
-    }
-
-    // ---------------- grid barrier: publish amax ----------------
-    if (tid == 0) {
-      ProducerWorkspace* ws = a.ws;
-      __hip_atomic_fetch_max(&ws->amax_bits, local_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&ws->arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      while (__hip_atomic_load(&ws->arrived, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x)
-        __builtin_amdgcn_s_sleep(2);
-      const uint32_t amax = __hip_atomic_load(&ws->amax_bits, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-      red[kWaves + 1] = amax;
-      // the last workgroup to leave returns the workspace to zero for the next call
-      const uint32_t d = __hip_atomic_fetch_add(&ws->departed, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (d == gridDim.x - 1) {
-        __hip_atomic_store(&ws->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ws->arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ws->departed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-    amax = __uint_as_float(red[kWaves + 1]);
+    amax = __uint_as_float(workgroup_max_u32(v, red, tid));
   }
   const float g = global_scale_from_amax(amax);
   const double g6 = 6.0 * (double)g;
@@ -463,7 +474,6 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
   const float inv_f = (float)inv_g6;
   if (blockIdx.x == 0 && tid == 0) *a.gout = g;
 
-  // ---------------- pass 2: scales, codes, pack, swizzle ----------------
   const int64_t qrow_bytes = a.k / 2;
   auto quantize_item = [&](int item, const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
     const int rt = item / a.items_k, kt = item - rt * a.items_k;
@@ -551,12 +561,12 @@ __global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) 
       }
     }
   };
-  // items in reverse order: the rows read last in pass 1, still in the memory-side
-  // cache, are read first. No workgroup barrier: the 16 waves drift apart and hide
-  // each other's load latency.
+  // Items in reverse order: the rows the absmax launch read last, still in the
+  // memory-side cache, are read first. No workgroup barrier: the 16 waves drift apart
+  // and hide each other's load latency.
   for (int item = nitems - 1 - (int)blockIdx.x; item >= 0; item -= (int)gridDim.x) {
     u32x4_t gv[kSteps][2], uv[kSteps][2];
-    load_item(item, gv, uv);
+    load_item<MODE>(a, item, wave, r4, blk, gv, uv);
     quantize_item(item, gv, uv);
   }
 }
@@ -575,10 +585,18 @@ const void* producer_kernel_ptr(int mode, bool given) {
   return given ? (const void*)producer_kernel<kPlain, true> : (const void*)producer_kernel<kPlain, false>;
 }
 
+const void* producer_absmax_kernel_ptr(int mode) {
+  if (mode == kSwiglu) return (const void*)producer_absmax_kernel<kSwiglu>;
+  if (mode == kModulate) return (const void*)producer_absmax_kernel<kModulate>;
+  return (const void*)producer_absmax_kernel<kPlain>;
+}
+
 int producer_block_threads() { return kProdThreads; }
 
-// amax_in == nullptr: the two-pass producer (cooperative launch, workspace used);
-// otherwise the single-pass producer with the caller's amax (ordinary launch).
+// amax_in == nullptr: the two-pass producer (absmax launch into the workspace's
+// partials, then the quantize launch); otherwise the single-read producer with the
+// caller's amax (the quantize launch alone). Both are ordinary launches of at most
+// max_blocks (<= kMaxPartials) workgroups.
 hipError_t launch_producer(int mode, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
                            const uint16_t* mod_scale, const uint16_t* mod_shift, int64_t m, int64_t k,
                            uint8_t* qdata, uint8_t* scales, float* gout, const float* amax_in, void* workspace,
@@ -601,17 +619,27 @@ hipError_t launch_producer(int mode, const uint16_t* x, int64_t ldx, const uint1
   args.amax_in = amax_in;
   args.mod_scale = mod_scale;
   args.mod_shift = mod_shift;
-  args.ws = (ProducerWorkspace*)workspace;
+  args.partials = workspace ? ((ProducerWorkspace*)workspace)->partial : nullptr;
+  args.npart = 0;
   args.silu_table = silu_table;
   const int64_t nitems = (int64_t)args.items_m * args.items_k;
+  if (max_blocks > kMaxPartials) max_blocks = kMaxPartials;
   int blocks = (int)(nitems < max_blocks ? nitems : max_blocks);
   if (blocks < 1) blocks = 1;
+  const size_t smem = producer_smem_bytes(mode);
+  if (amax_in) {
+    void* kargs[] = {&args};
+    return hipLaunchKernel(producer_kernel_ptr(mode, true), dim3(blocks), dim3(kProdThreads), kargs, smem, stream);
+  }
+  {
+    void* kargs[] = {&args};
+    hipError_t e = hipLaunchKernel(producer_absmax_kernel_ptr(mode), dim3(blocks), dim3(kProdThreads), kargs, smem,
+                                   stream);
+    if (e != hipSuccess) return e;
+  }
+  args.npart = blocks;
   void* kargs[] = {&args};
-  if (amax_in)
-    return hipLaunchKernel(producer_kernel_ptr(mode, true), dim3(blocks), dim3(kProdThreads), kargs,
-                           producer_smem_bytes(mode), stream);
-  return hipLaunchCooperativeKernel(producer_kernel_ptr(mode, false), dim3(blocks), dim3(kProdThreads), kargs,
-                                    (unsigned)producer_smem_bytes(mode), stream);
+  return hipLaunchKernel(producer_kernel_ptr(mode, false), dim3(blocks), dim3(kProdThreads), kargs, smem, stream);
 }
 
 }  // namespace nvfp4

@@ -84,14 +84,23 @@ def fused_compare(d1_got: np.ndarray, d1_ref: np.ndarray, plain_ref: np.ndarray,
     return out
 
 
+PARITY_ROWS = 4096  # seeded logical rows sampled per large configuration
+
+
 def sample_rows(m: int, m_pad: int, count: int, seed: int) -> np.ndarray:
-    """Seeded sample of logical rows, plus the first and last rows of every 256-row
-    tile boundary region near the tail, plus all padding rows."""
+    """Rows whose GEMM outputs are compared: `count` seeded logical rows, plus the rows
+    on both sides of every 256-row tile boundary (the GEMM's M tiles) and of every
+    128-row boundary in the last 512 rows (its quarter-tile tail), the last 64 logical
+    rows, row 0, and every padding row [m, m_pad)."""
     rng = np.random.default_rng(seed)
     base = rng.choice(m, size=min(count, m), replace=False)
+    b256 = np.arange(256, m_pad, 256)
+    b128 = np.arange(max(128, (m_pad - 512) // 128 * 128), m_pad, 128)
+    edges = np.concatenate([b256 - 1, b256, b128 - 1, b128])
     tail = np.arange(max(0, m - 64), m)
     pad = np.arange(m, m_pad)
-    return np.unique(np.concatenate([base, tail, [0], pad])).astype(np.int64)
+    rows = np.unique(np.concatenate([base, edges, tail, [0], pad])).astype(np.int64)
+    return rows[(rows >= 0) & (rows < m_pad)]
 
 
 def to_device_bf16(bits: np.ndarray, device):

@@ -55,7 +55,7 @@ def test_sizes_match_oracle_geometry(rows, k):
 def test_size_functions_reject_negative():
     assert nv.nvfp4_padded_rows(-1) == -1
     assert nv.nvfp4_qdata_bytes(-1, 64) == -1
-    assert nv.nvfp4_quantize_workspace_bytes() == 256
+    assert nv.nvfp4_quantize_workspace_bytes() == 4096
 
 
 FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced: validation fails first
@@ -224,6 +224,49 @@ def test_binding_raises_on_error():
     assert nv.COUNTERS["nvfp4_gemm_bf16out"]["failures"] >= 1
 
 
+def test_strict_and_fallback_dispatch():
+    """Strict calls raise; non-strict calls return False and count a fallback with the
+    status and detail kept; successes, fallbacks and failures add up to the attempts.
+    (Validation fails before any device access, so no GPU is needed.)"""
+    name = "nvfp4_gemm_bf16out"
+    before = nv.dispatch_counters().get(name, {"attempts": 0, "successes": 0, "fallbacks": 0, "failures": 0})
+    bad = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 64, None)  # m_padded % 16 != 0
+    with pytest.raises(nv.Nvfp4Error):
+        nv._call(name, *bad, strict=True)
+    assert nv._call(name, *bad, strict=False) is False
+    assert nv.LAST_FALLBACK[name][0] == 2 and "m_padded" in nv.LAST_FALLBACK[name][1]
+    saved = nv.STRICT
+    try:
+        nv.set_strict(False)
+        assert nv._call(name, *bad) is False
+        nv.set_strict(True)
+        with pytest.raises(nv.Nvfp4Error):
+            nv._call(name, *bad)
+    finally:
+        nv.set_strict(saved)
+    after = nv.dispatch_counters()[name]
+    assert after["attempts"] - before["attempts"] == 4
+    assert after["fallbacks"] - before["fallbacks"] == 2
+    assert after["failures"] - before["failures"] == 2
+    assert after["attempts"] == after["successes"] + after["fallbacks"] + after["failures"]
+
+
+def test_strict_default_follows_environment():
+    """NVFP4_STRICT=0 starts the binding non-strict; anything else (or unset) strict."""
+    code = ("import nvfp4_block_scaled_swiglu_amd as nv; print(int(nv.STRICT))")
+    env = dict(os.environ)
+    outs = []
+    for val in (None, "0", "1"):
+        if val is None:
+            env.pop("NVFP4_STRICT", None)
+        else:
+            env["NVFP4_STRICT"] = val
+        r = subprocess.run([os.environ.get("PYTHON", "python"), "-c", code], cwd=ROOT, env=env,
+                           capture_output=True, text=True, timeout=120)
+        outs.append(r.stdout.strip())
+    assert outs == ["1", "0", "1"]
+
+
 def test_valid_call_without_gpu_reports_no_device():
     """With valid arguments and no visible GPU the call reaches the device check and
     returns NVFP4_ERR_NO_DEVICE (nothing is launched)."""
@@ -232,3 +275,15 @@ def test_valid_call_without_gpu_reports_no_device():
         pytest.skip("a GPU is visible")
     assert call_quant() == 5
     assert "device" in nv.lib().nvfp4_last_error().decode().lower()
+
+
+def test_hbm_stream_ceiling_validation():
+    l = nv.lib()
+    chunk = l.nvfp4_hbm_stream_chunk_bytes()
+    assert chunk == 16384
+    assert l.nvfp4_hbm_stream_ceiling(None, chunk, FAKE, 0, None) == 1
+    assert l.nvfp4_hbm_stream_ceiling(FAKE, 0, FAKE, 0, None) == 1
+    assert l.nvfp4_hbm_stream_ceiling(FAKE, chunk + 16, FAKE, 0, None) == 1
+    assert l.nvfp4_hbm_stream_ceiling(FAKE, chunk, FAKE, chunk + 16, None) == 1
+    assert l.nvfp4_hbm_stream_ceiling(FAKE, chunk, FAKE, 8, None) == 1
+    assert l.nvfp4_hbm_stream_ceiling(FAKE + 4, chunk, FAKE, 0, None) == 3

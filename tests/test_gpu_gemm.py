@@ -140,17 +140,24 @@ def test_gemm_deterministic_and_prefix_invariant(gpu):
     assert torch.equal(d1[:512], d3)
 
 
-@pytest.mark.parametrize("name,rows", [("mid_fc2_slice", 1024), ("qkv", 1024), ("attn_out", 1024), ("fc1", 512),
-                                       ("qkv_pages", 512)])
-def test_large_configs(gpu, name, rows):
-    run_path(synth.BY_NAME[name], gpu, rows, 17)
+@pytest.mark.parametrize("name", ["mid_fc2_slice", "qkv", "attn_out", "fc1", "qkv_pages"])
+def test_large_configs(gpu, name):
+    """Configs 2 and 4 (and the pages' QKV width): 4,096 seeded rows, the tile-boundary
+    rows and every padding row."""
+    _, st = run_path(synth.BY_NAME[name], gpu, parity.PARITY_ROWS, 17)
+    assert st["checked"] >= parity.PARITY_ROWS * synth.BY_NAME[name].n
 
 
 def test_canonical_fc2(gpu):
-    run_path(synth.FC2, gpu, 4096, 440420)
+    _, st = run_path(synth.FC2, gpu, parity.PARITY_ROWS, 440420)
+    assert st["checked"] >= parity.PARITY_ROWS * synth.FC2.n
 
 
 @pytest.mark.parametrize("m", synth.RAGGED_M)
 def test_ragged_m(gpu, m):
+    """Config 5: each ragged M with 4,096 seeded rows, the tile-boundary rows, the last
+    64 logical rows and every padding row (the pages' row-shape gate found two
+    differing bf16 elements in a whole output at some of these M)."""
     w = [r for r in synth.RAGGED if r.m == m][0]
-    run_path(w, gpu, 192, m)
+    _, st = run_path(w, gpu, parity.PARITY_ROWS, m)
+    assert st["checked"] >= parity.PARITY_ROWS * w.n

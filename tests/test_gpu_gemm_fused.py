@@ -190,17 +190,24 @@ def test_tail_quarter_tiles_fused(gpu):
 
 
 def test_canonical_fc2_fused(gpu):
-    """The FC2 shape: SwiGLU producer, bias, gate and residual; sampled rows."""
+    """The FC2 shape: SwiGLU producer, bias, gate and residual. The producer's bytes
+    are first checked equal to the oracle's quantization, and the oracle then computes
+    the fused outputs from its own bytes; 4,096 seeded rows, tile-boundary rows and
+    padding rows."""
     import torch
     import nvfp4_block_scaled_swiglu_amd as nv
     w = synth.FC2
     _say("[fused] canonical FC2")
     gate_in, up_in = w.activations()
     a, aq, as_, ga = parity.run_quantize(gate_in, up_in, gpu)
-    del gate_in, up_in
+    rq, rs, rg = oracle.quantize(gate_in, up_in)
+    assert (aq == rq).all() and (as_ == rs).all() and ga == rg, "activation bytes differ from the oracle"
+    del gate_in, up_in, aq, as_
     W = w.weight()
     wt, wq, ws, gw = parity.run_quantize(W, None, gpu)
-    del W
+    rwq, rws, rgw = oracle.quantize(W)
+    assert (wq == rwq).all() and (ws == rws).all() and gw == rgw, "weight bytes differ from the oracle"
+    del W, wq, ws
     bias = bias_vector(w.n, 11)
     gate = synth.normal_bf16(1, w.n, seed=11, tag=6, sigma=0.7)[0]
     res = synth.normal_bf16(w.m_pad, w.n, seed=11, tag=7, sigma=0.3)
@@ -208,10 +215,12 @@ def test_canonical_fc2_fused(gpu):
     d = nv.nvfp4_gemm_bf16out_fused(a, wt, bias=dev_bf16(bias, gpu), gate=dev_bf16(gate, gpu),
                                     residual=dev_bf16(res, gpu))
     torch.cuda.synchronize()
-    rows = parity.sample_rows(w.m, w.m_pad, 96, 12)
-    plain = oracle.gemm_rows(aq, as_, w.m, ga, wq, ws, w.n, gw, w.k, rows)
-    r1, rd = oracle.gemm_rows_ex(aq, as_, w.m, ga, wq, ws, w.n, gw, w.k, rows, bias=bias, gate=gate, res=res)
+    rows = parity.sample_rows(w.m, w.m_pad, parity.PARITY_ROWS, 12)
+    _say(f"[fused] canonical FC2: oracle on {rows.size} rows")
+    plain = oracle.gemm_rows(rq, rs, w.m, rg, rwq, rws, w.n, rgw, w.k, rows)
+    r1, rd = oracle.gemm_rows_ex(rq, rs, w.m, rg, rwq, rws, w.n, rgw, w.k, rows, bias=bias, gate=gate, res=res)
     idx = torch.from_numpy(rows).to(gpu)
     st = parity.fused_compare(parity.tensor_bits(d1[idx]), r1, plain, parity.tensor_bits(d[idx]), rd, gate)
     _say(f"[fused] {st}")
     assert st["d1_violations"] == 0 and st["d_violations"] == 0, st
+    assert st["checked"] >= parity.PARITY_ROWS * w.n

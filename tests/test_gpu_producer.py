@@ -146,24 +146,61 @@ def test_extreme_magnitudes_plain(gpu):
 
 
 def test_workspace_reuse_and_determinism(gpu):
-    """Back-to-back calls on one workspace give identical bytes (the kernel returns the
-    workspace to zero), and the workspace is zero afterwards."""
+    """The workspace needs no initialisation: a workspace full of 0xA5 bytes, reused by
+    back-to-back calls of different sizes and modes, gives identical bytes each time,
+    equal to the oracle's."""
     import torch
     import nvfp4_block_scaled_swiglu_amd as nv
     w = synth.TINY
     gate, up = w.activations()
     g_t, u_t = parity.to_device_bf16(gate, gpu), parity.to_device_bf16(up, gpu)
-    ws = torch.zeros(nv.nvfp4_quantize_workspace_bytes(), dtype=torch.uint8, device=gpu)
-    outs = [nv.nvfp4_quantize_swiglu(g_t, u_t, workspace=ws) for _ in range(3)]
+    ws = torch.full((nv.nvfp4_quantize_workspace_bytes(),), 0xA5, dtype=torch.uint8, device=gpu)
+    outs = [nv.nvfp4_quantize_swiglu(g_t, u_t, workspace=ws) for _ in range(2)]
     x_t = parity.to_device_bf16(w.weight(), gpu)
     wq = nv.nvfp4_quantize(x_t, workspace=ws)
+    small = nv.nvfp4_quantize_swiglu(g_t[:20], u_t[:20], workspace=ws)
+    outs.append(nv.nvfp4_quantize_swiglu(g_t, u_t, workspace=ws))
     torch.cuda.synchronize()
-    assert int(ws.sum().item()) == 0
     for o in outs[1:]:
         assert torch.equal(o.qdata, outs[0].qdata) and torch.equal(o.scales, outs[0].scales)
         assert torch.equal(o.global_scale, outs[0].global_scale)
+    rq, rs, rg = oracle.quantize(gate, up)
+    assert (outs[0].qdata.cpu().numpy() == rq).all() and (outs[0].scales.cpu().numpy() == rs).all()
+    assert float(outs[0].global_scale.item()) == rg
     rq, rs, rg = oracle.quantize(w.weight())
     assert (wq.qdata.cpu().numpy() == rq).all() and float(wq.global_scale.item()) == rg
+    rq, rs, rg = oracle.quantize(gate[:20], up[:20])
+    assert (small.qdata.cpu().numpy() == rq).all() and (small.scales.cpu().numpy() == rs).all()
+    assert float(small.global_scale.item()) == rg
+
+
+def test_non_strict_failure_leaves_buffers(gpu):
+    """A call that fails validation, made non-strict, returns None, counts a fallback
+    and leaves the produced NVFP4 bytes and the output buffer as they were."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    w = synth.TINY
+    gate, up = w.activations()
+    a = nv.nvfp4_quantize_swiglu(parity.to_device_bf16(gate, gpu), parity.to_device_bf16(up, gpu))
+    wt = nv.nvfp4_quantize(parity.to_device_bf16(w.weight(), gpu))
+    torch.cuda.synchronize()
+    snap = (a.qdata.clone(), a.scales.clone(), a.global_scale.clone())
+    # the same bytes described with k = 96 (not a multiple of 64): the library refuses
+    bad_a = nv.Nvfp4Tensor(qdata=a.qdata, scales=a.scales, global_scale=a.global_scale, rows=a.rows, k=96)
+    bad_w = nv.Nvfp4Tensor(qdata=wt.qdata, scales=wt.scales, global_scale=wt.global_scale, rows=wt.rows, k=96)
+    out = torch.full((a.padded_rows, wt.rows), 7.0, dtype=torch.bfloat16, device=gpu)
+    before = nv.dispatch_counters().get("nvfp4_gemm_bf16out", {}).get("fallbacks", 0)
+    assert nv.nvfp4_gemm_bf16out(bad_a, bad_w, out=out, strict=False) is None
+    with pytest.raises(nv.Nvfp4Error):
+        nv.nvfp4_gemm_bf16out(bad_a, bad_w, out=out, strict=True)
+    torch.cuda.synchronize()
+    assert nv.dispatch_counters()["nvfp4_gemm_bf16out"]["fallbacks"] == before + 1
+    assert bool((out == 7.0).all())
+    assert torch.equal(a.qdata, snap[0]) and torch.equal(a.scales, snap[1]) and torch.equal(a.global_scale, snap[2])
+    # the fallback goes through the same, untouched bytes
+    d = nv.nvfp4_gemm_bf16out(a, wt)
+    torch.cuda.synchronize()
+    assert d is not None and bool(torch.isfinite(d.float()).all())
 
 
 @pytest.mark.parametrize("name", ["mid_fc2_slice", "qkv", "attn_out", "fc1"])

@@ -137,6 +137,25 @@ int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_
                           int64_t m, int64_t k, void* qdata_dev, void* scales_dev,
                           float* global_scale_dev, void* workspace_dev, void* stream);
 
+/*
+ * nvfp4_quantize_swiglu for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same operation, arguments, layouts and outputs, without the workspace argument.
+ * The absmax partials live in the library's own scratch, a fixed 4,096-byte device
+ * array per GPU (one slot for each of at most 1,024 absmax workgroups) held until
+ * the process ends; the call allocates nothing and calls no allocating routine.
+ * Set-up allocates, so nvfp4_init must have run on the current device first
+ * (otherwise NVFP4_ERR_NO_DEVICE). Every call on a GPU shares that GPU's scratch:
+ * each call writes every slot it reads, so nothing carries over between calls,
+ * but calls that overlap in time on one GPU (different streams) race and may
+ * produce wrong global scales; serialise them, or use nvfp4_quantize_swiglu with
+ * distinct workspaces. NVFP4_ERR_WORKSPACE if the device's producer grid would
+ * need more slots than the scratch holds (not reachable with 1,024 slots).
+ */
+int nvfp4_quantize_swiglu_noalloc(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up,
+                                  int64_t m, int64_t k, void* qdata_dev, void* scales_dev,
+                                  float* global_scale_dev, void* stream);
+
 /* Plain NVFP4 quantization of x (y = x): the same contract as
  * nvfp4_quantize_swiglu with one bf16 [rows, k] input of row stride ld_x. The
  * component-2 summary lists this generic producer (absmax_partial, scale_finalize,

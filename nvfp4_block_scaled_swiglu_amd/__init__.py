@@ -52,6 +52,7 @@ SIGNATURES = {
     "nvfp4_quantize_workspace_bytes": (_I64, []),
     "nvfp4_init": (_INT, []),
     "nvfp4_quantize_swiglu": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "nvfp4_quantize_swiglu_noalloc": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_quantize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_quantize_modulate": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "nvfp4_quantize_swiglu_amax": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -259,6 +260,27 @@ def nvfp4_quantize_swiglu(gate, up, out: Optional[Nvfp4Tensor] = None, m: Option
     if not _call("nvfp4_quantize_swiglu", gate.data_ptr(), gate.stride(0), up.data_ptr(), up.stride(0), m, k,
                  out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(), sh,
                  strict=strict):
+        return None
+    return out
+
+
+def nvfp4_quantize_swiglu_noalloc(gate, up, out: Nvfp4Tensor, m: Optional[int] = None, stream=None,
+                                  strict: Optional[bool] = None) -> Optional[Nvfp4Tensor]:
+    """nvfp4_quantize_swiglu with the library's fixed device scratch instead of a
+    workspace, into the caller's preallocated `out` (nothing is allocated here or in
+    the library; nvfp4_init must have run on the device). Calls overlapping on one GPU
+    race on the shared scratch."""
+    _bf16_2d(gate, "gate")
+    _bf16_2d(up, "up")
+    m = gate.shape[0] if m is None else m
+    k = gate.shape[1]
+    if up.shape[1] != k or up.shape[0] < m or gate.shape[0] < m:
+        raise ValueError("gate/up shapes disagree")
+    if out.rows != m or out.k != k:
+        raise ValueError("out must be an Nvfp4Tensor for the same rows and k")
+    if not _call("nvfp4_quantize_swiglu_noalloc", gate.data_ptr(), gate.stride(0), up.data_ptr(), up.stride(0), m,
+                 k, out.qdata.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(),
+                 _stream_handle(stream), strict=strict):
         return None
     return out
 

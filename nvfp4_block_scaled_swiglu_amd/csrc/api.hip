@@ -50,12 +50,25 @@ constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;  // 32-bit buffer offsets 
 struct DeviceState {
   std::atomic<bool> ready{false};
   const uint16_t* silu_table = nullptr;
+  void* scratch = nullptr;  // this device's copy of `scratch` (hipGetSymbolAddress)
   int producer_blocks[3] = {0, 0, 0};  // persistent grid per producer mode
   int cu_count = 0;
   char arch[64] = {0};
 };
 
 DeviceState g_dev[kMaxDevices];
+
+}  // namespace
+
+// Producer scratch of nvfp4_quantize_swiglu_noalloc: the absmax partials that the
+// other two-pass entry points keep in the caller's workspace. Each GPU holds its own
+// copy for the life of the process; host code uses only the per-device address that
+// set-up obtains with hipGetSymbolAddress (the name itself is a host-side stand-in).
+// Every call on a GPU shares it, and each call writes every slot it reads, so nothing
+// needs clearing between calls; calls that overlap in time on one GPU race.
+static __device__ __align__(256) uint32_t scratch[nvfp4::kMaxPartials];
+
+namespace {
 std::mutex g_init_mutex;
 thread_local char t_last_error[512] = "";
 thread_local char t_build_info[512] = "";
@@ -126,6 +139,9 @@ int ensure_device(DeviceState** out) {
 
   e = nvfp4::silu_table_address(&st.silu_table);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "silu table address: %s", hipGetErrorString(e));
+  e = hipGetSymbolAddress(&st.scratch, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !st.scratch)
+    return fail(NVFP4_ERR_LAUNCH, "producer scratch address: %s", hipGetErrorString(e));
   hipStream_t s;
   e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "stream create: %s", hipGetErrorString(e));
@@ -139,15 +155,17 @@ int ensure_device(DeviceState** out) {
   return NVFP4_OK;
 }
 
-// ws: the workspace of the two-pass producer, or the caller's amax of the single-pass one
+// ws: the workspace of the two-pass producer, or the caller's amax of the single-pass
+// one; with `scratch` (the library's own scratch stands in for the workspace) ws is unused
 int check_quant_args(const void* x, int64_t ldx, const void* u, int64_t ldu, bool swiglu, int64_t m, int64_t k,
-                     const void* qdata, const void* scales, const float* g, const void* ws, bool given) {
+                     const void* qdata, const void* scales, const float* g, const void* ws, bool given,
+                     bool scratch = false) {
   if (!g) return fail(NVFP4_ERR_INVALID_ARG, "null global-scale pointer");
   // with no rows nothing is read or written except the global scale
   if (m != 0 && (!x || (swiglu && !u) || !qdata || !scales))
     return fail(NVFP4_ERR_INVALID_ARG, "null input or output pointer");
   if (given && !ws) return fail(NVFP4_ERR_INVALID_ARG, "null amax pointer");
-  if (!given && !ws) return fail(NVFP4_ERR_WORKSPACE, "null workspace");
+  if (!given && !scratch && !ws) return fail(NVFP4_ERR_WORKSPACE, "null workspace");
   if (m < 0 || k <= 0) return fail(NVFP4_ERR_INVALID_ARG, "bad shape m=%lld k=%lld", (long long)m, (long long)k);
   if (k % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k=%lld is not a multiple of 64", (long long)k);
   if (ldx < k || (swiglu && ldu < k))
@@ -156,7 +174,7 @@ int check_quant_args(const void* x, int64_t ldx, const void* u, int64_t ldu, boo
   if (ldx % 8 != 0 || (swiglu && ldu % 8 != 0))
     return fail(NVFP4_ERR_MISALIGNED, "row strides must be multiples of 8 elements");
   if (!aligned16(x) || (swiglu && !aligned16(u)) || !aligned16(qdata) || !aligned16(scales) || ((uintptr_t)g & 3u) ||
-      (given ? ((uintptr_t)ws & 3u) != 0 : !aligned16(ws)))
+      (given ? ((uintptr_t)ws & 3u) != 0 : (!scratch && !aligned16(ws))))
     return fail(NVFP4_ERR_MISALIGNED, "pointers must be 16-byte aligned (global scale and amax 4-byte)");
   const int64_t rows_pad = (m + 15) / 16 * 16;
   const int64_t srows = (rows_pad + 127) / 128 * 128;
@@ -213,6 +231,33 @@ int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_
                           void* stream) {
   return quantize_common(1, false, gate_dev, ld_gate, up_dev, ld_up, nullptr, nullptr, m, k, qdata_dev, scales_dev,
                          global_scale_dev, nullptr, workspace_dev, stream);
+}
+
+int nvfp4_quantize_swiglu_noalloc(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up, int64_t m,
+                                  int64_t k, void* qdata_dev, void* scales_dev, float* global_scale_dev,
+                                  void* stream) {
+  // every argument is validated as for nvfp4_quantize_swiglu; the scratch is the workspace
+  int rc = check_quant_args(gate_dev, ld_gate, up_dev, ld_up, true, m, k, qdata_dev, scales_dev, global_scale_dev,
+                            nullptr, false, true);
+  if (rc != NVFP4_OK) return rc;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(NVFP4_ERR_NO_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
+  DeviceState& st = g_dev[dev];
+  // set-up allocates (a stream for the silu table build), so it is not done here
+  if (!st.ready.load(std::memory_order_acquire))
+    return fail(NVFP4_ERR_NO_DEVICE, "call nvfp4_init on device %d before nvfp4_quantize_swiglu_noalloc", dev);
+  // the absmax launch writes one slot per workgroup; its grid is capped at kMaxPartials
+  static_assert(sizeof(scratch) == sizeof(nvfp4::ProducerWorkspace), "scratch holds one workspace");
+  if ((int64_t)st.producer_blocks[1] * 4 > (int64_t)sizeof(scratch))
+    return fail(NVFP4_ERR_WORKSPACE, "producer grid of %d workgroups exceeds the %d-slot scratch",
+                st.producer_blocks[1], nvfp4::kMaxPartials);
+  e = nvfp4::launch_producer(1, (const uint16_t*)gate_dev, ld_gate, (const uint16_t*)up_dev, ld_up, nullptr, nullptr,
+                             m, k, (uint8_t*)qdata_dev, (uint8_t*)scales_dev, global_scale_dev, nullptr, st.scratch,
+                             st.silu_table, st.producer_blocks[1], (hipStream_t)stream);
+  if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int nvfp4_quantize_swiglu_amax(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up, int64_t m,

@@ -287,3 +287,17 @@ def test_hbm_stream_ceiling_validation():
     assert l.nvfp4_hbm_stream_ceiling(FAKE, chunk, FAKE, chunk + 16, None) == 1
     assert l.nvfp4_hbm_stream_ceiling(FAKE, chunk, FAKE, 8, None) == 1
     assert l.nvfp4_hbm_stream_ceiling(FAKE + 4, chunk, FAKE, 0, None) == 3
+
+
+def test_noalloc_entry_validation():
+    """The no-allocation producer validates like nvfp4_quantize_swiglu (no workspace
+    argument) and, with valid arguments and no GPU, stops at the device check."""
+    l = nv.lib()
+    f = l.nvfp4_quantize_swiglu_noalloc
+    assert f(None, 64, FAKE, 64, 16, 64, FAKE, FAKE, FAKE, None) == 1
+    assert f(FAKE, 64, FAKE, 64, 16, 96, FAKE, FAKE, FAKE, None) == 2
+    assert f(FAKE, 64, FAKE, 64, 16, 64, FAKE + 8, FAKE, FAKE, None) == 3
+    assert f(FAKE, 64, FAKE, 64, 16, 64, FAKE, FAKE, None, None) == 1
+    import torch
+    if not torch.cuda.is_available():
+        assert f(FAKE, 64, FAKE, 64, 16, 64, FAKE, FAKE, FAKE, None) == 5

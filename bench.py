@@ -139,7 +139,8 @@ def ceilings(dev, stream) -> dict:
             "hbm_copy_gbs": round(copy_gbs, 1), **stream_gbs,
             "note": "MFMA-only kernel (4 independent v_mfma_f32_32x32x16_f16 chains per wave, one wave per "
                     "SIMD), clock from s_memtime over s_memrealtime; copy of 1 GiB, read + write bytes; "
-                    "streaming probe (nvfp4_hbm_stream_ceiling) over 2 GiB reading only, and writing "
+                    "streaming probe (nvfp4_hbm_stream_ceiling: one workgroup per 16 KiB chunk, dispatched in "
+                    "address order) over 2 GiB reading only, and writing "
                     f"{QUANT_WRITE_SHARE:.4f} byte per byte read (the quantize launch's mix), read + write bytes"}
 
 
@@ -172,6 +173,19 @@ def stream_ceilings(dev, stream) -> dict:
         out[name] = round(best, 1)
     del src, dst
     return out
+
+
+def producer_floor(w, ceil: dict, t_prod: float) -> dict:
+    """The two-pass producer's time if each launch streamed at the probe's rate for its
+    own mix: the absmax launch reads gate and up (read-only rate), the quantize launch
+    reads them again and writes QDATA and scales (the read-write-mix rate)."""
+    n_in = 2 if w.swiglu else 1
+    read = n_in * w.m * w.k * 2
+    quant = producer_single_read_bytes(w.m, w.k, w.swiglu)
+    floor = read / (ceil["hbm_read_only_gbs"] * 1e6) + quant / (ceil["hbm_read_write_mix_gbs"] * 1e6)
+    return {"producer_floor_ms": round(floor, 4), "producer_frac_of_floor": round(floor / t_prod, 4),
+            "producer_floor_frac_of_hbm_peak": round(producer_bytes(w.m, w.k, w.swiglu) / (floor * 1e-3) / 1e9 /
+                                                     PEAK_HBM_GBS, 4)}
 
 
 def cold_times(run_gemm, run_producer, dev, stream, reps: int) -> dict:
@@ -830,7 +844,8 @@ def main() -> int:
         "warm_ms": {"gemm": percentiles(gemm_ms), "producer": percentiles(prod_ms)},
         "cold_ms": cold,
         "ceilings": dict(ceil, gemm_frac_of_mfma_ceiling=round(tflops / ceil["mfma_f16_tflops"], 4),
-                         producer_frac_of_copy=round(prod_gbs / ceil["hbm_copy_gbs"], 4)),
+                         producer_frac_of_copy=round(prod_gbs / ceil["hbm_copy_gbs"], 4),
+                         **producer_floor(w, ceil, t_prod)),
         "step_tflops": round(w.gemm_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "weight_quantize_ms": round(ev_w0.elapsed_time(ev_w1), 4),
         "gemm_distinct_bytes": gemm_bytes(w.m, w.n, w.k),

@@ -309,8 +309,8 @@ int nvfp4_mfma_ceiling(int64_t workgroups, int64_t iters, void* out_dev, int64_t
 /* Not a step of the method: the HBM rate of a plain streaming kernel for a given mix of
  * reads and writes, the ceiling beside which the producer's two launches are read (the
  * absmax launch only reads; the quantize launch writes about 0.14 byte per byte read).
- * A persistent grid reads all read_bytes of src in chunks of
- * nvfp4_hbm_stream_chunk_bytes() bytes, and chunk c writes dst bytes
+ * One workgroup per chunk of nvfp4_hbm_stream_chunk_bytes() bytes reads all read_bytes
+ * of src (a one-shot grid dispatched in address order), and chunk c writes dst bytes
  * [c * w, (c + 1) * w) with w = 16 * floor(write_bytes / 16 / chunks), so
  * 16 * chunks * floor(write_bytes / (16 * chunks)) bytes are written in all.
  * src_dev: 16-byte aligned, read_bytes a positive multiple of the chunk size; dst_dev:

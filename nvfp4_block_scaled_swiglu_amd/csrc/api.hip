@@ -171,6 +171,9 @@ int check_quant_args(const void* x, int64_t ldx, const void* u, int64_t ldu, boo
   if (ldx < k || (swiglu && ldu < k))
     return fail(NVFP4_ERR_INVALID_ARG, "row stride below k (ld=%lld, %lld, k=%lld)", (long long)ldx,
                 (long long)ldu, (long long)k);
+  // the kernels address a 128-row item with 32-bit offsets from its base
+  if (k > ((int64_t)1 << 23) || ldx > ((int64_t)1 << 23) || (swiglu && ldu > ((int64_t)1 << 23)))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k and row strides above 2^23 elements are not supported");
   if (ldx % 8 != 0 || (swiglu && ldu % 8 != 0))
     return fail(NVFP4_ERR_MISALIGNED, "row strides must be multiples of 8 elements");
   if (!aligned16(x) || (swiglu && !aligned16(u)) || !aligned16(qdata) || !aligned16(scales) || ((uintptr_t)g & 3u) ||
@@ -400,8 +403,9 @@ int nvfp4_hbm_stream_ceiling(const void* src_dev, int64_t read_bytes, void* dst_
                              void* stream) {
   const int64_t chunk = nvfp4::hbm_stream_chunk_bytes();
   if (!src_dev || !dst_dev) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
-  if (read_bytes <= 0 || read_bytes % chunk != 0)
-    return fail(NVFP4_ERR_INVALID_ARG, "read_bytes must be a positive multiple of %lld", (long long)chunk);
+  if (read_bytes <= 0 || read_bytes % chunk != 0 || read_bytes / chunk > 0x7FFFFFFF)
+    return fail(NVFP4_ERR_INVALID_ARG, "read_bytes must be a positive multiple of %lld (at most 2^31 chunks)",
+                (long long)chunk);
   if (write_bytes < 0 || write_bytes > read_bytes || write_bytes % 16 != 0)
     return fail(NVFP4_ERR_INVALID_ARG, "write_bytes must be a multiple of 16 in [0, read_bytes]");
   if (!aligned16(src_dev) || !aligned16(dst_dev)) return fail(NVFP4_ERR_MISALIGNED, "pointers must be 16-byte aligned");

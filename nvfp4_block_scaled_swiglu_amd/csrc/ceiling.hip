@@ -52,43 +52,43 @@ hipError_t launch_mfma_ceiling(uint64_t* out, int64_t workgroups, int64_t iters,
   return hipGetLastError();
 }
 
-// HBM streaming probe. The source is cut into chunks of kStreamChunk bytes; a persistent
-// grid walks them (chunk c by workgroup c mod gridDim.x), each thread loading 4 x 16 bytes
-// of the chunk with all four loads in flight before their use. For a write share w (bytes
-// written per byte read, w <= 1), each chunk also stores its share of the destination,
-// whole 16-byte pieces from the first threads: chunk c writes dst bytes
-// [c * wpc, (c + 1) * wpc), wpc = write_bytes / chunks. The loaded words are folded into an
-// XOR that is stored only if it equals a value the source never yields (so the loads stay
-// live without extra traffic).
+// HBM streaming probe. The source is cut into chunks of kStreamChunk bytes and each
+// workgroup streams one chunk and exits (a one-shot grid, dispatched in address order:
+// the fastest form measured on this device, ahead of persistent grids that walk the
+// chunks). Each thread loads 4 x 16 bytes of its chunk with all four loads in flight
+// before their use. For a write share w (bytes written per byte read, w <= 1), each chunk
+// also stores its share of the destination, whole 16-byte pieces from the first threads:
+// chunk c writes dst bytes [c * wpc, (c + 1) * wpc), wpc = write_bytes / chunks. The
+// loaded words are folded into an XOR that is stored only if it equals a value the
+// source never yields (so the loads stay live without extra traffic).
 constexpr int kStreamThreads = 256;
 constexpr int64_t kStreamChunk = kStreamThreads * 64;  // 16 KiB
 
-__global__ void __launch_bounds__(kStreamThreads) hbm_stream_kernel(const u32x4_t* __restrict__ src, int64_t chunks,
+__global__ void __launch_bounds__(kStreamThreads) hbm_stream_kernel(const u32x4_t* __restrict__ src,
                                                                   u32x4_t* __restrict__ dst, int64_t wpc16,
                                                                   uint32_t never) {
   const int t = threadIdx.x;
+  const int64_t c = blockIdx.x;
+  const u32x4_t* p = src + c * (kStreamChunk / 16);
+  u32x4_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = p[j * kStreamThreads + t];
   uint32_t acc = 0;
-  for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
-    const u32x4_t* p = src + c * (kStreamChunk / 16);
-    u32x4_t v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = p[j * kStreamThreads + t];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
-    for (int64_t i = t; i < wpc16; i += kStreamThreads) {
-      const u32x4_t w = {acc, (uint32_t)i, (uint32_t)c, 0u};
-      dst[c * wpc16 + i] = w;
-    }
+  for (int j = 0; j < 4; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+  for (int64_t i = t; i < wpc16; i += kStreamThreads) {
+    const u32x4_t w = {acc, (uint32_t)i, (uint32_t)c, 0u};
+    dst[c * wpc16 + i] = w;
   }
   if (acc == never) dst[0][0] = acc;
 }
 
-hipError_t launch_hbm_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, int workgroups,
+hipError_t launch_hbm_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, int /*workgroups*/,
                              hipStream_t stream) {
   const int64_t chunks = read_bytes / kStreamChunk;
   const int64_t wpc16 = write_bytes / 16 / chunks;
-  hbm_stream_kernel<<<dim3((unsigned)workgroups), dim3(kStreamThreads), 0, stream>>>(
-      (const u32x4_t*)src, chunks, (u32x4_t*)dst, wpc16, 0xFFFFFFFFu);
+  hbm_stream_kernel<<<dim3((unsigned)chunks), dim3(kStreamThreads), 0, stream>>>((const u32x4_t*)src, (u32x4_t*)dst,
+                                                                              wpc16, 0xFFFFFFFFu);
   return hipGetLastError();
 }
 

@@ -31,3 +31,10 @@ def test_only_producer_two_pass_and_single_read(gpu):
     d1 = run_bench("--only-producer", "--single-read")
     assert d2["producer_ms"] > 0 and d1["producer_ms"] > 0
     assert d1["algorithmic_bytes"] < d2["algorithmic_bytes"]
+
+
+def test_profile_step_with_copy_calibration(gpu):
+    """The timed step alone (the profiler's command): producer and GEMM timings."""
+    d = run_bench("--profile-step", "--copy-bytes", str(1 << 24))
+    assert d["mode"] == "profile-step" and d["producer_ms"] > 0 and d["gemm_ms"] > 0
+    assert d["dispatches_per_kernel"] == 3 and d["copy_gbs"] > 0

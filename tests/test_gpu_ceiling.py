@@ -17,3 +17,26 @@ def test_ceiling_reports_every_wave(gpu):
     assert (o[:, 0] > 0).all() and (o[:, 1] > 0).all()
     ghz = (o[:, 0].double() / (o[:, 1].double() / 100e6) / 1e9)
     assert ((ghz > 0.3) & (ghz < 4.0)).all(), ghz.tolist()
+
+
+def test_hbm_stream_probe_writes_its_share(gpu):
+    """The streaming probe reads every chunk and writes exactly the bytes it reports:
+    chunk c fills dst[c * w, (c + 1) * w) with words derived from its own index, and the
+    bytes after the written share keep their initial value."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    chunk = nv.lib().nvfp4_hbm_stream_chunk_bytes()
+    chunks = 64
+    src = torch.ones(chunks * chunk // 4, dtype=torch.int32, device=gpu)
+    dst = torch.full((chunks * chunk // 4,), -7, dtype=torch.int32, device=gpu)
+    print(f"[stream] {chunks} chunks of {chunk} B, write share 1/8", flush=True)
+    written = nv.nvfp4_hbm_stream_ceiling(src, chunks * chunk, dst, chunks * chunk // 8)
+    torch.cuda.synchronize()
+    assert written == chunks * chunk // 8
+    d = dst.cpu().view(-1, 4)  # 16-byte pieces: (xor, piece index, chunk index, 0)
+    per = chunk // 8 // 16
+    pieces = d[: chunks * per]
+    assert (pieces[:, 1] == torch.arange(chunks * per) % per).all()
+    assert (pieces[:, 2] == torch.arange(chunks * per) // per).all()
+    assert (pieces[:, 3] == 0).all()
+    assert (dst.cpu()[chunks * per * 4:] == -7).all()

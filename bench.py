@@ -175,6 +175,33 @@ def stream_ceilings(dev, stream) -> dict:
     return out
 
 
+def gemm_clock(a, wq, d, dev, reps: int = 5) -> dict:
+    """The shader clock during the GEMM: the same kernel on the same operands, launched
+    through nvfp4_gemm_bf16out_clock, whose workgroups stamp their shader-clock cycles
+    (s_memtime) and 100 MHz real-time ticks (s_memrealtime) from start to end. The clock
+    of a workgroup is cycles / ticks x 100 MHz; p50 over the persistent workgroups of
+    `reps` launches (run after the timed region, back to back)."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    clk = torch.zeros((8192, 2), dtype=torch.int64, device=dev)
+    ghz = []
+    for _ in range(reps):
+        clk.zero_()
+        nv.nvfp4_gemm_bf16out_clock(a, wq, d, clk)
+        torch.cuda.synchronize()
+        c = clk[: cu - cu % 8].double().cpu()
+        c = c[c[:, 1] > 0]
+        ghz += (c[:, 0] / (c[:, 1] / 100e6) / 1e9).tolist()
+    if not ghz:
+        return {"error": "no workgroup stamps"}
+    ghz.sort()
+    return {"ghz_p50": round(ghz[len(ghz) // 2], 3), "ghz_p10": round(ghz[len(ghz) // 10], 3),
+            "ghz_p90": round(ghz[(9 * len(ghz)) // 10], 3), "workgroups": len(ghz),
+            "source": "nvfp4_gemm_bf16out_clock: s_memtime cycles over s_memrealtime ticks per persistent "
+                      "workgroup, same kernel and operands as the timed GEMM"}
+
+
 def producer_floor(w, ceil: dict, t_prod: float) -> dict:
     """The two-pass producer's time if each launch streamed at the probe's rate for its
     own mix: the absmax launch reads gate and up (read-only rate), the quantize launch
@@ -383,13 +410,16 @@ def profile_step(w, args, dev) -> int:
     torch.cuda.synchronize()
     t_prod = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs)
     t_gemm = statistics.fmean(e[1].elapsed_time(e[2]) for e in evs)
+    clock = gemm_clock(a, wq, d, dev)  # after the timed launches: 5 more, stamped
     out = {"mode": "profile-step", "workload": w.name, "steps": args.steps, "warmup": args.warmup,
+           "gemm_clock": clock,
            "producer_ms": round(t_prod, 4), "gemm_ms": round(t_gemm, 4),
            "gemm_tflops": round(w.gemm_flops / (t_gemm * 1e-3) / 1e12, 2),
            "producer_gbs": round(producer_bytes(w.m, w.k, w.swiglu) / (t_prod * 1e-3) / 1e9, 1),
            "dispatches_per_kernel": args.warmup + args.steps,
            "note": "the activation producer is two launches (absmax, then quantize); the weight's plain "
-                   "quantization (one absmax and one quantize launch of the plain kernels) runs once before"}
+                   "quantization (one absmax and one quantize launch of the plain kernels) runs once before; "
+                   "5 clock-stamped GEMM launches follow the timed steps"}
     if args.copy_bytes > 0:
         out.update(copy_calibration(args.copy_bytes, args.steps, dev, stream))
     print(json.dumps(out), flush=True)
@@ -760,6 +790,7 @@ def main() -> int:
     cold = cold_times(lambda: nv.nvfp4_gemm_bf16out(a, wq, out=d), producer_once, dev, stream,
                       min(args.steps, 10))
     ceil = ceilings(dev, stream)
+    clock = gemm_clock(a, wq, d, dev)
     import statistics
     t_prod = statistics.fmean(prod_ms)
     t_gemm = statistics.fmean(gemm_ms)
@@ -846,6 +877,7 @@ def main() -> int:
         "ceilings": dict(ceil, gemm_frac_of_mfma_ceiling=round(tflops / ceil["mfma_f16_tflops"], 4),
                          producer_frac_of_copy=round(prod_gbs / ceil["hbm_copy_gbs"], 4),
                          **producer_floor(w, ceil, t_prod)),
+        "gemm_clock": clock,
         "step_tflops": round(w.gemm_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "weight_quantize_ms": round(ev_w0.elapsed_time(ev_w1), 4),
         "gemm_distinct_bytes": gemm_bytes(w.m, w.n, w.k),

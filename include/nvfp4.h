@@ -321,6 +321,20 @@ int64_t nvfp4_hbm_stream_chunk_bytes(void);
 int nvfp4_hbm_stream_ceiling(const void* src_dev, int64_t read_bytes, void* dst_dev, int64_t write_bytes,
                              void* stream);
 
+/* Not a step of the method: nvfp4_gemm_bf16out (same arguments, same kernel and
+ * output) with shader-clock stamps, for the clock the GEMM runs at. Workgroup
+ * b < slots writes its shader-clock cycles (s_memtime) from start to end to
+ * clk_dev[2 b] and its 100 MHz real-time ticks (s_memrealtime) over the same span to
+ * clk_dev[2 b + 1] (uint64 each); their ratio is the clock during its work.
+ * clk_dev: 8-byte aligned device memory of 16 * slots bytes, owned by the caller;
+ * slots in [1, 2^20] (the persistent grid has one workgroup per CU, plus the
+ * quarter-tile tail). Errors as nvfp4_gemm_bf16out, plus NVFP4_ERR_INVALID_ARG /
+ * NVFP4_ERR_MISALIGNED for the clock buffer. */
+int nvfp4_gemm_bf16out_clock(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
+                             const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
+                             void* d_dev, int64_t m_padded, int64_t n, int64_t k, void* clk_dev, int64_t slots,
+                             void* stream);
+
 /* ---- diagnostics -------------------------------------------------------------------------- */
 
 /* Static text for a status code. The statuses are what a caller's guard tests

@@ -58,6 +58,7 @@ SIGNATURES = {
     "nvfp4_quantize_swiglu_amax": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_quantize_amax": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_gemm_bf16out": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "nvfp4_gemm_bf16out_clock": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "nvfp4_gemm_bf16out_fused": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_gemm_swiglu_pair": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P]),
     "nvfp4_silu_bf16": (_INT, [_P, _P, _I64, _P]),
@@ -440,6 +441,21 @@ def nvfp4_gemm_swiglu_pair(a: Nvfp4Tensor, w: Nvfp4Tensor, bias=None, amax=None,
                  _stream_handle(stream), strict=strict):
         return None
     return gate_out, up_out
+
+
+def nvfp4_gemm_bf16out_clock(a: Nvfp4Tensor, w: Nvfp4Tensor, out, clk, stream=None):
+    """nvfp4_gemm_bf16out into `out` with per-workgroup shader-clock stamps in `clk`
+    (an int64 CUDA tensor [slots, 2]: cycles, 100 MHz ticks); a measurement aid."""
+    import torch
+    m_pad, n = a.padded_rows, w.rows
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (m_pad, n) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [m_padded, n] tensor")
+    if clk.dtype != torch.int64 or clk.dim() != 2 or clk.shape[1] != 2 or not clk.is_contiguous():
+        raise ValueError("clk must be a contiguous int64 [slots, 2] tensor")
+    _call("nvfp4_gemm_bf16out_clock", a.qdata.data_ptr(), a.scales.data_ptr(), a.global_scale.data_ptr(),
+          w.qdata.data_ptr(), w.scales.data_ptr(), w.global_scale.data_ptr(), out.data_ptr(), m_pad, n, a.k,
+          clk.data_ptr(), clk.shape[0], _stream_handle(stream))
+    return out
 
 
 def nvfp4_mfma_ceiling(workgroups: int, iters: int, stream=None):

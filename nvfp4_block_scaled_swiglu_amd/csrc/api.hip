@@ -336,6 +336,20 @@ int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const 
                      m_padded, n, k, nvfp4::GemmEpilogue(), stream);
 }
 
+int nvfp4_gemm_bf16out_clock(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
+                             const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
+                             void* d_dev, int64_t m_padded, int64_t n, int64_t k, void* clk_dev, int64_t slots,
+                             void* stream) {
+  if (!clk_dev || slots < 1 || slots > (int64_t)1 << 20)
+    return fail(NVFP4_ERR_INVALID_ARG, "clock stamps need a buffer and 1..2^20 slots");
+  if ((uintptr_t)clk_dev & 7u) return fail(NVFP4_ERR_MISALIGNED, "clock buffer must be 8-byte aligned");
+  nvfp4::GemmEpilogue ep;
+  ep.clk = (uint64_t*)clk_dev;
+  ep.clk_slots = (int)slots;
+  return gemm_common(a_qdata_dev, a_scales_dev, a_global_dev, w_qdata_dev, w_scales_dev, w_global_dev, d_dev,
+                     m_padded, n, k, ep, stream);
+}
+
 int nvfp4_gemm_bf16out_fused(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
                              const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
                              void* d_dev, int64_t m_padded, int64_t n, int64_t k, const void* bias_dev,

@@ -46,6 +46,10 @@ struct GemmEpilogue {
   float* amax = nullptr;
   int64_t amax_rows = 0;
   const uint16_t* silu_table = nullptr;
+  // measurement aid: workgroup b < clk_slots writes its shader-clock cycles and
+  // 100 MHz ticks from start to end to clk[2b], clk[2b + 1] (null: nothing recorded)
+  uint64_t* clk = nullptr;
+  int clk_slots = 0;
 };
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {

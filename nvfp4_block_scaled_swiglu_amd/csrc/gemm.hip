@@ -836,8 +836,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
 }
 
 template <int EPI>
-__global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+__device__ __forceinline__ void gemm_body(const GemmArgs& a, unsigned char* smem) {
   // Tiles (256 x 256) are numbered m-band-major: band = 8 M-tiles, within a band M
   // first. Workgroups [0, big_tiles) run tiles [0, big_tiles) whole, remapped so that
   // each XCD (workgroups are dispatched round-robin over the 8 XCDs) owns one
@@ -886,6 +885,26 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
     const int64_t qm0 = m0 + (quarter >> 1) * kTileQuarter, qn0 = n0 + (quarter & 1) * kTileQuarter;
     if (qm0 >= a.m_pad || qn0 >= a.n) return;  // a quarter wholly past the padded output
     run_tile<2, 2, EPI>(a, qm0, qn0, smem);
+  }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // clock stamps in the plain kernel only (the fused kernels have no registers to spare)
+  const bool stamp = EPI == 0 && a.ep.clk != nullptr && (int)blockIdx.x < a.ep.clk_slots;
+  uint64_t c0 = 0, t0 = 0;
+  if (stamp) {
+    c0 = __builtin_amdgcn_s_memtime();
+    t0 = __builtin_amdgcn_s_memrealtime();
+  }
+  gemm_body<EPI>(a, smem);
+  if (stamp) {
+    const uint64_t c1 = __builtin_amdgcn_s_memtime(), t1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+      a.ep.clk[2 * blockIdx.x] = c1 - c0;
+      a.ep.clk[2 * blockIdx.x + 1] = t1 - t0;
+    }
   }
 }
 

@@ -38,3 +38,4 @@ def test_traffic_summaries_match_the_sources():
     so the bench line reports their traffic rather than null."""
     assert bench.measured_gemm_traffic() is not None
     assert bench.measured_traffic(bench.PRODUCER_TRAFFIC_SUMMARY, bench.PRODUCER_SOURCES) is not None
+    assert bench.measured_traffic(bench.SINGLE_READ_TRAFFIC_SUMMARY, bench.PRODUCER_SOURCES) is not None

@@ -301,3 +301,13 @@ def test_noalloc_entry_validation():
     import torch
     if not torch.cuda.is_available():
         assert f(FAKE, 64, FAKE, 64, 16, 64, FAKE, FAKE, FAKE, None) == 5
+
+
+def test_gemm_clock_entry_validation():
+    """The clock-stamped GEMM validates its clock buffer, then as nvfp4_gemm_bf16out."""
+    f = nv.lib().nvfp4_gemm_bf16out_clock
+    g = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 16, 64)
+    assert f(*g, None, 4, None) == 1
+    assert f(*g, FAKE, 0, None) == 1
+    assert f(*g, FAKE + 4, 4, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 64, FAKE, 4, None) == 2

@@ -40,3 +40,30 @@ def test_hbm_stream_probe_writes_its_share(gpu):
     assert (pieces[:, 2] == torch.arange(chunks * per) // per).all()
     assert (pieces[:, 3] == 0).all()
     assert (dst.cpu()[chunks * per * 4:] == -7).all()
+
+
+def test_gemm_clock_stamps_leave_the_output_unchanged(gpu):
+    """The clock-stamped GEMM (a measurement aid) writes the same output as
+    nvfp4_gemm_bf16out, bit for bit, and every persistent workgroup's stamps give a
+    clock in the device's range."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    import synth
+    from tests import parity
+    cu = torch.cuda.get_device_properties(gpu).multi_processor_count
+    w = synth.Workload("clock", m=3 * 1024, n=1024, k=512, seed=31, swiglu=True)  # 48 tiles
+    gate, up = w.activations()
+    a, *_ = parity.run_quantize(gate, up, gpu)
+    wt, *_ = parity.run_quantize(w.weight(), None, gpu)
+    print(f"[clock] {w.m}x{w.n}x{w.k}", flush=True)
+    d0 = nv.nvfp4_gemm_bf16out(a, wt)
+    d1 = torch.empty_like(d0)
+    clk = torch.zeros((1024, 2), dtype=torch.int64, device=gpu)
+    nv.nvfp4_gemm_bf16out_clock(a, wt, d1, clk)
+    torch.cuda.synchronize()
+    assert torch.equal(d0, d1)
+    c = clk.cpu()
+    used = c[:, 1] > 0
+    assert used.sum() >= min(48, cu - cu % 8)
+    ghz = c[used, 0].double() / (c[used, 1].double() / 100e6) / 1e9
+    assert ((ghz > 0.3) & (ghz < 4.0)).all(), ghz.tolist()

@@ -58,11 +58,11 @@ def test_swizzle_is_a_tiled_bijection(rows, k):
     cp = oracle.scale_cols(k)
     r = np.arange(rp, dtype=np.int64)[:, None]
     c = np.arange(cp, dtype=np.int64)[None, :]
-    # vectorised evaluation of the oracle's offset, checked against its scalar form
+    # the oracle's offsets on a grid sample
     off = np.vectorize(oracle.scale_offset, otypes=[np.int64])(
         np.broadcast_to(r, (rp, cp))[:: max(1, rp // 64), :: max(1, cp // 16)],
         np.broadcast_to(c, (rp, cp))[:: max(1, rp // 64), :: max(1, cp // 16)], cp)
-    full = ((r >> 7) * (cp // 4) + (c >> 2)) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4 + (c & 3)
+    full = tiled_positions(rp, cp)  # the storage order stated as reshapes (below), no offset formula
     np.testing.assert_array_equal(off, full[:: max(1, rp // 64), :: max(1, cp // 16)])
     flat = full.ravel()
     assert flat.min() == 0 and flat.max() == rp * cp - 1

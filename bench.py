@@ -69,10 +69,9 @@ def measured_gemm_traffic():
     return measured_traffic(GEMM_TRAFFIC_SUMMARY, GEMM_SOURCES)
 
 
-def measured_traffic(summary: str, sources):
-    """HBM bytes per launch from a committed counter summary (FETCH_SIZE and
-    WRITE_SIZE, each scaled by a copy kernel of known size), or None when the summary
-    was taken on a different kernel source than the one built here."""
+def summary_values(summary: str, sources):
+    """The value block of a committed counter summary, or None when the summary was
+    taken on a different kernel source than the one built here."""
     import hashlib
     try:
         h = hashlib.sha256()
@@ -85,10 +84,39 @@ def measured_traffic(summary: str, sources):
                 if ":" in line and not line.startswith(("#", "|", "`")):
                     k, _, v = line.partition(":")
                     vals[k.strip()] = v.strip()
-        if vals.get("source_sha256") != h.hexdigest():
+        return vals if vals.get("source_sha256") == h.hexdigest() else None
+    except OSError:
+        return None
+
+
+def measured_traffic(summary: str, sources):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by a copy kernel of known size), or None when the summary
+    was taken on a different kernel source than the one built here."""
+    try:
+        v = summary_values(summary, sources)
+        return None if v is None else int(v["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_run(summary: str, sources, work: float, peak: float, unit_scale: float):
+    """Where the `traffic` figure comes from: separate rocprofv3 runs of
+    `bench.py --profile-step` on this kernel source, not this process. Gives that
+    command's kernel-trace time per launch and the rate and fraction of peak at that
+    time (work per launch / unit_scale per second)."""
+    try:
+        v = summary_values(summary, sources)
+        if v is None or "trace_ms_per_launch" not in v:
             return None
-        return int(vals["traffic_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        ms = float(v["trace_ms_per_launch"])
+        rate = work / (ms * 1e-3) / unit_scale
+        return {"summary": summary, "source": "separate rocprofv3 runs (bench.py --profile-step), not this process",
+                "trace_ms_per_launch": ms, "achieved_at_trace_ms": round(rate, 1),
+                "frac_at_trace_ms": round(rate / peak, 4),
+                "counter_run_ms_per_launch": (float(v["counter_run_ms_per_launch"])
+                                              if "counter_run_ms_per_launch" in v else None)}
+    except (KeyError, ValueError):
         return None
 
 
@@ -175,22 +203,33 @@ def stream_ceilings(dev, stream) -> dict:
     return out
 
 
-def gemm_clock(a, wq, d, dev, reps: int = 5) -> dict:
+def gemm_clock(a, wq, d, dev, reps: int = 5, warm: int = 5) -> dict:
     """The shader clock during the GEMM: the same kernel on the same operands, launched
     through nvfp4_gemm_bf16out_clock, whose workgroups stamp their shader-clock cycles
     (s_memtime) and 100 MHz real-time ticks (s_memrealtime) from start to end. The clock
     of a workgroup is cycles / ticks x 100 MHz; p50 over the persistent workgroups of
-    `reps` launches (run after the timed region, back to back)."""
+    `reps` stamped launches. They run back to back after `warm` plain launches, with no
+    host synchronisation in between (a launch after an idle gap runs slower while the
+    clocks ramp), each timed with events so that its duration can be set beside the
+    timed launches'."""
     import torch
     import nvfp4_block_scaled_swiglu_amd as nv
     cu = torch.cuda.get_device_properties(dev).multi_processor_count
-    clk = torch.zeros((8192, 2), dtype=torch.int64, device=dev)
+    clks = torch.zeros((reps, 8192, 2), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warm):
+        nv.nvfp4_gemm_bf16out(a, wq, out=d)
+    evs = []
+    for r in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        nv.nvfp4_gemm_bf16out_clock(a, wq, d, clks[r])
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
     ghz = []
-    for _ in range(reps):
-        clk.zero_()
-        nv.nvfp4_gemm_bf16out_clock(a, wq, d, clk)
-        torch.cuda.synchronize()
-        c = clk[: cu - cu % 8].double().cpu()
+    for r in range(reps):
+        c = clks[r, : cu - cu % 8].double().cpu()
         c = c[c[:, 1] > 0]
         ghz += (c[:, 0] / (c[:, 1] / 100e6) / 1e9).tolist()
     if not ghz:
@@ -198,8 +237,10 @@ def gemm_clock(a, wq, d, dev, reps: int = 5) -> dict:
     ghz.sort()
     return {"ghz_p50": round(ghz[len(ghz) // 2], 3), "ghz_p10": round(ghz[len(ghz) // 10], 3),
             "ghz_p90": round(ghz[(9 * len(ghz)) // 10], 3), "workgroups": len(ghz),
-            "source": "nvfp4_gemm_bf16out_clock: s_memtime cycles over s_memrealtime ticks per persistent "
-                      "workgroup, same kernel and operands as the timed GEMM"}
+            "launch_ms": [round(x.elapsed_time(y), 4) for x, y in evs],
+            "source": f"nvfp4_gemm_bf16out_clock: s_memtime cycles over s_memrealtime ticks per persistent "
+                      f"workgroup, same kernel and operands as the timed GEMM, {reps} launches back to back "
+                      f"after {warm} plain ones"}
 
 
 def producer_floor(w, ceil: dict, t_prod: float) -> dict:
@@ -410,7 +451,7 @@ def profile_step(w, args, dev) -> int:
     torch.cuda.synchronize()
     t_prod = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs)
     t_gemm = statistics.fmean(e[1].elapsed_time(e[2]) for e in evs)
-    clock = gemm_clock(a, wq, d, dev)  # after the timed launches: 5 more, stamped
+    clock = gemm_clock(a, wq, d, dev)  # after the timed launches: 5 warm, then 5 stamped
     out = {"mode": "profile-step", "workload": w.name, "steps": args.steps, "warmup": args.warmup,
            "gemm_clock": clock,
            "producer_ms": round(t_prod, 4), "gemm_ms": round(t_gemm, 4),
@@ -833,6 +874,8 @@ def main() -> int:
             "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
             "traffic": measured_gemm_traffic() if w.name == "fc2_canonical" else None,
             "traffic_summary": GEMM_TRAFFIC_SUMMARY,
+            "traffic_run": (traffic_run(GEMM_TRAFFIC_SUMMARY, GEMM_SOURCES, w.gemm_flops, PEAK_MFMA_TFLOPS, 1e12)
+                            if w.name == "fc2_canonical" else None),
             "kernel": "nvfp4::gemm_kernel<0>",
             "algorithmic_per_launch": f"{w.gemm_flops:.4e} FLOP (2*M*N*K, logical M)",
             "avg_launch_ms": round(t_gemm, 4),
@@ -846,6 +889,8 @@ def main() -> int:
             "traffic": (measured_traffic(PRODUCER_TRAFFIC_SUMMARY, PRODUCER_SOURCES)
                         if w.name == "fc2_canonical" else None),
             "traffic_summary": PRODUCER_TRAFFIC_SUMMARY,
+            "traffic_run": (traffic_run(PRODUCER_TRAFFIC_SUMMARY, PRODUCER_SOURCES, pbytes, PEAK_HBM_GBS, 1e9)
+                            if w.name == "fc2_canonical" else None),
             "kernel": ("nvfp4::producer_absmax_kernel<1> then nvfp4::producer_kernel<1, false>" if w.swiglu else
                        "nvfp4::producer_absmax_kernel<0> then nvfp4::producer_kernel<0, false>"),
             "algorithmic_per_launch": f"{pbytes} B per call of its two launches (inputs read twice, QDATA + "

@@ -222,7 +222,16 @@ int nvfp4_quantize_amax(const void* x_dev, int64_t ld_x, int64_t rows, int64_t k
  * w_qdata_dev, w_scales_dev : weight [n, k] as written by nvfp4_quantize(rows = n).
  * d_dev                     : out, bf16 [m_padded, n] row-major, 16-byte aligned.
  * m_padded % 16 == 0, n % 16 == 0, k % 64 == 0. Rows of D whose activation rows
- * are zero padding come out +0. Takes no workspace.
+ * are zero padding come out +0. Takes no workspace from the caller.
+ * Scheduling state: when the output has more 256 x 256 tiles than the device has
+ * CUs, the workgroups take their tiles from run-time queues, so that faster XCDs
+ * take more tiles. Here that means one persistent workgroup per CU; in the fused
+ * entries below, one tile per workgroup. The library keeps 64 queue sets per
+ * device (static device memory, 8 KiB) for all GEMM entries together. Launch i on
+ * a device uses set i % 64, and the launch leaves its set cleared when it ends. So
+ * up to 64 GEMM launches may be in flight at once on one device, from any streams.
+ * A launch captured in a HIP graph keeps its set: replays of one captured launch
+ * must not overlap each other.
  */
 int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
                        const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
@@ -249,8 +258,8 @@ int nvfp4_gemm_bf16out(const void* a_qdata_dev, const void* a_scales_dev, const 
  *                stream): each element is read before the same thread writes it.
  * Every other argument as nvfp4_gemm_bf16out. Rows past the logical rows of the
  * activation come out RN_bf16(bias) (zero activation rows), combined with the
- * residual like any other row. No workspace; errors as nvfp4_gemm_bf16out, plus
- * NVFP4_ERR_INVALID_ARG for a gate without a residual.
+ * residual like any other row. No workspace; tile queues and errors as
+ * nvfp4_gemm_bf16out, plus NVFP4_ERR_INVALID_ARG for a gate without a residual.
  */
 int nvfp4_gemm_bf16out_fused(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
                              const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,
@@ -278,7 +287,8 @@ int nvfp4_gemm_bf16out_fused(const void* a_qdata_dev, const void* a_scales_dev, 
  *                    running maximum; a non-negative number) before the call;
  *                    4-byte aligned. Calls that fold into one amax may overlap.
  * amax_rows        : the logical rows, 0 <= amax_rows <= m_padded.
- * n_half           : a positive multiple of 8. Other arguments as nvfp4_gemm_bf16out.
+ * n_half           : a positive multiple of 8. Other arguments, the tile queues and
+ *                    the errors as nvfp4_gemm_bf16out.
  */
 int nvfp4_gemm_swiglu_pair(const void* a_qdata_dev, const void* a_scales_dev, const float* a_global_dev,
                            const void* w_qdata_dev, const void* w_scales_dev, const float* w_global_dev,

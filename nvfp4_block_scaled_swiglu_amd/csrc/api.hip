@@ -32,7 +32,7 @@ size_t gemm_smem_bytes(int kind);
 const void* gemm_kernel_ptr(int kind);
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
-                       const GemmEpilogue& ep, int cu_count, hipStream_t stream);
+                       const GemmEpilogue& ep, int cu_count, uint64_t* sched, hipStream_t stream);
 hipError_t launch_mfma_ceiling(uint64_t* out, int64_t workgroups, int64_t iters, hipStream_t stream);
 hipError_t launch_hbm_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, int workgroups,
                              hipStream_t stream);
@@ -51,6 +51,8 @@ struct DeviceState {
   std::atomic<bool> ready{false};
   const uint16_t* silu_table = nullptr;
   void* scratch = nullptr;  // this device's copy of `scratch` (hipGetSymbolAddress)
+  uint64_t* gemm_queues = nullptr;  // this device's copy of `gemm_queues`
+  std::atomic<uint32_t> gemm_launches{0};  // picks the queue set of each plain GEMM launch
   int producer_blocks[3] = {0, 0, 0};  // persistent grid per producer mode
   int cu_count = 0;
   char arch[64] = {0};
@@ -67,6 +69,11 @@ DeviceState g_dev[kMaxDevices];
 // Every call on a GPU shares it, and each call writes every slot it reads, so nothing
 // needs clearing between calls; calls that overlap in time on one GPU race.
 static __device__ __align__(256) uint32_t scratch[nvfp4::kMaxPartials];
+
+// Tile queues of the plain GEMM's persistent grid (zero at load). Launch i on a device
+// uses set i % kGemmQueueSets; its last workgroup leaves the set zeroed again, so up to
+// kGemmQueueSets plain GEMM launches may run at the same time on one GPU.
+static __device__ __align__(256) uint64_t gemm_queues[nvfp4::kGemmQueueSets * nvfp4::kGemmQueueWords];
 
 namespace {
 std::mutex g_init_mutex;
@@ -142,6 +149,10 @@ int ensure_device(DeviceState** out) {
   e = hipGetSymbolAddress(&st.scratch, HIP_SYMBOL(scratch));
   if (e != hipSuccess || !st.scratch)
     return fail(NVFP4_ERR_LAUNCH, "producer scratch address: %s", hipGetErrorString(e));
+  void* q = nullptr;
+  e = hipGetSymbolAddress(&q, HIP_SYMBOL(gemm_queues));
+  if (e != hipSuccess || !q) return fail(NVFP4_ERR_LAUNCH, "gemm queue address: %s", hipGetErrorString(e));
+  st.gemm_queues = (uint64_t*)q;
   hipStream_t s;
   e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "stream create: %s", hipGetErrorString(e));
@@ -322,9 +333,11 @@ static int gemm_common(const void* a_qdata_dev, const void* a_scales_dev, const 
   if (m_padded == 0) return ok();
   nvfp4::GemmEpilogue ep2 = ep;
   ep2.silu_table = st->silu_table;
+  const uint32_t set = st->gemm_launches.fetch_add(1, std::memory_order_relaxed) % nvfp4::kGemmQueueSets;
+  uint64_t* queues = st->gemm_queues + (size_t)set * nvfp4::kGemmQueueWords;
   hipError_t e = nvfp4::launch_gemm((const uint8_t*)a_qdata_dev, (const uint8_t*)a_scales_dev, a_global_dev,
                                     (const uint8_t*)w_qdata_dev, (const uint8_t*)w_scales_dev, w_global_dev,
-                                    (uint16_t*)d_dev, m_padded, n, k, ep2, st->cu_count, (hipStream_t)stream);
+                                    (uint16_t*)d_dev, m_padded, n, k, ep2, st->cu_count, queues, (hipStream_t)stream);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -29,6 +29,11 @@ struct ProducerWorkspace {
 };
 static_assert(sizeof(ProducerWorkspace) == 4096, "workspace layout");
 
+// Tile-queue words of the plain GEMM's persistent grid: one set of kGemmQueueWords
+// per launch in flight, kGemmQueueSets sets per device (static device memory).
+constexpr int kGemmQueueWords = 16;
+constexpr int kGemmQueueSets = 64;
+
 // What the GEMM does after its K loop (host -> launch_gemm).
 //   kind 0: D = RN_bf16(alpha * acc)
 //   kind 1: D1 = RN_bf16(alpha * acc + bias), D = RN_bf16(res + gate * D1)

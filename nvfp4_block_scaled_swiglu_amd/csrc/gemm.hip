@@ -44,10 +44,15 @@
 // Traversal: tiles are numbered m-band-major in bands of 8 M-tiles, and workgroup
 // ids (dispatched round-robin over the 8 XCDs) are remapped so that each XCD owns
 // one contiguous range of tiles; its 32 concurrent workgroups then share A row
-// bands and W panels in that XCD's L2. The plain kernel runs the whole tiles with
-// one persistent workgroup per CU that walks its XCD's range in the same order; the
-// first two K steps of its next tile are loaded while the current tile's epilogue
-// runs, staged through an LDS area of its own.
+// bands and W panels in that XCD's L2. The plain kernel runs every tile with one
+// persistent workgroup per CU. After its first tile, a workgroup takes the next
+// tile of its XCD's range from a queue at run time, and once that range is used up
+// it takes tiles from the back of the range of the XCD with the most left, then the
+// quarters of the tail: the XCDs hold clocks a few per cent apart under this load,
+// and a fixed split would leave the fast ones idle at the end. The first two K
+// steps of the next tile are loaded while the current tile's epilogue runs, staged
+// through an LDS area of its own. The fused kinds take their tiles from the same
+// queues, one per workgroup, from a grid with a round of spare workgroups.
 #include "common.hpp"
 
 namespace nvfp4 {
@@ -106,6 +111,8 @@ struct GemmArgs {
   int persist_wgs;                             // > 0: workgroups [0, persist_wgs) loop over the whole tiles
   int cgroups;                                 // scale column groups = C / 4
   int ksteps;
+  int quarter_units;                           // 4 x (tiles past big_tiles): the quarter-tile tail
+  uint64_t* sched;                             // the persistent grid's tile queues (TileQueues)
   GemmEpilogue ep;  // the epilogue's operands (kind 1 and 2 kernels)
 };
 
@@ -237,13 +244,102 @@ __device__ __forceinline__ void tile_origin(const GemmArgs& a, int t, int64_t& m
   n0 = (int64_t)(in_band / band_m) * kTileBig;
 }
 
+// ---- tile queues of the persistent grid ----
+// The eight XCDs of the chip hold different clocks under this load (a few per cent
+// apart), so a fixed split of the tiles leaves the fastest XCDs idle at the end. The
+// whole tiles are split into one contiguous range per XCD as before (its 32
+// workgroups then share A row bands and W panels in that XCD's L2), but beyond each
+// workgroup's first tile they are taken at run time:
+//   sched[x], x < 8: XCD x's queue. The low 32 bits count tiles taken from the front
+//     of its range past the `slots` first tiles (which go one to each of its
+//     workgroups), the high 32 bits tiles taken from the back by other XCDs' workgroups
+//     once their own queue is empty. Both kinds of take add 1 to the same word, and a
+//     take succeeds iff front + back before it is below the range's dynamic length, so
+//     every tile is taken exactly once and the front and back never hand out the same
+//     tile.
+//   sched[8]: the next 128 x 128 quarter of the tail tiles, taken after every queue is
+//     empty.
+//   sched[9]: workgroups that have finished taking. The last one clears sched[0..9],
+//     so the words are zero for the next launch that uses them.
+// All of them are agent-scope atomics (the XCDs' L2 caches are not coherent with each
+// other); a take is one atomic with return, issued a K step before its result is used.
+static_assert(kGemmQueueWords >= 10, "a queue set holds the 8 XCD queues, the quarter count and the exit count");
+
+__device__ __forceinline__ void xcd_range(const GemmArgs& a, int x, int& start, int& len) {
+  const int per = a.big_tiles / 8, rem = a.big_tiles % 8;
+  start = x * per + (x < rem ? x : rem);
+  len = per + (x < rem ? 1 : 0);
+}
+
+// the tile of a front take whose atomic returned `old`, or -1 when the queue was empty
+__device__ __forceinline__ int front_tile(const GemmArgs& a, int x, int slots, uint64_t old) {
+  int start, len;
+  xcd_range(a, x, start, len);
+  const int64_t dyn = len > slots ? len - slots : 0;
+  const uint32_t f = (uint32_t)old, b = (uint32_t)(old >> 32);
+  return (int64_t)f + b < dyn ? start + slots + (int)f : -1;
+}
+
+// Wave 0 of a persistent workgroup, all lanes: a tile from the back of the queue with
+// the most tiles left, or -1 when every queue is empty. Lanes 0..7 read the eight
+// queue words at once; lane 0 takes. A failed take means that queue emptied between
+// the read and the take, and the counts only grow, so it reads as empty from then on:
+// after at most 8 failures every queue is empty, and the loop bound is never reached.
+__device__ __forceinline__ int steal_tile(const GemmArgs& a, int slots, int lane) {
+  for (int round = 0; round < 9; ++round) {
+    int left = 0;
+    if (lane < 8) {
+      const uint64_t v = __hip_atomic_load(a.sched + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int start, len;
+      xcd_range(a, lane, start, len);
+      const int64_t l = (int64_t)(len > slots ? len - slots : 0) - (int64_t)(uint32_t)v - (int64_t)(uint32_t)(v >> 32);
+      left = l <= 0 ? 0 : (l < (1 << 24) ? (int)l : (1 << 24) - 1);
+    }
+    int key = left * 8 + (lane & 7);  // the most tiles left, then the highest XCD
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) {
+      const int o = __shfl_xor(key, off, 64);
+      key = key > o ? key : o;
+    }
+    key = __builtin_amdgcn_readfirstlane(key);
+    if (key < 8) return -1;
+    const int y = key & 7;
+    int t = -1;
+    if (lane == 0) {
+      const uint64_t old = __hip_atomic_fetch_add(a.sched + y, (uint64_t)1 << 32, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      int start, len;
+      xcd_range(a, y, start, len);
+      const int64_t dyn = len > slots ? len - slots : 0;
+      const uint32_t f = (uint32_t)old, b = (uint32_t)(old >> 32);
+      if ((int64_t)f + b < dyn) t = start + len - 1 - (int)b;
+    }
+    t = __builtin_amdgcn_readfirstlane(t);
+    if (t >= 0) return t;
+  }
+  return -1;
+}
+
+// LDS of the persistent workgroups: the stages, then per kind the plain kernel's
+// epilogue staging or the SwiGLU pair's candidate lists, then one word that
+// broadcasts a taken tile to the workgroup's waves
+constexpr size_t kPersistStagingBytes = (size_t)kWaves * 32 * (BigTile::TN / WAVES_N * 2 + 16);
+constexpr size_t kCandBytes = (size_t)kWaves * kCand * 4;
+template <int EPI>
+constexpr size_t sched_slot_offset() {
+  return (size_t)kStages * BigTile::StageBytes + (EPI == 0 ? kPersistStagingBytes : EPI == 2 ? kCandBytes : 0);
+}
+constexpr size_t kSchedSlotOffset = sched_slot_offset<0>();
+
 // PERSIST (plain epilogue, whole tiles): after tile (m0, n0) the workgroup goes on with
-// tiles t_next, t_next + t_stride, ... < t_end. The first two K steps of the next
-// tile are loaded while the current tile's epilogue runs; that epilogue stages
-// through its own LDS area, past the pipeline stages.
+// the tiles it takes from the queues (front of XCD `xcd`'s queue, else the back of
+// another's), until none is left. The take for the next tile is issued in the first K
+// step of the current one. The first two K steps of the next tile are loaded while the
+// current tile's epilogue runs; that epilogue stages through its own LDS area, past
+// the pipeline stages.
 template <int FM, int FN, int EPI, bool PERSIST = false>
 __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t n0, unsigned char* smem,
-                                         int t_next = 0, int t_stride = 0, int t_end = 0) {
+                                         int xcd = 0, int slots = 0) {
   using T = TileShape<FM, FN>;
   constexpr int kStageBytes = T::StageBytes, kCodesA = T::CodesA, kCodesW = T::CodesW, kScaleA = T::ScaleA;
   constexpr int kLoads = T::Loads;
@@ -386,8 +482,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
   read_codes(0, 0, ca[0], cw[0]);
   dequant_k(0, 0);
 
-  // one K step; `loads`: issue the loads of step ks + 2; `next`: a step ks + 1 follows
-  auto kstep = [&](int ks, int stage, bool loads, bool next) __attribute__((always_inline)) {
+  // one K step; `loads`: issue the loads of step ks + 2; `next`: a step ks + 1 follows;
+  // `take`: thread 0 takes the workgroup's next tile (the result is waited for with the
+  // next K step's loads, a K step later)
+  uint64_t qold = 0;
+  auto kstep = [&](int ks, int stage, bool loads, bool next, bool take) __attribute__((always_inline)) {
     const int next_stage = stage == 2 ? 0 : stage + 1;
     const int far_stage = next_stage == 2 ? 0 : next_stage + 1;
 #pragma unroll
@@ -408,6 +507,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
         stage_barrier();
         read_scales(next_stage, nsa, nsw);
         read_codes(next_stage, 0, ca[0], cw[0]);
+        if (take && tid == 0)
+          qold = __hip_atomic_fetch_add(a.sched + xcd, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (kk < 7) {
         dequant_k(kk + 1, nxt);
@@ -433,25 +534,47 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
   };
 
   int stage = 0, ks = 0;
+  bool took = false;
+  if constexpr (PERSIST) {
+    if (nks > 2) {
+      kstep(0, 0, true, true, true);
+      stage = 1;
+      ks = 1;
+      took = true;
+    }
+  }
   for (; ks + 2 < nks; ++ks) {
-    kstep(ks, stage, true, true);
+    kstep(ks, stage, true, true, false);
     stage = stage == 2 ? 0 : stage + 1;
   }
   if (ks + 1 < nks) {
-    kstep(ks, stage, false, true);
+    kstep(ks, stage, false, true, false);
     stage = stage == 2 ? 0 : stage + 1;
     ++ks;
   }
-  kstep(ks, stage, false, false);
+  kstep(ks, stage, false, false, false);
 
   // the epilogue's tile; PERSIST moves (m0, n0) on to the next tile and starts its loads
   const int64_t em0 = m0, en0 = n0;
   bool more = false;
   if constexpr (PERSIST) {
-    more = t_next < t_end;
-    stage_barrier();  // every wave has finished reading the last K step's stage
+    // wave 0 resolves the next tile: its own queue's front (taken in the first K step,
+    // or now for tiles of at most two K steps), else the back of another queue
+    volatile int* slot = (volatile int*)(smem + kSchedSlotOffset);
+    if (wave == 0) {
+      if (!took && tid == 0)
+        qold = __hip_atomic_fetch_add(a.sched + xcd, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int nt = -1;
+      if (tid == 0) nt = front_tile(a, xcd, slots, qold);
+      nt = __builtin_amdgcn_readfirstlane(nt);
+      if (nt < 0) nt = steal_tile(a, slots, lane);
+      if (tid == 0) *slot = nt;
+    }
+    stage_barrier();  // every wave has finished reading the last K step's stage; the slot is written
+    const int nt = __builtin_amdgcn_readfirstlane(*slot);
+    more = nt >= 0;
     if (more) {
-      tile_origin(a, t_next, m0, n0);
+      tile_origin(a, nt, m0, n0);
       prologue();
     }
   }
@@ -830,7 +953,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
     }
   }
   if (!more) break;
-  t_next += t_stride;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile's first steps have landed
   }  // tiles
 }
@@ -844,28 +966,97 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, unsigned char* smem
   // 128 x 128 quarters; they are dispatched last and fill the CUs that free up.
   const int b = blockIdx.x;
   if constexpr (EPI == 0) {
-    if (b < a.persist_wgs) {
-      // persistent: workgroup b (on XCD b % 8) walks its XCD's tile range with a stride
-      // of the XCD's workgroup count, the order in which the non-persistent grid runs it
-      const int nb = a.big_tiles, slots = a.persist_wgs / 8;
-      const int per = nb / 8, rem = nb % 8;
-      const int xcd = b % 8, slot = b / 8;
-      const int t0 = xcd * per + (xcd < rem ? xcd : rem);
-      const int t_end = t0 + per + (xcd < rem ? 1 : 0);
-      const int t = t0 + slot;
-      if (t >= t_end) return;
-      int64_t m0, n0;
-      tile_origin(a, t, m0, n0);
-      run_tile<4, 4, 0, true>(a, m0, n0, smem, t + slots, slots, t_end);
+    if (a.persist_wgs > 0) {
+      // persistent (plain kernel): workgroup b (on XCD b % 8) starts with tile `slot`
+      // of its XCD's range and then takes tiles from the queues inside run_tile; after
+      // the whole tiles, the quarters of the tail tiles, one take each
+      const int slots = a.persist_wgs / 8, xcd = b % 8, slot = b / 8;
+      const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+      volatile int* qslot = (volatile int*)(smem + sched_slot_offset<EPI>());
+      int start, len;
+      xcd_range(a, xcd, start, len);
+      if (slot < len) {
+        int64_t m0, n0;
+        tile_origin(a, start + slot, m0, n0);
+        run_tile<4, 4, 0, true>(a, m0, n0, smem, xcd, slots);
+      }
+      for (;;) {
+        stage_barrier();  // every wave has read the slot's previous value
+        if (wave == 0 && tid == 0) {
+          const uint64_t q = __hip_atomic_fetch_add(a.sched + 8, (uint64_t)1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+          *qslot = q < (uint64_t)a.quarter_units ? (int)q : -1;
+        }
+        stage_barrier();
+        const int q = __builtin_amdgcn_readfirstlane(*qslot);
+        if (q < 0) break;
+        int64_t m0, n0;
+        tile_origin(a, a.big_tiles + q / 4, m0, n0);
+        const int64_t qm0 = m0 + ((q % 4) >> 1) * kTileQuarter, qn0 = n0 + ((q % 4) & 1) * kTileQuarter;
+        if (qm0 < a.m_pad && qn0 < a.n) run_tile<2, 2, EPI>(a, qm0, qn0, smem);  // else wholly past the output
+      }
+      // this workgroup takes nothing more; the last one to finish clears the queues
+      if (tid == 0) {
+        const uint64_t done = __hip_atomic_fetch_add(a.sched + 9, (uint64_t)1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (uint64_t)gridDim.x - 1) {
+#pragma unroll
+          for (int i = 0; i < 10; ++i) __hip_atomic_store(a.sched + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      return;
+    }
+  }
+  if constexpr (EPI != 0) {
+    if (a.sched) {
+      // fused kinds: a grid of one unit per workgroup plus a round of spare workgroups.
+      // Each takes one unit: the front of its XCD's queue (every tile of the range is
+      // taken at run time), else the back of the fullest other queue, else a quarter
+      // of the tail; a workgroup that finds none exits. The spare workgroups of a fast
+      // XCD take the tiles its slower neighbours have not reached.
+      const int xcd = b % 8;
+      const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+      volatile int* uslot = (volatile int*)(smem + sched_slot_offset<EPI>());
+      if (wave == 0) {
+        int u = -1;
+        if (tid == 0)
+          u = front_tile(a, xcd, 0,
+                         __hip_atomic_fetch_add(a.sched + xcd, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        u = __builtin_amdgcn_readfirstlane(u);
+        if (u < 0) u = steal_tile(a, 0, lane);
+        if (u < 0 && tid == 0) {
+          const uint64_t q = __hip_atomic_fetch_add(a.sched + 8, (uint64_t)1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+          u = q < (uint64_t)a.quarter_units ? a.big_tiles + (int)q : -1;  // units past big_tiles are quarters
+        }
+        if (tid == 0) *uslot = u;
+      }
+      stage_barrier();
+      const int u = __builtin_amdgcn_readfirstlane(*uslot);
+      if (u >= a.big_tiles) {
+        const int q = u - a.big_tiles;
+        int64_t m0, n0;
+        tile_origin(a, a.big_tiles + q / 4, m0, n0);
+        const int64_t qm0 = m0 + ((q % 4) >> 1) * kTileQuarter, qn0 = n0 + ((q % 4) & 1) * kTileQuarter;
+        if (qm0 < a.m_pad && qn0 < a.n) run_tile<2, 2, EPI>(a, qm0, qn0, smem);
+      } else if (u >= 0) {
+        int64_t m0, n0;
+        tile_origin(a, u, m0, n0);
+        run_tile<4, 4, EPI>(a, m0, n0, smem);
+      }
+      if (tid == 0) {
+        const uint64_t done = __hip_atomic_fetch_add(a.sched + 9, (uint64_t)1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (uint64_t)gridDim.x - 1) {
+#pragma unroll
+          for (int i = 0; i < 10; ++i) __hip_atomic_store(a.sched + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
       return;
     }
   }
   int t, quarter = -1;
-  if (a.persist_wgs > 0 && b >= a.persist_wgs) {
-    const int q = b - a.persist_wgs;
-    t = a.big_tiles + q / 4;
-    quarter = q % 4;
-  } else if (b < a.big_tiles) {
+  if (b < a.big_tiles) {
     const int nb = a.big_tiles;
     const int per = nb / 8, rem = nb % 8;
     const int xcd = b % 8, idx = b / 8;
@@ -910,11 +1101,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(GemmArgs a) {
 
 // ---- host side -----------------------------------------------------------------------------
 
-// the plain kernel's persistent workgroups stage their epilogue past the pipeline stages
-constexpr size_t kPersistStagingBytes = (size_t)kWaves * 32 * (BigTile::TN / WAVES_N * 2 + 16);
+// the plain kernel's persistent workgroups stage their epilogue past the pipeline stages,
+// followed by the word that broadcasts a taken tile
 size_t gemm_smem_bytes(int kind) {
-  return (size_t)kStages * BigTile::StageBytes +
-         (kind == 2 ? (size_t)kWaves * kCand * 4 : kind == 0 ? kPersistStagingBytes : 0);
+  return (kind == 2 ? sched_slot_offset<2>() : kind == 1 ? sched_slot_offset<1>() : sched_slot_offset<0>()) + 16;
 }
 const void* gemm_kernel_ptr(int kind) {
   return kind == 2 ? (const void*)gemm_kernel<2> : kind == 1 ? (const void*)gemm_kernel<1> : (const void*)gemm_kernel<0>;
@@ -922,7 +1112,7 @@ const void* gemm_kernel_ptr(int kind) {
 
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
                        const uint8_t* ws, const float* gw, uint16_t* d, int64_t m_pad, int64_t n, int64_t k,
-                       const GemmEpilogue& ep, int cu_count, hipStream_t stream) {
+                       const GemmEpilogue& ep, int cu_count, uint64_t* sched, hipStream_t stream) {
   GemmArgs args;
   args.ep = ep;
   args.aq = aq;
@@ -950,12 +1140,25 @@ hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, co
   // at most a quarter of the CUs' worth, its tiles run as 128 x 128 quarters.
   const int tail = cu_count > 0 ? ntiles % cu_count : 0;
   args.big_tiles = (tail > 0 && ntiles > cu_count && 4 * tail <= cu_count) ? ntiles - tail : ntiles;
-  // The plain kernel runs the whole tiles with persistent workgroups, a multiple of
-  // 8 of them (each XCD the same count), one per CU, when there are more tiles than
-  // that: the next tile's first loads then overlap the current tile's epilogue.
+  // The plain kernel runs every tile with persistent workgroups, a multiple of 8 of
+  // them (each XCD the same count), one per CU, when there are more whole tiles than
+  // that: the next tile's first loads then overlap the current tile's epilogue, and
+  // the tiles past each workgroup's first are taken from the queue set `sched` (zero
+  // on entry, zero again when the launch ends). Taken at run time, the whole tiles end
+  // up to one tile apart across the CUs whatever the count; when the last round is
+  // more than a quarter full, half a round of tiles runs as quarters to even that out.
   const int persist = cu_count - cu_count % 8;
-  args.persist_wgs = (ep.kind == 0 && persist >= 8 && args.big_tiles > persist) ? persist : 0;
-  const int grid = (args.persist_wgs > 0 ? args.persist_wgs : args.big_tiles) + 4 * (ntiles - args.big_tiles);
+  const bool dynamic = sched && persist >= 8;
+  if (dynamic && tail > 0 && 4 * tail > cu_count && ntiles - persist / 2 > persist)
+    args.big_tiles = ntiles - persist / 2;
+  args.quarter_units = 4 * (ntiles - args.big_tiles);
+  args.persist_wgs = (dynamic && ep.kind == 0 && args.big_tiles > persist) ? persist : 0;
+  // the fused kinds take one unit per workgroup at run time when there are more whole
+  // tiles than CUs, with a round of spare workgroups; otherwise the grid is static
+  const bool fused_dynamic = dynamic && ep.kind != 0 && args.big_tiles > persist;
+  args.sched = (args.persist_wgs > 0 || fused_dynamic) ? sched : nullptr;
+  const int grid = args.persist_wgs > 0 ? args.persist_wgs
+                                        : args.big_tiles + args.quarter_units + (fused_dynamic ? persist : 0);
   if (ep.kind == 2)
     gemm_kernel<2><<<dim3(grid), dim3(kGemmThreads), gemm_smem_bytes(2), stream>>>(args);
   else if (ep.kind == 1)

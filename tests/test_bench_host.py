@@ -39,3 +39,16 @@ def test_traffic_summaries_match_the_sources():
     assert bench.measured_gemm_traffic() is not None
     assert bench.measured_traffic(bench.PRODUCER_TRAFFIC_SUMMARY, bench.PRODUCER_SOURCES) is not None
     assert bench.measured_traffic(bench.SINGLE_READ_TRAFFIC_SUMMARY, bench.PRODUCER_SOURCES) is not None
+
+
+def test_traffic_run_names_its_own_profiled_run():
+    """The traffic figure is labelled as coming from the separate profiled runs, with
+    that command's own kernel-trace time and the fraction of peak at that time."""
+    r = bench.traffic_run(bench.GEMM_TRAFFIC_SUMMARY, bench.GEMM_SOURCES, 2.0 * 37810 * 5376 * 14336,
+                          bench.PEAK_MFMA_TFLOPS, 1e12)
+    assert r is not None and "separate" in r["source"] and r["summary"] == bench.GEMM_TRAFFIC_SUMMARY
+    assert 1.0 < r["trace_ms_per_launch"] < 10.0
+    assert abs(r["frac_at_trace_ms"] - 2.0 * 37810 * 5376 * 14336 / (r["trace_ms_per_launch"] * 1e-3) / 1e12 /
+               bench.PEAK_MFMA_TFLOPS) < 1e-3
+    p = bench.traffic_run(bench.PRODUCER_TRAFFIC_SUMMARY, bench.PRODUCER_SOURCES, 4641423360, bench.PEAK_HBM_GBS, 1e9)
+    assert p is not None and 0.3 < p["trace_ms_per_launch"] < 3.0

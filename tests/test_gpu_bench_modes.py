@@ -38,3 +38,17 @@ def test_profile_step_with_copy_calibration(gpu):
     d = run_bench("--profile-step", "--copy-bytes", str(1 << 24))
     assert d["mode"] == "profile-step" and d["producer_ms"] > 0 and d["gemm_ms"] > 0
     assert d["dispatches_per_kernel"] == 3 and d["copy_gbs"] > 0
+
+
+def test_chain_times_every_step_of_both_paths(gpu):
+    """The FC1 -> FC2 block, fused against unfused (full size, one timed step): every
+    step of each path is timed, the unfused path's elementwise kernels included."""
+    d = run_bench("--chain")
+    assert d["mode"] == "chain"
+    assert set(d["fused"]) == {"modulate_quantize", "fc1_gemm", "fc2_producer", "fc2_gemm", "total_ms"}
+    assert set(d["unfused"]) == {"modulate", "quantize", "fc1_gemm", "fc2_producer", "fc2_gemm", "bias_add",
+                                 "gated_residual", "total_ms"}
+    for path in ("fused", "unfused"):
+        parts = {k: v for k, v in d[path].items() if k != "total_ms"}
+        assert all(v > 0 for v in parts.values())
+        assert abs(sum(parts.values()) - d[path]["total_ms"]) < 1e-3

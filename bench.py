@@ -69,22 +69,36 @@ def measured_gemm_traffic():
     return measured_traffic(GEMM_TRAFFIC_SUMMARY, GEMM_SOURCES)
 
 
+def source_digest(sources) -> str:
+    """sha256 of the kernel sources' code: each file with its // and /* */ comments
+    removed and every run of white space collapsed to one space, so that a change of
+    comments alone does not retire a summary. (The sources hold no string literal
+    that contains a comment marker.)"""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
 def summary_values(summary: str, sources):
     """The value block of a committed counter summary, or None when the summary was
-    taken on a different kernel source than the one built here."""
-    import hashlib
+    taken on different kernel code than the code built here (source_digest)."""
     try:
-        h = hashlib.sha256()
-        for f in sources:
-            with open(os.path.join(ROOT, f), "rb") as fh:
-                h.update(fh.read())
+        digest = source_digest(sources)
         vals = {}
         with open(os.path.join(ROOT, summary)) as fh:
             for line in fh:
                 if ":" in line and not line.startswith(("#", "|", "`")):
                     k, _, v = line.partition(":")
                     vals[k.strip()] = v.strip()
-        return vals if vals.get("source_sha256") == h.hexdigest() else None
+        return vals if vals.get("source_sha256") == digest else None
     except OSError:
         return None
 

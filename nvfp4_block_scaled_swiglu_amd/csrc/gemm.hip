@@ -260,7 +260,10 @@ __device__ __forceinline__ void tile_origin(const GemmArgs& a, int t, int64_t& m
 //   sched[8]: the next 128 x 128 quarter of the tail tiles, taken after every queue is
 //     empty.
 //   sched[9]: workgroups that have finished taking. The last one clears sched[0..9],
-//     so the words are zero for the next launch that uses them.
+//     so the words are zero for the next launch that uses them. Relaxed order is
+//     enough: a workgroup counts itself only after its last take has returned its
+//     value, and the last one issues its clears only after its count has returned
+//     gridDim.x - 1, so every take on a word is performed before the clear of it.
 // All of them are agent-scope atomics (the XCDs' L2 caches are not coherent with each
 // other); a take is one atomic with return, issued a K step before its result is used.
 static_assert(kGemmQueueWords >= 10, "a queue set holds the 8 XCD queues, the quarter count and the exit count");

@@ -52,3 +52,15 @@ def test_traffic_run_names_its_own_profiled_run():
                bench.PEAK_MFMA_TFLOPS) < 1e-3
     p = bench.traffic_run(bench.PRODUCER_TRAFFIC_SUMMARY, bench.PRODUCER_SOURCES, 4641423360, bench.PEAK_HBM_GBS, 1e9)
     assert p is not None and 0.3 < p["trace_ms_per_launch"] < 3.0
+
+
+def test_source_digest_ignores_comments_only(tmp_path):
+    """A summary stays valid across comment edits and is retired by any code edit."""
+    a = tmp_path / "a.hip"
+    a.write_text("int x = 1; // one\n/* block\n   comment */ int y;\n")
+    b = tmp_path / "b.hip"
+    b.write_text("int x = 1;   // other words\n\nint y;\n")
+    c = tmp_path / "c.hip"
+    c.write_text("int x = 2;\nint y;\n")
+    assert bench.source_digest([str(a)]) == bench.source_digest([str(b)])
+    assert bench.source_digest([str(a)]) != bench.source_digest([str(c)])

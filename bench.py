@@ -294,18 +294,30 @@ def cold_times(run_gemm, run_producer, dev, stream, reps: int) -> dict:
 
 def host_cpu() -> dict:
     """What the CPU baseline runs on: logical CPUs of this process (nproc), the OS count,
-    and the CPU model name."""
-    model = ""
+    and the CPU model name as `lscpu` reports it (else /proc/cpuinfo's)."""
+    import subprocess
+    model, lscpu_cpus = "", None
     try:
-        with open("/proc/cpuinfo") as fh:
-            for line in fh:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            key, _, val = line.partition(":")
+            if key.strip() == "Model name" and not model:
+                model = val.strip()
+            elif key.strip() == "CPU(s)" and lscpu_cpus is None and val.strip().isdigit():
+                lscpu_cpus = int(val.strip())
+    except (OSError, subprocess.SubprocessError):
         pass
+    if not model:
+        try:
+            with open("/proc/cpuinfo") as fh:
+                for line in fh:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
     nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-    return {"nproc": nproc, "os_cpu_count": os.cpu_count(), "cpu_model": model}
+    return {"nproc": nproc, "os_cpu_count": os.cpu_count(), "lscpu_cpus": lscpu_cpus, "cpu_model": model}
 
 
 def baseline_threads() -> int:

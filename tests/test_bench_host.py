@@ -64,3 +64,9 @@ def test_source_digest_ignores_comments_only(tmp_path):
     c.write_text("int x = 2;\nint y;\n")
     assert bench.source_digest([str(a)]) == bench.source_digest([str(b)])
     assert bench.source_digest([str(a)]) != bench.source_digest([str(c)])
+
+
+def test_host_cpu_names_the_host():
+    h = bench.host_cpu()
+    assert h["nproc"] >= 1 and h["os_cpu_count"] >= h["nproc"] and h["cpu_model"]
+    assert 1 <= bench.baseline_threads() <= h["nproc"]

@@ -182,7 +182,7 @@ def ceilings(dev, stream) -> dict:
             "note": "MFMA-only kernel (4 independent v_mfma_f32_32x32x16_f16 chains per wave, one wave per "
                     "SIMD), clock from s_memtime over s_memrealtime; copy of 1 GiB, read + write bytes; "
                     "streaming probe (nvfp4_hbm_stream_ceiling: one workgroup per 16 KiB chunk, dispatched in "
-                    "address order) over 2 GiB reading only, and writing "
+                    "address order, non-temporal loads and stores) over 2 GiB reading only, and writing "
                     f"{QUANT_WRITE_SHARE:.4f} byte per byte read (the quantize launch's mix), read + write bytes"}
 
 

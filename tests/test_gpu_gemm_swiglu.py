@@ -64,6 +64,11 @@ def run_pair(a, wt, bias, device):
 
 @pytest.mark.parametrize("m,n_half,k", [(16, 8, 64), (100, 136, 192), (300, 256, 320), (513, 264, 448)])
 def test_pair_against_oracle(gpu, m, n_half, k):
+    check_pair(gpu, m, n_half, k)
+
+
+def check_pair(gpu, m, n_half, k):
+    """Gate and up with bias against the oracle on every element, and the emitted amax."""
     _say(f"[swiglu-pair] m={m} n_half={n_half} k={k}")
     a, wt, (rq, rs, rg, rwq, rws, rgw) = make_operands(m, n_half, k, m + n_half, gpu)
     bias = synth.normal_bf16(1, 2 * n_half, seed=m, tag=5, sigma=0.2)[0]

@@ -83,13 +83,16 @@ int64_t nvfp4_qdata_bytes(int64_t rows, int64_t k);
  * rows < 0 or k < 0. */
 int64_t nvfp4_scale_bytes(int64_t rows, int64_t k);
 
-/* Bytes of the two-pass producers' workspace: one partial absmax slot per
- * workgroup of the absmax launch, read back by the quantize launch. The
- * component-2 summary's "conclusion" names the global scale as the dependency
- * that needs an explicit synchronisation design; this buffer carries it across
- * the launch boundary. The caller allocates it on the device (16-byte aligned)
- * and owns it; its contents need no initialisation, since every call writes the
- * slots it reads. Calls that may overlap in time (different streams) need distinct
+/* Bytes of the two-pass producers' workspace (16,384): 64 absmax slots, 256 bytes
+ * apart, into which the absmax launch folds its workgroups' maxima by atomic max
+ * and which the quantize launch reduces to the tensor amax. The component-2
+ * summary's "conclusion" names the global scale as the dependency that needs an
+ * explicit synchronisation design; this buffer carries it across the launch
+ * boundary. The caller allocates it on the device (16-byte aligned), owns it, and
+ * fills it with zeros before its first use; the quantize launch clears the slots
+ * after reading them, so every completed call leaves the workspace zero-filled
+ * again. After a call that failed between its two launches (NVFP4_ERR_LAUNCH), zero
+ * it again. Calls that may overlap in time (different streams) need distinct
  * workspaces. */
 int64_t nvfp4_quantize_workspace_bytes(void);
 
@@ -128,9 +131,12 @@ int nvfp4_init(void);
  * the smallest UE4M3 byte with v(S) * 6 * g >= max |y| over its 16 elements; each
  * code is the E2M1 value nearest to |y| / (v(S) * g), ties to the even code, with
  * the sign of y (also on zero). Two ordinary launches on `stream`: the absmax pass
- * writes per-workgroup partial maxima into the workspace, and the
- * pack-and-swizzle pass reduces them to the global scale (the launch boundary is
- * the grid-wide synchronisation). Inputs must be finite and keep every
+ * folds per-workgroup maxima into the workspace's slots, and the pack-and-swizzle
+ * pass reduces them to the global scale (the launch boundary is the grid-wide
+ * synchronisation) and clears them. The pack-and-swizzle pass takes its work from
+ * run-time counters in static device memory (one set per launch, 64 sets per GPU
+ * used in turn and left zero by each launch), so at most 64 producer launches may
+ * be in flight on one GPU at a time. Inputs must be finite and keep every
  * |silu(gate) * up| below 2^128.
  */
 int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up,
@@ -141,16 +147,15 @@ int nvfp4_quantize_swiglu(const void* gate_dev, int64_t ld_gate, const void* up_
  * nvfp4_quantize_swiglu for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation): the
  * same operation, arguments, layouts and outputs, without the workspace argument.
- * The absmax partials live in the library's own scratch, a fixed 4,096-byte device
- * array per GPU (one slot for each of at most 1,024 absmax workgroups) held until
- * the process ends; the call allocates nothing and calls no allocating routine.
- * Set-up allocates, so nvfp4_init must have run on the current device first
- * (otherwise NVFP4_ERR_NO_DEVICE). Every call on a GPU shares that GPU's scratch:
- * each call writes every slot it reads, so nothing carries over between calls,
- * but calls that overlap in time on one GPU (different streams) race and may
+ * The absmax slots live in the library's own scratch, a fixed 16,384-byte device
+ * array per GPU (one workspace, zero at load) held until the process ends; the call
+ * allocates nothing and calls no allocating routine. Set-up allocates, so
+ * nvfp4_init must have run on the current device first (otherwise
+ * NVFP4_ERR_NO_DEVICE). Every call on a GPU shares that GPU's scratch: each call's
+ * quantize launch clears the slots after reading them, so every call starts from
+ * zero, but calls that overlap in time on one GPU (different streams) race and may
  * produce wrong global scales; serialise them, or use nvfp4_quantize_swiglu with
- * distinct workspaces. NVFP4_ERR_WORKSPACE if the device's producer grid would
- * need more slots than the scratch holds (not reachable with 1,024 slots).
+ * distinct workspaces.
  */
 int nvfp4_quantize_swiglu_noalloc(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up,
                                   int64_t m, int64_t k, void* qdata_dev, void* scales_dev,
@@ -196,8 +201,8 @@ int nvfp4_quantize_modulate(const void* x_dev, int64_t ld_x, int64_t rows, int64
  * Every other argument, layout and output as nvfp4_quantize_swiglu; no workspace.
  * An amax below the true maximum is the caller's error; the result is still
  * defined: a block whose maximum exceeds v(126) * 6 * g gets scale byte 126 and
- * its codes saturate at +-6 (magnitude code 7). One ordinary (non-cooperative)
- * launch; nvfp4_init sizes its grid as for the two-pass producer.
+ * its codes saturate at +-6 (magnitude code 7). One ordinary launch, the two-pass
+ * producer's pack-and-swizzle pass (with its run-time counters).
  */
 int nvfp4_quantize_swiglu_amax(const void* gate_dev, int64_t ld_gate, const void* up_dev, int64_t ld_up,
                                int64_t m, int64_t k, const float* amax_dev, void* qdata_dev,

@@ -221,12 +221,13 @@ _workspaces: Dict[Tuple[int, int], "torch.Tensor"] = {}
 
 def _workspace(device, stream_handle: int):
     """A producer workspace per (device, stream), so that calls on different streams
-    never share one (its contents need no initialisation)."""
+    never share one. It starts zero-filled, as the library requires; every completed
+    call leaves it zero-filled again."""
     import torch
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
     ws = _workspaces.get(key)
     if ws is None:
-        ws = torch.empty((nvfp4_quantize_workspace_bytes(),), dtype=torch.uint8, device=device)
+        ws = torch.zeros((nvfp4_quantize_workspace_bytes(),), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

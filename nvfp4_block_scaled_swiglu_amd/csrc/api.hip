@@ -24,10 +24,11 @@ size_t producer_smem_bytes(int mode);
 const void* producer_kernel_ptr(int mode, bool given);
 const void* producer_absmax_kernel_ptr(int mode);
 int producer_block_threads();
+int64_t producer_units(int64_t m, int64_t k);
 hipError_t launch_producer(int mode, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
                            const uint16_t* mod_scale, const uint16_t* mod_shift, int64_t m, int64_t k,
                            uint8_t* qdata, uint8_t* scales, float* gout, const float* amax_in, void* workspace,
-                           const uint16_t* silu_table, int max_blocks, hipStream_t stream);
+                           uint32_t* queue, const uint16_t* silu_table, int quant_blocks, hipStream_t stream);
 size_t gemm_smem_bytes(int kind);
 const void* gemm_kernel_ptr(int kind);
 hipError_t launch_gemm(const uint8_t* aq, const uint8_t* as, const float* ga, const uint8_t* wq,
@@ -53,7 +54,9 @@ struct DeviceState {
   void* scratch = nullptr;  // this device's copy of `scratch` (hipGetSymbolAddress)
   uint64_t* gemm_queues = nullptr;  // this device's copy of `gemm_queues`
   std::atomic<uint32_t> gemm_launches{0};  // picks the queue set of each plain GEMM launch
-  int producer_blocks[3] = {0, 0, 0};  // persistent grid per producer mode
+  uint32_t* producer_queues = nullptr;  // this device's copy of `producer_queues`
+  std::atomic<uint32_t> producer_launches{0};  // picks the counter set of each quantize launch
+  int producer_blocks[3] = {0, 0, 0};  // quantize launch's persistent grid per producer mode
   int cu_count = 0;
   char arch[64] = {0};
 };
@@ -62,13 +65,19 @@ DeviceState g_dev[kMaxDevices];
 
 }  // namespace
 
-// Producer scratch of nvfp4_quantize_swiglu_noalloc: the absmax partials that the
-// other two-pass entry points keep in the caller's workspace. Each GPU holds its own
-// copy for the life of the process; host code uses only the per-device address that
-// set-up obtains with hipGetSymbolAddress (the name itself is a host-side stand-in).
-// Every call on a GPU shares it, and each call writes every slot it reads, so nothing
-// needs clearing between calls; calls that overlap in time on one GPU race.
-static __device__ __align__(256) uint32_t scratch[nvfp4::kMaxPartials];
+// Producer scratch of nvfp4_quantize_swiglu_noalloc: the absmax slots that the other
+// two-pass entry points keep in the caller's workspace (16 KiB). Each GPU holds its own
+// copy for the life of the process, zero at load; host code uses only the per-device
+// address that set-up obtains with hipGetSymbolAddress (the name itself is a host-side
+// stand-in). Every call on a GPU shares it; each call's quantize launch clears the slots
+// after reading them, so every call starts from zero; calls that overlap in time on one
+// GPU race.
+static __device__ __align__(256) uint32_t scratch[sizeof(nvfp4::ProducerWorkspace) / 4];
+
+// Unit counters of the producer's quantize launch (zero at load). Launch i on a device
+// uses set i % kProdQueueSets; its last wave leaves the set zeroed again, so up to
+// kProdQueueSets quantize launches may run at the same time on one GPU.
+static __device__ __align__(256) uint32_t producer_queues[nvfp4::kProdQueueSets * nvfp4::kProdQueueSetWords];
 
 // Tile queues of the plain GEMM's persistent grid (zero at load). Launch i on a device
 // uses set i % kGemmQueueSets; its last workgroup leaves the set zeroed again, so up to
@@ -119,16 +128,14 @@ int ensure_device(DeviceState** out) {
   snprintf(st.arch, sizeof(st.arch), "%s", prop.gcnArchName);
   st.cu_count = prop.multiProcessorCount;
 
-  // kernels with more than 64 KiB of dynamic LDS must opt in
+  // kernels with more than 64 KiB of dynamic LDS must opt in; the quantize launch runs
+  // as many persistent workgroups as fit on the device at once
   for (int mode = 0; mode < 3; ++mode) {
     for (int given = 0; given < 2; ++given) {
       e = hipFuncSetAttribute(nvfp4::producer_kernel_ptr(mode, given != 0),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)nvfp4::producer_smem_bytes(mode));
       if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer LDS attribute: %s", hipGetErrorString(e));
     }
-    e = hipFuncSetAttribute(nvfp4::producer_absmax_kernel_ptr(mode), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)nvfp4::producer_smem_bytes(mode));
-    if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "absmax LDS attribute: %s", hipGetErrorString(e));
     int per_cu = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nvfp4::producer_kernel_ptr(mode, false),
                                                      nvfp4::producer_block_threads(),
@@ -136,7 +143,6 @@ int ensure_device(DeviceState** out) {
     if (e != hipSuccess || per_cu < 1)
       return fail(NVFP4_ERR_LAUNCH, "producer occupancy query: %s (%d)", hipGetErrorString(e), per_cu);
     st.producer_blocks[mode] = per_cu * st.cu_count;
-    if (st.producer_blocks[mode] > nvfp4::kMaxPartials) st.producer_blocks[mode] = nvfp4::kMaxPartials;
   }
   for (int kind = 0; kind < 3; ++kind) {
     e = hipFuncSetAttribute(nvfp4::gemm_kernel_ptr(kind), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -153,6 +159,10 @@ int ensure_device(DeviceState** out) {
   e = hipGetSymbolAddress(&q, HIP_SYMBOL(gemm_queues));
   if (e != hipSuccess || !q) return fail(NVFP4_ERR_LAUNCH, "gemm queue address: %s", hipGetErrorString(e));
   st.gemm_queues = (uint64_t*)q;
+  void* pq = nullptr;
+  e = hipGetSymbolAddress(&pq, HIP_SYMBOL(producer_queues));
+  if (e != hipSuccess || !pq) return fail(NVFP4_ERR_LAUNCH, "producer queue address: %s", hipGetErrorString(e));
+  st.producer_queues = (uint32_t*)pq;
   hipStream_t s;
   e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "stream create: %s", hipGetErrorString(e));
@@ -164,6 +174,12 @@ int ensure_device(DeviceState** out) {
   st.ready.store(true, std::memory_order_release);
   *out = &st;
   return NVFP4_OK;
+}
+
+// The counter set of the next quantize launch on this device.
+uint32_t* producer_queue_set(DeviceState& st) {
+  const uint32_t set = st.producer_launches.fetch_add(1, std::memory_order_relaxed) % nvfp4::kProdQueueSets;
+  return st.producer_queues + (size_t)set * nvfp4::kProdQueueSetWords;
 }
 
 // ws: the workspace of the two-pass producer, or the caller's amax of the single-pass
@@ -190,10 +206,8 @@ int check_quant_args(const void* x, int64_t ldx, const void* u, int64_t ldu, boo
   if (!aligned16(x) || (swiglu && !aligned16(u)) || !aligned16(qdata) || !aligned16(scales) || ((uintptr_t)g & 3u) ||
       (given ? ((uintptr_t)ws & 3u) != 0 : (!scratch && !aligned16(ws))))
     return fail(NVFP4_ERR_MISALIGNED, "pointers must be 16-byte aligned (global scale and amax 4-byte)");
-  const int64_t rows_pad = (m + 15) / 16 * 16;
-  const int64_t srows = (rows_pad + 127) / 128 * 128;
-  if (srows / 128 * ((k + 255) / 256) > (int64_t)1 << 30)
-    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "tensor too large");
+  // units of 4 rows x 512 columns are numbered with 32-bit integers
+  if (nvfp4::producer_units(m, k) > (int64_t)1 << 30) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "tensor too large");
   return NVFP4_OK;
 }
 
@@ -234,8 +248,9 @@ static int quantize_common(int mode, bool given, const void* x, int64_t ldx, con
   if (rc != NVFP4_OK) return rc;
   hipError_t e = nvfp4::launch_producer(mode, (const uint16_t*)x, ldx, (const uint16_t*)u, ldu,
                                         (const uint16_t*)mod_scale, (const uint16_t*)mod_shift, m, k,
-                                        (uint8_t*)qdata, (uint8_t*)scales, g, amax, ws, st->silu_table,
-                                        st->producer_blocks[mode], (hipStream_t)stream);
+                                        (uint8_t*)qdata, (uint8_t*)scales, g, amax, given ? nullptr : ws,
+                                        producer_queue_set(*st), st->silu_table, st->producer_blocks[mode],
+                                        (hipStream_t)stream);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -262,14 +277,11 @@ int nvfp4_quantize_swiglu_noalloc(const void* gate_dev, int64_t ld_gate, const v
   // set-up allocates (a stream for the silu table build), so it is not done here
   if (!st.ready.load(std::memory_order_acquire))
     return fail(NVFP4_ERR_NO_DEVICE, "call nvfp4_init on device %d before nvfp4_quantize_swiglu_noalloc", dev);
-  // the absmax launch writes one slot per workgroup; its grid is capped at kMaxPartials
+  // the scratch is one workspace: a fixed set of absmax slots, whatever the shape
   static_assert(sizeof(scratch) == sizeof(nvfp4::ProducerWorkspace), "scratch holds one workspace");
-  if ((int64_t)st.producer_blocks[1] * 4 > (int64_t)sizeof(scratch))
-    return fail(NVFP4_ERR_WORKSPACE, "producer grid of %d workgroups exceeds the %d-slot scratch",
-                st.producer_blocks[1], nvfp4::kMaxPartials);
   e = nvfp4::launch_producer(1, (const uint16_t*)gate_dev, ld_gate, (const uint16_t*)up_dev, ld_up, nullptr, nullptr,
                              m, k, (uint8_t*)qdata_dev, (uint8_t*)scales_dev, global_scale_dev, nullptr, st.scratch,
-                             st.silu_table, st.producer_blocks[1], (hipStream_t)stream);
+                             producer_queue_set(st), st.silu_table, st.producer_blocks[1], (hipStream_t)stream);
   if (e != hipSuccess) return fail(NVFP4_ERR_LAUNCH, "producer launch: %s", hipGetErrorString(e));
   return ok();
 }

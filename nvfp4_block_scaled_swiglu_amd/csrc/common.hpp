@@ -19,15 +19,27 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
-// Workspace of the two-pass producer: one partial maximum per absmax-pass
-// workgroup (fp32 bits of a non-negative bf16 value, so unsigned order is value
-// order). The absmax launch writes every slot the quantize launch then reads, so
-// the contents never need initialising.
-constexpr int kMaxPartials = 1024;
+// Workspace of the two-pass producer: kAmaxSlots slots, kSlotStride words apart (one
+// per 256 bytes, so that the atomic maxima of the absmax launch spread over the memory
+// channels). The absmax launch folds each workgroup's max |y| into slot
+// (workgroup % kAmaxSlots) by atomic max (fp32 bits of a non-negative bf16 value, so
+// unsigned order is value order); the quantize launch reads every slot and its last
+// wave clears them. The workspace must therefore be zero before its first use, and
+// every completed call leaves it zero.
+constexpr int kAmaxSlots = 64;
+constexpr int kSlotStride = 64;
 struct ProducerWorkspace {
-  uint32_t partial[kMaxPartials];
+  uint32_t slot[kAmaxSlots * kSlotStride];
 };
-static_assert(sizeof(ProducerWorkspace) == 4096, "workspace layout");
+static_assert(sizeof(ProducerWorkspace) == 16384, "workspace layout");
+
+// Unit queues of the producer's quantize launch: kProdQueueCounters counters
+// kSlotStride words apart, then the word that counts the waves that have finished.
+// Launch i on a device uses set i % kProdQueueSets (static device memory, zero at
+// load); its last wave leaves the set zero again.
+constexpr int kProdQueueCounters = 32;
+constexpr int kProdQueueSetWords = (kProdQueueCounters + 1) * kSlotStride;
+constexpr int kProdQueueSets = 64;
 
 // Tile-queue words of the plain GEMM's persistent grid: one set of kGemmQueueWords
 // per launch in flight, kGemmQueueSets sets per device (static device memory).

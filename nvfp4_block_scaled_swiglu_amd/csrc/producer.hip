@@ -16,70 +16,73 @@
 //   QDATA   = two codes per byte (even element low), rows [m, m_pad) zero
 //   scales  = 512-byte tiles of 128 rows x 4 scale columns, padding zero
 //
-// Structure: two ordinary launches on the caller's stream. Each runs a persistent
-// grid (one 16-wave workgroup per CU, the bf16 SiLU table in LDS) over work items of
-// 64 rows x 512 columns; each lane owns one 16-element block of a row per step (a wave
-// covers 2 rows x 32 blocks).
-//  - The absmax launch reduces |y| with the next item's loads in flight (wavefront
-//    shuffles, then LDS across waves) and writes one partial maximum per workgroup
-//    into the caller's workspace.
+// Work is cut into units of 4 rows x 512 columns; a wave takes a unit in two steps
+// of 2 rows, each lane owning one 16-element block of a row per step (1 KB runs of
+// each input row per step).
+//
+// Two ordinary launches on the caller's stream:
+//  - The absmax launch is a one-shot grid of small workgroups (4 waves, one unit
+//    each), dispatched in address order. It needs no table: for SwiGLU, every |y| is
+//    bounded by max(gate, 0.28125) * |up| (exact in fp32), and that bound is |y|
+//    itself up to the bf16 rounding when gate >= 8 (silu_bf16 is the identity
+//    there); only elements whose bound reaches the wave's exact maximum are looked up
+//    in the device silu table. Each workgroup folds its maximum into one of the
+//    workspace's 64 slots by atomic max.
 //  - The kernel boundary is the grid-wide synchronisation the global scale needs.
-//  - The quantize launch reduces the partials to amax, derives g, walks the items in
-//    reverse order (so the rows the absmax launch read last, still in the memory-side
-//    cache, are read first), recomputes y, and stores QDATA rows (32 lanes store one
-//    full 256-byte row segment) and each scale byte at its place in its 512-byte
-//    tile. It has no workgroup barrier, so the 16 waves drift apart and hide each
-//    other's load latency.
+//  - The quantize launch runs one persistent 12-wave workgroup per CU with the bf16
+//    silu table in LDS. Its waves take units from 32 interleaved run-time counters
+//    (each wave its own counter, takes issued two units ahead), in reverse address
+//    order, so that the rows the absmax launch read last, still in the memory-side
+//    cache, come first and the whole grid moves through memory together. It reduces
+//    the slots to amax, derives g, recomputes y, and stores QDATA rows (32 lanes
+//    store one 256-byte row segment) and each scale byte at its place in its tile.
+//    Its last wave clears the counters and the slots for the next call.
 // With GIVEN (amax from the caller) only the quantize launch runs: every input byte
 // is read once.
 //
 // Exactness: every rounding decision equals the exact one.
-//  - y: a product of two bf16 values is exact in fp32 when it is >= 2^-126; a block
-//    with some |y| <= 2^-126 (or zero) has its nonzero subnormal products
-//    recomputed in fp64 and rounded once.
+//  - y: a product of two bf16 values is exact in fp32 when it is >= 2^-126; smaller
+//    nonzero products are recomputed in fp64 and rounded once.
 //  - S: read off the bits of an fp32 estimate of bmax / 6g (relative error below
 //    2^-22); estimates within 2^-17 of a grid point are settled by exact fp64
 //    compares (v(e) * 6g has <= 30 significant bits).
 //  - codes: the hardware fp32 -> E2M1 conversion (round to nearest even) is applied
 //    to |y| * r_lo and |y| * r_hi, two brackets of the exact quotient built from a
 //    1-ulp reciprocal with a 2^-20 margin; when the two codes agree the exact code
-//    is that code (rounding is monotone), otherwise the element is decided by exact
-//    fp64 compares against the seven midpoints.
+//    is that code (rounding is monotone). Otherwise the codes are neighbours i and
+//    i + 1, and the sign of fma(mid_i * v(S), g, -|y|) decides (mid_i * v(S) has at
+//    most 7 significant bits, and for unit >= 2^-90 the exact difference, when not
+//    zero, is a normal fp32 number, so the fused result has the exact sign); a tie
+//    goes to the even code. Smaller units use exact fp64 compares.
 #include "common.hpp"
 
 namespace nvfp4 {
 
-constexpr int kProdThreads = 1024;   // 16 waves, four per SIMD
-constexpr int kWaves = kProdThreads / 64;
-// A work item is 64 rows x 512 columns: each lane owns one 16-column block of a row
-// per step, a wave covers 2 rows x 32 blocks (1 KB of each bf16 input row, one
-// 256-byte QDATA row segment), and the 16 waves cover the 64 rows in 2 steps. Runs
-// of 1 KB per row keep HBM page use and the spread of addresses over the XCDs even.
-constexpr int kItemCols = 512;
-constexpr int kLanesPerRow = kItemCols / 16;
-constexpr int kWaveRows = 64 / kLanesPerRow;
-constexpr int kRowsPerStep = kWaves * kWaveRows;
-constexpr int kItemRows = 2 * kRowsPerStep;
-constexpr int kRedBytes = 128;       // wave maxima and a broadcast slot
-constexpr int kSteps = kItemRows / kRowsPerStep;
+constexpr int kUnitRows = 4;
+constexpr int kUnitCols = 512;
+constexpr int kSteps = 2;                   // steps of 2 rows per unit
+constexpr int kLanesPerRow = kUnitCols / 16;
+constexpr int kAbsWaves = 4;                // absmax workgroup: 4 waves, one unit each
+constexpr int kQuantWaves = 12;             // quantize workgroup: 12 waves, persistent
+static_assert(kLanesPerRow * 2 == 64 && kSteps * 2 == kUnitRows, "unit geometry");
 
 struct ProducerArgs {
-  const uint16_t* x;  // gate (SwiGLU) or x (plain)
+  const uint16_t* x;  // gate (SwiGLU) or x (plain, modulate)
   const uint16_t* u;  // up (SwiGLU)
   int64_t ldx, ldu;   // row strides, elements
   int64_t m, k, m_pad;
   int64_t cpad;       // scale columns
-  int items_m;        // scale row-tiles
   int items_k;        // 512-column segments
+  int nunits;         // (scale rows / 4) * items_k
   uint8_t* qdata;
   uint8_t* scales;
   float* gout;
-  const float* amax_in;  // caller-supplied amax (single-pass variant), else unused
+  const float* amax_in;       // caller-supplied amax (GIVEN), else unused
   const uint16_t* mod_scale;  // modulation scale and shift, bf16 [k] (MODE kModulate)
   const uint16_t* mod_shift;
-  uint32_t* partials;  // absmax launch: one slot per workgroup (the caller's workspace)
-  int npart;           // quantize launch: slots to reduce (the absmax launch's grid)
-  const uint16_t* silu_table;
+  uint32_t* slots;            // the workspace's absmax slots (two-pass), else null
+  uint32_t* queue;            // the quantize launch's counter set
+  const uint16_t* silu_table; // the device silu table (65,536 bf16)
 };
 
 // ---- small helpers ---------------------------------------------------------------------
@@ -190,8 +193,6 @@ __device__ __forceinline__ uint32_t e2m1_step_exact(uint32_t y16, uint32_t s, fl
   return up ? il + 1u : il;
 }
 
-// ---- the kernel ------------------------------------------------------------------------------
-
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 // A nonzero product below 2^-126 may have been rounded in fp32: redo such products
@@ -217,6 +218,7 @@ __device__ __noinline__ Y8 block_y_fix(u32x4_t g0, u32x4_t g1, u32x4_t u0, u32x4
   return yb;
 }
 
+
 // What y is: x itself, RN_bf16(silu_bf16(gate) * up), or the adaLN-modulated
 // RN_bf16(fma_fp32(x, RN_fp32(1 + scale), shift)).
 constexpr int kPlain = 0, kSwiglu = 1, kModulate = 2;
@@ -225,35 +227,6 @@ constexpr int kPlain = 0, kSwiglu = 1, kModulate = 2;
 __device__ __forceinline__ float modulate_f32(uint32_t x16, uint32_t scale16, uint32_t shift16) {
   const float m = 1.0f + bf16_bits_to_float(scale16);
   return __builtin_fmaf(bf16_bits_to_float(x16), m, bf16_bits_to_float(shift16));
-}
-
-// y for the 16 elements of one block, as 8 packed bf16 pairs. For kSwiglu, uv holds
-// up; for kModulate, the item's scale (mv[0]) and shift (mv[1]) of the lane's 16
-// columns. Products are formed in fp32 (exact whenever the result is a normal fp32
-// number); the caller detects blocks that may hold a rounded subnormal product and
-// repairs them with block_y_fix.
-template <int MODE>
-__device__ __forceinline__ void block_y(const u32x4_t (&gv)[2], const u32x4_t (&uv)[2],
-                                        const u32x4_t (&mv)[2][2], const uint16_t* tab, uint32_t (&yb)[8]) {
-  if (MODE == kModulate) {
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const uint32_t xw = gv[w >> 2][w & 3], sw = mv[0][w >> 2][w & 3], bw = mv[1][w >> 2][w & 3];
-      yb[w] = cvt_pk_bf16(modulate_f32(xw & 0xFFFFu, sw & 0xFFFFu, bw & 0xFFFFu),
-                          modulate_f32(xw >> 16, sw >> 16, bw >> 16));
-    }
-  } else if (MODE == kSwiglu) {
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const uint32_t gw = gv[w >> 2][w & 3], uw = uv[w >> 2][w & 3];
-      const float p0 = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16) * __uint_as_float(uw << 16);
-      const float p1 = __uint_as_float((uint32_t)tab[gw >> 16] << 16) * __uint_as_float(uw & 0xFFFF0000u);
-      yb[w] = cvt_pk_bf16(p0, p1);
-    }
-  } else {
-#pragma unroll
-    for (int w = 0; w < 8; ++w) yb[w] = gv[w >> 2][w & 3];
-  }
 }
 
 typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
@@ -277,305 +250,546 @@ __device__ __forceinline__ void block_mag_range(const uint32_t (&yb)[8], uint32_
   mn = lo.x < lo.y ? lo.x : lo.y;
 }
 
-// The 16 bf16 values of this lane's block in each step of an item (zero outside the
-// logical rows and columns). For kModulate the up slots carry the item's modulation
-// instead: uv[0] = the scale and uv[1] = the shift of the lane's 16 columns.
-static_assert(kSteps == 2, "modulation vectors ride in the two up slots");
+
+// ---- unit loads ------------------------------------------------------------------------
+//
+// The lane's 16 bf16 values of each step of unit uu (zero outside the logical rows and
+// columns). Addresses are a per-unit base plus a per-lane offset.
+struct LaneGeom {
+  int r4, blk;          // row within a step, 16-column block of the unit
+  uint32_t lx, lu;      // byte offsets of the lane's first element in x / u
+  int64_t step_x, step_u;  // bytes between the steps (2 rows)
+};
+
+__device__ __forceinline__ LaneGeom lane_geom(const ProducerArgs& a, int lane) {
+  LaneGeom L;
+  L.r4 = lane / kLanesPerRow;
+  L.blk = lane % kLanesPerRow;
+  L.lx = (uint32_t)((L.r4 * a.ldx + L.blk * 16) * 2);
+  L.lu = (uint32_t)((L.r4 * a.ldu + L.blk * 16) * 2);
+  L.step_x = 2 * a.ldx * 2;
+  L.step_u = 2 * a.ldu * 2;
+  return L;
+}
+
 template <int MODE>
-__device__ __forceinline__ void load_item(const ProducerArgs& a, int item, int wave, int r4, int blk,
-                                          u32x4_t (&gv)[kSteps][2], u32x4_t (&uv)[kSteps][2]) {
-  const int rt = item / a.items_k, kt = item - rt * a.items_k;
-  const int64_t col = (int64_t)kt * kItemCols + blk * 16;
-  const u32x4_t z = {0u, 0u, 0u, 0u};
-  if (MODE == kModulate) {
-    const bool cok = col < a.k;
-    const u32x4_t* ps = (const u32x4_t*)(a.mod_scale + col);
-    const u32x4_t* pb = (const u32x4_t*)(a.mod_shift + col);
-    uv[0][0] = cok ? ps[0] : z;
-    uv[0][1] = cok ? ps[1] : z;
-    uv[1][0] = cok ? pb[0] : z;
-    uv[1][1] = cok ? pb[1] : z;
-  }
+__device__ __forceinline__ void load_unit(const ProducerArgs& a, const LaneGeom& L, int uu, u32x4_t (&gv)[kSteps][2],
+                                          u32x4_t (&uv)[kSteps][2]) {
+  constexpr bool SWIGLU = MODE == kSwiglu;
+  const int rt = uu / a.items_k, kt = uu - rt * a.items_k;
+  const int64_t row0 = (int64_t)rt * kUnitRows;
+  const int64_t col0 = (int64_t)kt * kUnitCols;
+  const char* bx = (const char*)a.x + (row0 * a.ldx + col0) * 2;
+  const char* bu = SWIGLU ? (const char*)a.u + (row0 * a.ldu + col0) * 2 : nullptr;
+  if (row0 + kUnitRows <= a.m && col0 + kUnitCols <= a.k) {  // the whole unit is inside (wave-uniform)
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    const int64_t row = (int64_t)rt * kItemRows + s * kRowsPerStep + wave * kWaveRows + r4;
-    const bool ok = row < a.m && col < a.k;
-    const u32x4_t* px = (const u32x4_t*)(a.x + row * a.ldx + col);
-    gv[s][0] = ok ? px[0] : z;
-    gv[s][1] = ok ? px[1] : z;
-    if (MODE == kSwiglu) {
-      const u32x4_t* pu = (const u32x4_t*)(a.u + row * a.ldu + col);
-      uv[s][0] = ok ? pu[0] : z;
-      uv[s][1] = ok ? pu[1] : z;
+    for (int s = 0; s < kSteps; ++s) {
+      const u32x4_t* px = (const u32x4_t*)(bx + s * L.step_x + L.lx);
+      gv[s][0] = px[0];
+      gv[s][1] = px[1];
+      if (SWIGLU) {
+        const u32x4_t* pu = (const u32x4_t*)(bu + s * L.step_u + L.lu);
+        uv[s][0] = pu[0];
+        uv[s][1] = pu[1];
+      }
+    }
+  } else {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    const bool cok = col0 + L.blk * 16 < a.k;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const bool ok = cok && row0 + 2 * s + L.r4 < a.m;
+      const u32x4_t* px = (const u32x4_t*)(bx + s * L.step_x + L.lx);
+      gv[s][0] = ok ? px[0] : z;
+      gv[s][1] = ok ? px[1] : z;
+      if (SWIGLU) {
+        const u32x4_t* pu = (const u32x4_t*)(bu + s * L.step_u + L.lu);
+        uv[s][0] = ok ? pu[0] : z;
+        uv[s][1] = ok ? pu[1] : z;
+      }
     }
   }
 }
 
-// The bf16 silu table into LDS (SwiGLU only).
-__device__ __forceinline__ void stage_silu_table(const uint16_t* src_tab, uint16_t* tab, int tid) {
-  const u32x4_t* src = (const u32x4_t*)src_tab;
-  u32x4_t* dst = (u32x4_t*)tab;
-  for (int i = tid; i < 65536 * 2 / 16; i += kProdThreads) dst[i] = src[i];
-  __syncthreads();
+// The modulation scale (mv[0]) and shift (mv[1]) of the lane's 16 columns of unit uu.
+__device__ __forceinline__ void load_modulation(const ProducerArgs& a, const LaneGeom& L, int uu,
+                                                u32x4_t (&mv)[2][2]) {
+  const int kt = uu % a.items_k;
+  const int64_t col = (int64_t)kt * kUnitCols + L.blk * 16;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  const bool cok = col < a.k;
+  const u32x4_t* ps = (const u32x4_t*)(a.mod_scale + col);
+  const u32x4_t* pb = (const u32x4_t*)(a.mod_shift + col);
+  mv[0][0] = cok ? ps[0] : z;
+  mv[0][1] = cok ? ps[1] : z;
+  mv[1][0] = cok ? pb[0] : z;
+  mv[1][1] = cok ? pb[1] : z;
 }
 
-// Workgroup maximum of v (unsigned), returned to every thread. Uses red[0 .. kWaves].
-__device__ __forceinline__ uint32_t workgroup_max_u32(uint32_t v, uint32_t* red, int tid) {
-  const uint32_t wmax = wave_max_u32(v);
-  if ((tid & 63) == 0) red[tid >> 6] = wmax;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t r = 0;
-    for (int i = 0; i < kWaves; ++i) r = red[i] > r ? red[i] : r;
-    red[kWaves] = r;
-  }
-  __syncthreads();
-  const uint32_t r = red[kWaves];
-  __syncthreads();
+// ---- pass 1: the tensor absmax -----------------------------------------------------------
+
+// |y| of one SwiGLU element exactly, as the fp32 bits of a bf16 magnitude. For
+// gate >= 8, silu_bf16(gate) = gate (1 - sigma(8) < 3.4e-4, under half a bf16 ulp of 8),
+// so the table is not read; a product below 2^-126 is formed in fp64 and rounded once.
+__device__ __forceinline__ uint32_t swiglu_abs_bits(const uint16_t* __restrict__ tab, uint32_t g16, uint32_t u16) {
+  const float gf = bf16_bits_to_float(g16);
+  const float s = gf >= 8.0f ? gf : bf16_bits_to_float(tab[g16]);
+  const float uf = bf16_bits_to_float(u16);
+  const float p = fabsf(s * uf);
+  if (p != 0.0f && p < 0x1p-126f) return (rn_bf16_from_double((double)s * (double)uf) & 0x7FFFu) << 16;
+  return (cvt_pk_bf16(p, 0.0f) & 0x7FFFu) << 16;
+}
+
+typedef __attribute__((ext_vector_type(2))) short i16x2_t;
+
+// The screening key of each element pair: S = bits(G) + bits(|u|) per half, with
+// G = max(gate, 0.28125) (bf16 bits; a signed 16-bit max, since 0.28125 > 0 and
+// negative bf16 values are negative as int16). S fits 16 bits (<= 0x7F7F + 0x7F7F).
+__device__ __forceinline__ uint32_t swiglu_key(uint32_t gw, uint32_t uw) {
+  i16x2_t gi;
+  __builtin_memcpy(&gi, &gw, 4);
+  const i16x2_t floor_bits = {0x3E90, 0x3E90};  // 0.28125
+  const i16x2_t G = __builtin_elementwise_max(gi, floor_bits);
+  u16x2_t gu;
+  __builtin_memcpy(&gu, &G, 4);
+  const u16x2_t S = gu + as_u16x2(uw & 0x7FFF7FFFu);
+  uint32_t r;
+  __builtin_memcpy(&r, &S, 4);
   return r;
 }
 
-// ---- pass 1: the tensor absmax ------------------------------------------------------------------
-//
-// Each workgroup reduces max |y| over its items (every gridDim.x-th item, the next
-// item's loads in flight while the current one is reduced) and writes it to its own
-// slot of the workspace: the bits of a bf16 magnitude shifted into fp32 position.
-// The quantize launch that follows on the same stream reduces the slots; the kernel
-// boundary between the two launches is the grid-wide synchronisation the global
-// scale needs.
-template <int MODE>
-__global__ void __launch_bounds__(kProdThreads) producer_absmax_kernel(ProducerArgs a) {
-  constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint32_t* red = (uint32_t*)smem;
-  uint16_t* tab = (uint16_t*)(smem + kRedBytes);
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int r4 = lane / kLanesPerRow;
-  const int blk = lane % kLanesPerRow;
-  const int nitems = a.items_m * a.items_k;
-  if (SWIGLU) stage_silu_table(a.silu_table, tab, tid);
-
-  uint32_t local_bits = 0;  // fp32 bits of a non-negative value
-  // rows past m read zeros; only the modulation would turn them into nonzero y
-  auto absmax_item = [&](int item, const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
-    const int64_t row0 = (int64_t)(item / a.items_k) * kItemRows + wave * kWaveRows + r4;
+// Exact max |y| over the lane's elements whose key lies in [lo, hi).
+__device__ __forceinline__ uint32_t swiglu_scan(const uint16_t* __restrict__ tab, const u32x4_t (&gv)[kSteps][2],
+                                                const u32x4_t (&uv)[kSteps][2], const uint32_t (&key)[kSteps][8],
+                                                uint32_t lo, uint32_t hi) {
+  uint32_t m = 0;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      if (MOD && row0 + s * kRowsPerStep >= a.m) continue;
+  for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const uint32_t gw = gv[s][w >> 2][w & 3];
-        if (MOD) {
-          const uint32_t sw = uv[0][w >> 2][w & 3], bw = uv[1][w >> 2][w & 3];
-          const float p0 = fabsf(modulate_f32(gw & 0xFFFFu, sw & 0xFFFFu, bw & 0xFFFFu));
-          const float p1 = fabsf(modulate_f32(gw >> 16, sw >> 16, bw >> 16));
-          const uint32_t b = __float_as_uint(fmaxf(p0, p1));
-          local_bits = b > local_bits ? b : local_bits;
-        } else if (SWIGLU) {
-          const uint32_t uw = uv[s][w >> 2][w & 3];
-          const float s0 = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16);
-          const float s1 = __uint_as_float((uint32_t)tab[gw >> 16] << 16);
-          const float p0 = fabsf(s0 * __uint_as_float(uw << 16));
-          const float p1 = fabsf(s1 * __uint_as_float(uw & 0xFFFF0000u));
-          const uint32_t b = __float_as_uint(fmaxf(p0, p1));
-          local_bits = b > local_bits ? b : local_bits;
-        } else {
-          const uint32_t m0 = gw & 0x7FFFu, m1 = (gw >> 16) & 0x7FFFu;
-          const uint32_t b = (m0 > m1 ? m0 : m1) << 16;
-          local_bits = b > local_bits ? b : local_bits;
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t k0 = key[s][w] & 0xFFFFu, k1 = key[s][w] >> 16;
+      const bool c0 = k0 >= lo && k0 < hi, c1 = k1 >= lo && k1 < hi;
+      if (c0 || c1) {
+        const uint32_t gw = gv[s][w >> 2][w & 3], uw = uv[s][w >> 2][w & 3];
+        if (c0) {
+          const uint32_t v = swiglu_abs_bits(tab, gw & 0xFFFFu, uw & 0xFFFFu);
+          m = v > m ? v : m;
+        }
+        if (c1) {
+          const uint32_t v = swiglu_abs_bits(tab, gw >> 16, uw >> 16);
+          m = v > m ? v : m;
         }
       }
     }
-  };
-  {
-    u32x4_t gA[kSteps][2], uA[kSteps][2], gB[kSteps][2], uB[kSteps][2];
-    int item = blockIdx.x;
-    if (item < nitems) load_item<MODE>(a, item, wave, r4, blk, gA, uA);
-    while (item < nitems) {
-      const int n1 = item + (int)gridDim.x;
-      if (n1 < nitems) load_item<MODE>(a, n1, wave, r4, blk, gB, uB);
-      absmax_item(item, gA, uA);
-      item = n1;
-      if (item >= nitems) break;
-      const int n2 = item + (int)gridDim.x;
-      if (n2 < nitems) load_item<MODE>(a, n2, wave, r4, blk, gA, uA);
-      absmax_item(item, gB, uB);
-      item = n2;
-    }
-  }
-  // workgroup max of the unrounded |products| (SwiGLU) or of |x|
-  local_bits = workgroup_max_u32(local_bits, red, tid);
-  // A product below 2^-126 may have been rounded in fp32; if this workgroup's maximum
-  // is such a product, redo its elements exactly (never taken for inputs whose absmax
-  // is a normal number).
-  if (SWIGLU && local_bits != 0 && local_bits < 0x00800000u) {
-    uint32_t best = 0;  // bf16 magnitude bits
-    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-      u32x4_t gv[kSteps][2], uv[kSteps][2];
-      load_item<MODE>(a, item, wave, r4, blk, gv, uv);
-      for (int s = 0; s < kSteps; ++s)
-        for (int j = 0; j < 16; ++j) {
-          const uint32_t g16 = (gv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
-          const uint32_t u16 = (uv[s][j >> 3][(j >> 1) & 3] >> (16 * (j & 1))) & 0xFFFFu;
-          const double p = (double)bf16_bits_to_float(tab[g16]) * (double)bf16_bits_to_float(u16);
-          const uint32_t y = rn_bf16_from_double(p) & 0x7FFFu;
-          best = y > best ? y : best;
-        }
-    }
-    local_bits = workgroup_max_u32(best, red, tid) << 16;
-  } else if (SWIGLU || MOD) {
-    // RN_bf16 is monotone, so the rounded maximum is the maximum of the rounded values.
-    local_bits = (cvt_pk_bf16(__uint_as_float(local_bits), 0.0f) & 0xFFFFu) << 16;
-  }
-  if (tid == 0) a.partials[blockIdx.x] = local_bits;
+  return m;
 }
 
-// ---- pass 2: scales, codes, pack, swizzle ---------------------------------------------------------
-//
-// GIVEN: the tensor amax comes from the caller (a device float). Otherwise it is the
-// maximum of the absmax launch's a.npart workgroup partials.
-template <int MODE, bool GIVEN>
-__global__ void __launch_bounds__(kProdThreads) producer_kernel(ProducerArgs a) {
+// max |y| of one SwiGLU unit held by a wave, exactly (fp32 bits of a bf16 magnitude;
+// the same value in every lane), screened in the log domain:
+//   |y| = RN_bf16(|silu_bf16(g)| |u|) <= RN_bf16(B), B = max(g, 0.28125) |u|, since
+//   silu(g) < g for g > 0 and |silu(g)| <= 0.2785 for g <= 0, kept by the rounding.
+//   For finite x, log2 x <= bits(x) / 128 - 127 + 0.0861 (0.0861 = max of
+//   log2(1 + t) - t on [0, 1); bf16 subnormals and zero satisfy it without the term),
+//   so log2 B <= S / 128 - 254 + 0.1722; and for a normal bf16 value M,
+//   log2 M >= bits(M) / 128 - 127. Hence S <= bits(M) + 16233 implies B < M and
+//   |y| <= M: such elements cannot raise an exact maximum M.
+// The elements within 23 of the wave's largest key are evaluated exactly (the likely
+// maximum); then every element whose key still reaches bits(M) + 16234 is; if M is
+// below 2^-126 (or zero), every element is.
+__device__ __forceinline__ uint32_t swiglu_unit_absmax(const uint16_t* __restrict__ tab, const u32x4_t (&gv)[kSteps][2],
+                                                       const u32x4_t (&uv)[kSteps][2]) {
+  uint32_t key[kSteps][8];
+  u16x2_t kmax = {0, 0};
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      key[s][w] = swiglu_key(gv[s][w >> 2][w & 3], uv[s][w >> 2][w & 3]);
+      kmax = __builtin_elementwise_max(kmax, as_u16x2(key[s][w]));
+    }
+  const uint32_t lmax = kmax.x > kmax.y ? kmax.x : kmax.y;
+  const uint32_t top = wave_max_u32(lmax);
+  const uint32_t t1 = top - 23u;  // keys are >= 0x3E90, so no wrap
+  uint32_t m = 0;
+  if (lmax >= t1) m = swiglu_scan(tab, gv, uv, key, t1, 0x10000u);
+  m = wave_max_u32(m);
+  const uint32_t mb = m >> 16;  // bf16 bits of the exact maximum so far
+  if (mb < 0x0080u) {
+    // the maximum so far is subnormal or zero: the bound argument needs a normal M
+    const uint32_t m2 = swiglu_scan(tab, gv, uv, key, 0u, t1);
+    m = wave_max_u32(m2 > m ? m2 : m);
+  } else {
+    const uint32_t t2 = mb + 16234u;
+    if (t2 < t1) {
+      uint32_t m2 = 0;
+      if (lmax >= t2) m2 = swiglu_scan(tab, gv, uv, key, t2, t1);
+      m = wave_max_u32(m2 > m ? m2 : m);
+    }
+  }
+  return m;
+}
+
+// The absmax launch reads a unit row by row: load instruction r takes row r's 1 KB
+// segment of each input in one contiguous piece (lane L: columns 8L .. 8L + 7), with
+// non-temporal loads, since nothing here is read twice. Measured on MI355X after the
+// FC2 GEMM, this streams gate and up about 10 % faster than 32 bytes per lane in two
+// interleaved loads; the maximum does not care which lane holds which element. gv[s][h]
+// holds unit row 2s + h (zero outside the logical rows and columns); mv, for kModulate,
+// the scale and shift of the lane's 8 columns.
+template <int MODE>
+__device__ __forceinline__ void load_unit_rows(const ProducerArgs& a, int lane, int uu, u32x4_t (&gv)[kSteps][2],
+                                               u32x4_t (&uv)[kSteps][2], u32x4_t (&mv)[2]) {
   constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint32_t* red = (uint32_t*)smem;                          // wave maxima + a broadcast slot
-  uint16_t* tab = (uint16_t*)(smem + kRedBytes);            // 65,536 entries (SwiGLU only)
+  const int rt = uu / a.items_k, kt = uu - rt * a.items_k;
+  const int64_t row0 = (int64_t)rt * kUnitRows;
+  const int64_t col0 = (int64_t)kt * kUnitCols;
+  const int64_t col = col0 + lane * 8;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  if (row0 + kUnitRows <= a.m && col0 + kUnitCols <= a.k) {  // the whole unit is inside (wave-uniform)
+#pragma unroll
+    for (int r = 0; r < kUnitRows; ++r) {
+      gv[r >> 1][r & 1] = __builtin_nontemporal_load((const u32x4_t*)(a.x + (row0 + r) * a.ldx + col));
+      if (SWIGLU) uv[r >> 1][r & 1] = __builtin_nontemporal_load((const u32x4_t*)(a.u + (row0 + r) * a.ldu + col));
+    }
+  } else {
+    const bool cok = col < a.k;
+#pragma unroll
+    for (int r = 0; r < kUnitRows; ++r) {
+      const bool ok = cok && row0 + r < a.m;
+      gv[r >> 1][r & 1] = ok ? __builtin_nontemporal_load((const u32x4_t*)(a.x + (row0 + r) * a.ldx + col)) : z;
+      if (SWIGLU)
+        uv[r >> 1][r & 1] = ok ? __builtin_nontemporal_load((const u32x4_t*)(a.u + (row0 + r) * a.ldu + col)) : z;
+    }
+  }
+  if (MOD) {
+    const bool cok = col < a.k;
+    mv[0] = cok ? *(const u32x4_t*)(a.mod_scale + col) : z;
+    mv[1] = cok ? *(const u32x4_t*)(a.mod_shift + col) : z;
+  }
+}
 
+// One-shot grid: workgroup b covers units 4b .. 4b + 3 (more only when the grid is
+// capped), one per wave, in address order; its maximum goes to slot b % kAmaxSlots.
+template <int MODE>
+__global__ void __launch_bounds__(kAbsWaves * 64) producer_absmax_kernel(ProducerArgs a) {
+  constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
+  __shared__ uint32_t red[kAbsWaves];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so unit arithmetic stays scalar
   const int lane = tid & 63;
-  const int r4 = lane / kLanesPerRow;   // row within the wave's rows of a step
-  const int blk = lane % kLanesPerRow;  // 16-column block of the item's column segment
-  const int nitems = a.items_m * a.items_k;
-  if (SWIGLU) stage_silu_table(a.silu_table, tab, tid);
+  uint32_t mall = 0;  // fp32 bits of a bf16 magnitude
+  const int groups = (a.nunits + kAbsWaves - 1) / kAbsWaves;
+  for (int b = blockIdx.x; b < groups; b += gridDim.x) {
+    const int uu = b * kAbsWaves + wave;
+    if (uu >= a.nunits) break;
+    u32x4_t gv[kSteps][2], uv[kSteps][2], mv[2];
+    load_unit_rows<MODE>(a, lane, uu, gv, uv, mv);
+    uint32_t m = 0;
+    if (SWIGLU) {
+      m = swiglu_unit_absmax(a.silu_table, gv, uv);
+    } else if (MOD) {
+      const int64_t row0 = (int64_t)(uu / a.items_k) * kUnitRows;
+#pragma unroll
+      for (int r = 0; r < kUnitRows; ++r) {
+        if (row0 + r >= a.m) continue;  // padding rows are zero, not the shift
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t xw = gv[r >> 1][r & 1][w], sw = mv[0][w], bw = mv[1][w];
+          const uint32_t yw = cvt_pk_bf16(modulate_f32(xw & 0xFFFFu, sw & 0xFFFFu, bw & 0xFFFFu),
+                                          modulate_f32(xw >> 16, sw >> 16, bw >> 16));
+          const uint32_t m0 = (yw & 0x7FFFu) << 16, m1 = (yw & 0x7FFF0000u);
+          m = m0 > m ? m0 : m;
+          m = m1 > m ? m1 : m;
+        }
+      }
+    } else {
+      u16x2_t pm = {0, 0};
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) pm = __builtin_elementwise_max(pm, as_u16x2(gv[s][w >> 2][w & 3] & 0x7FFF7FFFu));
+      m = (uint32_t)(pm.x > pm.y ? pm.x : pm.y) << 16;
+    }
+    mall = m > mall ? m : mall;
+  }
+  mall = wave_max_u32(mall);
+  if (lane == 0) red[wave] = mall;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < kAbsWaves; ++i) r = red[i] > r ? red[i] : r;
+    if (r != 0)
+      __hip_atomic_fetch_max(a.slots + (blockIdx.x % kAmaxSlots) * kSlotStride, r, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
+// ---- pass 2: scales, codes, pack, swizzle ---------------------------------------------------
+
+// y for the 16 elements of one block, as 8 packed bf16 pairs. For kSwiglu, uv holds
+// up; for kModulate, mv the lane's scale (mv[0]) and shift (mv[1]). Products are formed
+// in fp32 (exact whenever the result is a normal fp32 number); the caller detects
+// blocks that may hold a rounded subnormal product and repairs them with block_y_fix.
+template <int MODE>
+__device__ __forceinline__ void block_y(const u32x4_t (&gv)[2], const u32x4_t (&uv)[2], const u32x4_t (&mv)[2][2],
+                                        const uint16_t* tab, uint32_t (&yb)[8]) {
+  if (MODE == kModulate) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t xw = gv[w >> 2][w & 3], sw = mv[0][w >> 2][w & 3], bw = mv[1][w >> 2][w & 3];
+      yb[w] = cvt_pk_bf16(modulate_f32(xw & 0xFFFFu, sw & 0xFFFFu, bw & 0xFFFFu),
+                          modulate_f32(xw >> 16, sw >> 16, bw >> 16));
+    }
+  } else if (MODE == kSwiglu) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t gw = gv[w >> 2][w & 3], uw = uv[w >> 2][w & 3];
+      const float p0 = __uint_as_float((uint32_t)tab[gw & 0xFFFFu] << 16) * __uint_as_float(uw << 16);
+      const float p1 = __uint_as_float((uint32_t)tab[gw >> 16] << 16) * __uint_as_float(uw & 0xFFFF0000u);
+      yb[w] = cvt_pk_bf16(p0, p1);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) yb[w] = gv[w >> 2][w & 3];
+  }
+}
+
+struct QuantCtx {
+  float g, bscale, inv_f;
+  double g6;
+};
+
+__device__ __forceinline__ QuantCtx quant_ctx(float amax) {
+  QuantCtx c;
+  c.g = global_scale_from_amax(amax);
+  c.g6 = 6.0 * (double)c.g;
+  // 1 / (6g) in fp32; for a tiny g both factors of bmax / (6g) are scaled by 2^64 (exact)
+  double inv_g6 = c.g6 > 0.0 ? 1.0 / c.g6 : 0.0;
+  c.bscale = 1.0f;
+  if (inv_g6 > 0x1p+100) {
+    inv_g6 *= 0x1p-64;
+    c.bscale = 0x1p+64f;
+  }
+  c.inv_f = (float)inv_g6;
+  return c;
+}
+
+// The 8 codes of one half-block, c from the lower bracket and ch from the upper one,
+// where they differ: element j is the lower code il or the next one up. For unit >=
+// 2^-90 the sign of fma(mid * v(S), g, -|y|) decides exactly (mid * v(S) = (4 mid) *
+// (v(S) / 4) has at most 7 significant bits; the exact difference, when not zero, is a
+// multiple of 2^-122, so the fused result keeps its sign); a tie goes to the even index.
+// Smaller units use exact fp64 compares.
+__device__ __forceinline__ uint32_t fix_half(uint32_t c, uint32_t ch, uint32_t y0, uint32_t y1, uint32_t y2, uint32_t y3,
+                                             float vS4, float g, bool fma_ok, uint32_t S) {
+  const uint32_t dall = c ^ ch;
+  uint32_t d = dall;
+  while (d) {
+    const uint32_t j = (uint32_t)__builtin_ctz(d) >> 2;  // element 0..7 of the half
+    const uint32_t sh = j << 2;
+    d &= ~(0xFu << sh);
+    const uint32_t yw = (j & 4u) ? ((j & 2u) ? y3 : y2) : ((j & 2u) ? y1 : y0);
+    const uint32_t y16 = (j & 1u) ? (yw >> 16) : (yw & 0xFFFFu);
+    const uint32_t il = (c >> sh) & 7u, ih = (ch >> sh) & 7u;
+    if (ih == il + 1u) {
+      bool up;
+      if (fma_ok) {
+        const float ay = __uint_as_float((y16 & 0x7FFFu) << 16);
+        const uint64_t mids4 = 0x00140E0A07050301ull;  // 4 x the midpoint above index 0..6
+        const float mid4 = (float)(uint32_t)((mids4 >> (8u * il)) & 0xFFu);
+        const float dd = __builtin_fmaf(mid4 * vS4, g, -ay);
+        up = (il & 1u) ? (dd <= 0.0f) : (dd < 0.0f);
+      } else {
+        up = e2m1_step_exact(y16, S, g, il) != il;
+      }
+      if (up) c ^= dall & (0xFu << sh);
+    } else {
+      c = (c & ~(0xFu << sh)) | (e2m1_code_exact(y16, S, g) << sh);
+    }
+  }
+  return c;
+}
+
+// One step of a unit: the scale byte and the 16 codes of the lane's block of row `row`
+// (column `col`), stored at qdst / sdst. `store_q`: the row is below m_pad; `cok`: the
+// block is inside the columns.
+template <int MODE>
+__device__ __forceinline__ void quantize_block(const ProducerArgs& a, const QuantCtx& c, const u32x4_t (&gv)[2],
+                                               const u32x4_t (&uv)[2], const u32x4_t (&mv)[2][2], const uint16_t* tab,
+                                               int64_t row, bool store_q, bool cok, uint8_t* qdst, uint8_t* sdst) {
+  constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
+  const float g = c.g;
+  uint32_t yb[8];
+  block_y<MODE>(gv, uv, mv, tab, yb);
+  if (MOD && row >= a.m) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) yb[w] = 0u;  // padding rows are zero, not the shift
+  }
+  // block maximum of |y| (bf16 magnitudes compare as integers)
+  uint32_t mx, mn;
+  block_mag_range(yb, mx, mn);
+  if (SWIGLU && mn <= 0x0080u) {
+    // some |y| <= 2^-126 (or zero): its fp32 product may have been subnormal and
+    // rounded; redo such products exactly
+    Y8 y;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) y.v[w] = yb[w];
+    y = block_y_fix(gv[0], gv[1], uv[0], uv[1], y, tab);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) yb[w] = y.v[w];
+    block_mag_range(yb, mx, mn);
+  }
+  const uint32_t S = (mx == 0) ? 0u : block_scale_byte(bf16_bits_to_float(mx), c.bscale, c.inv_f, c.g6);
+
+  // E2M1 codes of the 16 elements
+  const float vS = ue4m3_to_float(S);
+  const float unit = vS * g;
+  const bool exact_block = (S != 0) && !(unit >= 0x1p-100f);
+  const float rcp = (S == 0) ? 1.0f : __builtin_amdgcn_rcpf(unit);
+  const float rlo = rcp * (1.0f - 0x1p-20f);
+  const float rhi = rcp * (1.0f + 0x1p-20f);
+  uint32_t clo0 = 0, chi0 = 0, clo1 = 0, chi1 = 0;
+  fp4_pair<0>(clo0, chi0, yb[0], rlo, rhi);
+  fp4_pair<1>(clo0, chi0, yb[1], rlo, rhi);
+  fp4_pair<2>(clo0, chi0, yb[2], rlo, rhi);
+  fp4_pair<3>(clo0, chi0, yb[3], rlo, rhi);
+  fp4_pair<0>(clo1, chi1, yb[4], rlo, rhi);
+  fp4_pair<1>(clo1, chi1, yb[5], rlo, rhi);
+  fp4_pair<2>(clo1, chi1, yb[6], rlo, rhi);
+  fp4_pair<3>(clo1, chi1, yb[7], rlo, rhi);
+  if (exact_block) {
+    uint32_t cc[2] = {0u, 0u};
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t y16 = (yb[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      cc[j >> 3] |= e2m1_code_exact(y16, S, g) << (4 * (j & 7));
+    }
+    clo0 = cc[0];
+    clo1 = cc[1];
+  } else if ((clo0 ^ chi0) | (clo1 ^ chi1)) {
+    // The two bracket codes differ only where |y| / unit lies within the bracket of an
+    // E2M1 rounding boundary: there the code is one of two neighbours, decided by one
+    // exact comparison with that boundary (the other elements keep theirs).
+    const bool fma_ok = unit >= 0x1p-90f;
+    const float vS4 = vS * 0.25f;
+    if (clo0 ^ chi0) clo0 = fix_half(clo0, chi0, yb[0], yb[1], yb[2], yb[3], vS4, g, fma_ok, S);
+    if (clo1 ^ chi1) clo1 = fix_half(clo1, chi1, yb[4], yb[5], yb[6], yb[7], vS4, g, fma_ok, S);
+  }
+  if (store_q && cok) {
+    const u32x2_t v = {clo0, clo1};
+    *(u32x2_t*)qdst = v;
+  }
+  if (cok) *sdst = (uint8_t)S;
+}
+
+// Persistent grid of kQuantWaves-wave workgroups. Wave w (global index) takes units
+// from counter w % kProdQueueCounters of the launch's set: the t-th take of counter j
+// is unit t * kProdQueueCounters + j, walked from the end of the tensor (uu = nunits -
+// 1 - unit). Takes are issued two units ahead of their use. GIVEN: the tensor amax
+// comes from the caller (a device float); otherwise it is the maximum of the
+// workspace's slots, which the last wave clears together with the counters.
+template <int MODE, bool GIVEN>
+__global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs a) {
+  constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
+  __shared__ uint32_t red[kQuantWaves];  // wave maxima
+  // The bf16 silu table (SwiGLU only) at a fixed LDS address, so that each lookup's
+  // address is one shift of the gate bits.
+  uint16_t* tab = nullptr;
+  if constexpr (SWIGLU) {
+    __shared__ __attribute__((aligned(16))) uint16_t silu_lds[65536];
+    tab = silu_lds;
+  }
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so unit arithmetic stays scalar
+  const int lane = tid & 63;
+  const LaneGeom L = lane_geom(a, lane);
+  const int j = (blockIdx.x * kQuantWaves + wave) % kProdQueueCounters;
+  uint32_t* ctr = a.queue + j * kSlotStride;
+
+  uint32_t t0 = 0, t1 = 0;
+  if (lane == 0) {
+    t0 = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t1 = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  int u = (int)__builtin_amdgcn_readfirstlane(t0) * kProdQueueCounters + j;
+  int un = (int)__builtin_amdgcn_readfirstlane(t1) * kProdQueueCounters + j;
+  // the first unit's loads are in flight while the table is staged and amax reduced
+  u32x4_t gv[kSteps][2], uv[kSteps][2], mv[2][2];
+  if (u < a.nunits) {
+    load_unit<MODE>(a, L, a.nunits - 1 - u, gv, uv);
+    if (MOD) load_modulation(a, L, a.nunits - 1 - u, mv);
+  }
+  uint32_t slot_max = 0;
+  if (!GIVEN && tid < kAmaxSlots) slot_max = a.slots[tid * kSlotStride];
+  if (SWIGLU) {
+    const u32x4_t* src = (const u32x4_t*)a.silu_table;
+    u32x4_t* dst = (u32x4_t*)tab;
+    for (int i = tid; i < 65536 * 2 / 16; i += kQuantWaves * 64) dst[i] = src[i];
+  }
   float amax;
   if constexpr (GIVEN) {
     amax = a.amax_in[0];
+    if (SWIGLU) __syncthreads();
   } else {
-    uint32_t v = 0;
-    for (int i = tid; i < a.npart; i += kProdThreads) {
-      const uint32_t p = a.partials[i];
-      v = p > v ? p : v;
-    }
-    amax = __uint_as_float(workgroup_max_u32(v, red, tid));
+    slot_max = wave_max_u32(slot_max);
+    if (lane == 0) red[wave] = slot_max;
+    __syncthreads();
+    uint32_t r = 0;
+    for (int i = 0; i < kQuantWaves; ++i) r = red[i] > r ? red[i] : r;
+    amax = __uint_as_float(r);
   }
-  const float g = global_scale_from_amax(amax);
-  const double g6 = 6.0 * (double)g;
-  // 1 / (6g) in fp32; for a tiny g both factors of bmax / (6g) are scaled by 2^64 (exact)
-  double inv_g6 = g6 > 0.0 ? 1.0 / g6 : 0.0;
-  float bscale = 1.0f;
-  if (inv_g6 > 0x1p+100) {
-    inv_g6 *= 0x1p-64;
-    bscale = 0x1p+64f;
-  }
-  const float inv_f = (float)inv_g6;
-  if (blockIdx.x == 0 && tid == 0) *a.gout = g;
+  const QuantCtx c = quant_ctx(amax);
+  if (blockIdx.x == 0 && tid == 0) *a.gout = c.g;
 
-  const int64_t qrow_bytes = a.k / 2;
-  auto quantize_item = [&](int item, const u32x4_t (&gv)[kSteps][2], const u32x4_t (&uv)[kSteps][2]) {
-    const int rt = item / a.items_k, kt = item - rt * a.items_k;
-    const int64_t col = (int64_t)kt * kItemCols + blk * 16;
+  const int64_t qrow = a.k / 2;
+  while (u < a.nunits) {
+    uint32_t tr = 0;
+    if (lane == 0) tr = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    {
+      const int uu = a.nunits - 1 - u;
+      const int rt = uu / a.items_k, kt = uu - rt * a.items_k;
+      const int64_t row0 = (int64_t)rt * kUnitRows;
+      const bool cok = (int64_t)kt * kUnitCols + L.blk * 16 < a.k;
+      const bool store_q = row0 < a.m_pad;  // units are 4-row aligned, m_pad 16-row aligned
+      uint8_t* bq = a.qdata + row0 * qrow + kt * (kUnitCols / 2) + L.r4 * qrow + L.blk * 8;
+      // scale byte of (row, block column bc) in its 128 x 4 tile; a unit stays inside one
+      // 32-row group of one tile
+      const int64_t bc = (int64_t)kt * kLanesPerRow + L.blk;
+      uint8_t* bs = a.scales + ((row0 >> 7) * (a.cpad / 4) + (bc >> 2)) * 512 + (row0 & 31) * 16 +
+                    ((row0 >> 5) & 3) * 4 + L.r4 * 16 + (bc & 3);
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int lrow = s * kRowsPerStep + wave * kWaveRows + r4;
-      const int64_t row = (int64_t)rt * kItemRows + lrow;
-      uint32_t yb[8];
-      block_y<MODE>(gv[s], uv[s], uv, tab, yb);
-      if (MOD && row >= a.m) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) yb[w] = 0u;  // padding rows are zero, not the shift
-      }
-      // block maximum of |y| (bf16 magnitudes compare as integers)
-      uint32_t mx, mn;
-      block_mag_range(yb, mx, mn);
-      if (SWIGLU && mn <= 0x0080u) {
-        // some |y| <= 2^-126 (or zero): its fp32 product may have been subnormal and
-        // rounded; redo such products exactly
-        Y8 y;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) y.v[w] = yb[w];
-        y = block_y_fix(gv[s][0], gv[s][1], uv[s][0], uv[s][1], y, tab);
-#pragma unroll
-        for (int w = 0; w < 8; ++w) yb[w] = y.v[w];
-        block_mag_range(yb, mx, mn);
-      }
-      const uint32_t S = (mx == 0) ? 0u : block_scale_byte(bf16_bits_to_float(mx), bscale, inv_f, g6);
-
-      // E2M1 codes of the 16 elements
-      const float unit = ue4m3_to_float(S) * g;
-      const bool exact_block = (S != 0) && !(unit >= 0x1p-100f);
-      const float rcp = (S == 0) ? 1.0f : __builtin_amdgcn_rcpf(unit);
-      const float rlo = rcp * (1.0f - 0x1p-20f);
-      const float rhi = rcp * (1.0f + 0x1p-20f);
-      uint32_t clo0 = 0, chi0 = 0, clo1 = 0, chi1 = 0;
-      fp4_pair<0>(clo0, chi0, yb[0], rlo, rhi);
-      fp4_pair<1>(clo0, chi0, yb[1], rlo, rhi);
-      fp4_pair<2>(clo0, chi0, yb[2], rlo, rhi);
-      fp4_pair<3>(clo0, chi0, yb[3], rlo, rhi);
-      fp4_pair<0>(clo1, chi1, yb[4], rlo, rhi);
-      fp4_pair<1>(clo1, chi1, yb[5], rlo, rhi);
-      fp4_pair<2>(clo1, chi1, yb[6], rlo, rhi);
-      fp4_pair<3>(clo1, chi1, yb[7], rlo, rhi);
-      if (exact_block) {
-        uint32_t c[2] = {0u, 0u};
-        for (int j = 0; j < 16; ++j) {
-          const uint32_t y16 = (yb[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-          c[j >> 3] |= e2m1_code_exact(y16, S, g) << (4 * (j & 7));
-        }
-        clo0 = c[0];
-        clo1 = c[1];
-      } else if ((clo0 ^ chi0) | (clo1 ^ chi1)) {
-        // The two bracket codes differ only where |y| / unit lies within the bracket of
-        // an E2M1 rounding boundary: there the code is one of two neighbours, decided
-        // by one exact comparison with that boundary (the other elements keep theirs).
-        uint64_t d = ((uint64_t)(clo1 ^ chi1) << 32) | (clo0 ^ chi0);
-        while (d) {
-          const int j = (int)(__builtin_ctzll(d) >> 2);  // element 0..15
-          d &= ~(0xFull << (4 * j));
-          const uint32_t y16 = (yb[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-          const uint32_t sh = 4 * (j & 7);
-          const uint32_t nl = ((j < 8 ? clo0 : clo1) >> sh) & 15u, nh = ((j < 8 ? chi0 : chi1) >> sh) & 15u;
-          const uint32_t il = nl & 7u, ih = nh & 7u;
-          uint32_t code;
-          if (ih == il + 1u) {
-            code = ((y16 >> 15) << 3) | e2m1_step_exact(y16, S, g, il);
-          } else {
-            code = e2m1_code_exact(y16, S, g);
-          }
-          if (j < 8) clo0 = (clo0 & ~(15u << sh)) | (code << sh);
-          else clo1 = (clo1 & ~(15u << sh)) | (code << sh);
-        }
-      }
-      if (row < a.m_pad && col < a.k) {
-        const u32x2_t v = {clo0, clo1};
-        *(u32x2_t*)(a.qdata + row * qrow_bytes + col / 2) = v;
-      }
-      // the scale byte at its place in its 128 x 4 tile (rows past m_pad hold zero)
-      if (col < a.k) {
-        const int64_t bc = (int64_t)kt * kLanesPerRow + blk;  // block column
-        const int64_t tile = (row >> 7) * (a.cpad / 4) + (bc >> 2);
-        a.scales[tile * 512 + (row & 31) * 16 + ((row >> 5) & 3) * 4 + (bc & 3)] = (uint8_t)S;
-      }
+      for (int s = 0; s < kSteps; ++s)
+        quantize_block<MODE>(a, c, gv[s], uv[s], mv, tab, row0 + 2 * s + L.r4, store_q, cok, bq + s * 2 * qrow,
+                             bs + s * 32);
     }
-  };
-  // Items in reverse order: the rows the absmax launch read last, still in the
-  // memory-side cache, are read first. No workgroup barrier: the 16 waves drift apart
-  // and hide each other's load latency.
-  for (int item = nitems - 1 - (int)blockIdx.x; item >= 0; item -= (int)gridDim.x) {
-    u32x4_t gv[kSteps][2], uv[kSteps][2];
-    load_item<MODE>(a, item, wave, r4, blk, gv, uv);
-    quantize_item(item, gv, uv);
+    u = un;
+    un = (int)__builtin_amdgcn_readfirstlane(tr) * kProdQueueCounters + j;
+    if (u < a.nunits) {
+      load_unit<MODE>(a, L, a.nunits - 1 - u, gv, uv);
+      if (MOD) load_modulation(a, L, a.nunits - 1 - u, mv);
+    }
+  }
+  // Every take of this wave has returned (its last value was read above). The last wave
+  // to count itself clears the counter set and, after a two-pass call, the slots: every
+  // wave read the slots before its loop.
+  uint32_t done = 0;
+  if (lane == 0)
+    done = __hip_atomic_fetch_add(a.queue + kProdQueueCounters * kSlotStride, 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  done = __builtin_amdgcn_readfirstlane(done);
+  if (done == gridDim.x * kQuantWaves - 1) {
+    if (lane < kProdQueueCounters)
+      __hip_atomic_store(a.queue + lane * kSlotStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!GIVEN && lane < kAmaxSlots)
+      __hip_atomic_store(a.slots + lane * kSlotStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0)
+      __hip_atomic_store(a.queue + kProdQueueCounters * kSlotStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // ---- host side --------------------------------------------------------------------------------
 
-size_t producer_smem_bytes(int mode) {
-  return kRedBytes + (mode == kSwiglu ? 65536 * 2 : 0);
-}
+// dynamic LDS of the quantize launch (its table and wave maxima are static)
+size_t producer_smem_bytes(int) { return 0; }
 
 const void* producer_kernel_ptr(int mode, bool given) {
   if (mode == kSwiglu)
@@ -591,16 +805,22 @@ const void* producer_absmax_kernel_ptr(int mode) {
   return (const void*)producer_absmax_kernel<kPlain>;
 }
 
-int producer_block_threads() { return kProdThreads; }
+int producer_block_threads() { return kQuantWaves * 64; }
 
-// amax_in == nullptr: the two-pass producer (absmax launch into the workspace's
-// partials, then the quantize launch); otherwise the single-read producer with the
-// caller's amax (the quantize launch alone). Both are ordinary launches of at most
-// max_blocks (<= kMaxPartials) workgroups.
+int64_t producer_units(int64_t m, int64_t k) {
+  const int64_t m_pad = (m + 15) / 16 * 16;
+  const int64_t scale_rows = (m_pad + 127) / 128 * 128;
+  return scale_rows / kUnitRows * ((k + kUnitCols - 1) / kUnitCols);
+}
+
+// amax_in == nullptr: the two-pass producer (absmax launch into the workspace's slots,
+// then the quantize launch); otherwise the single-read producer with the caller's amax
+// (the quantize launch alone). `queue` is a zeroed counter set of kProdQueueSetWords
+// words; the quantize launch's grid is `quant_blocks` workgroups.
 hipError_t launch_producer(int mode, const uint16_t* x, int64_t ldx, const uint16_t* u, int64_t ldu,
                            const uint16_t* mod_scale, const uint16_t* mod_shift, int64_t m, int64_t k,
                            uint8_t* qdata, uint8_t* scales, float* gout, const float* amax_in, void* workspace,
-                           const uint16_t* silu_table, int max_blocks, hipStream_t stream) {
+                           uint32_t* queue, const uint16_t* silu_table, int quant_blocks, hipStream_t stream) {
   ProducerArgs args;
   args.x = x;
   args.u = u;
@@ -610,36 +830,29 @@ hipError_t launch_producer(int mode, const uint16_t* x, int64_t ldx, const uint1
   args.k = k;
   args.m_pad = (m + 15) / 16 * 16;
   args.cpad = (k / 16 + 3) / 4 * 4;
-  const int64_t scale_rows = (args.m_pad + 127) / 128 * 128;
-  args.items_m = (int)(scale_rows / kItemRows);
-  args.items_k = (int)((k + kItemCols - 1) / kItemCols);
+  args.items_k = (int)((k + kUnitCols - 1) / kUnitCols);
+  args.nunits = (int)producer_units(m, k);
   args.qdata = qdata;
   args.scales = scales;
   args.gout = gout;
   args.amax_in = amax_in;
   args.mod_scale = mod_scale;
   args.mod_shift = mod_shift;
-  args.partials = workspace ? ((ProducerWorkspace*)workspace)->partial : nullptr;
-  args.npart = 0;
+  args.slots = workspace ? ((ProducerWorkspace*)workspace)->slot : nullptr;
+  args.queue = queue;
   args.silu_table = silu_table;
-  const int64_t nitems = (int64_t)args.items_m * args.items_k;
-  if (max_blocks > kMaxPartials) max_blocks = kMaxPartials;
-  int blocks = (int)(nitems < max_blocks ? nitems : max_blocks);
-  if (blocks < 1) blocks = 1;
   const size_t smem = producer_smem_bytes(mode);
-  if (amax_in) {
+  if (!amax_in) {
+    const int64_t groups = ((int64_t)args.nunits + kAbsWaves - 1) / kAbsWaves;
+    const int grid = (int)(groups < ((int64_t)1 << 30) ? groups : ((int64_t)1 << 30));
     void* kargs[] = {&args};
-    return hipLaunchKernel(producer_kernel_ptr(mode, true), dim3(blocks), dim3(kProdThreads), kargs, smem, stream);
-  }
-  {
-    void* kargs[] = {&args};
-    hipError_t e = hipLaunchKernel(producer_absmax_kernel_ptr(mode), dim3(blocks), dim3(kProdThreads), kargs, smem,
-                                   stream);
+    hipError_t e = hipLaunchKernel(producer_absmax_kernel_ptr(mode), dim3(grid < 1 ? 1 : grid), dim3(kAbsWaves * 64),
+                                   kargs, 0, stream);
     if (e != hipSuccess) return e;
   }
-  args.npart = blocks;
   void* kargs[] = {&args};
-  return hipLaunchKernel(producer_kernel_ptr(mode, false), dim3(blocks), dim3(kProdThreads), kargs, smem, stream);
+  return hipLaunchKernel(producer_kernel_ptr(mode, amax_in != nullptr), dim3(quant_blocks < 1 ? 1 : quant_blocks),
+                         dim3(kQuantWaves * 64), kargs, smem, stream);
 }
 
 }  // namespace nvfp4

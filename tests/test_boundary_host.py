@@ -55,7 +55,7 @@ def test_sizes_match_oracle_geometry(rows, k):
 def test_size_functions_reject_negative():
     assert nv.nvfp4_padded_rows(-1) == -1
     assert nv.nvfp4_qdata_bytes(-1, 64) == -1
-    assert nv.nvfp4_quantize_workspace_bytes() == 4096
+    assert nv.nvfp4_quantize_workspace_bytes() == 16384
 
 
 FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced: validation fails first

@@ -146,21 +146,27 @@ def test_extreme_magnitudes_plain(gpu):
 
 
 def test_workspace_reuse_and_determinism(gpu):
-    """The workspace needs no initialisation: a workspace full of 0xA5 bytes, reused by
-    back-to-back calls of different sizes and modes, gives identical bytes each time,
-    equal to the oracle's."""
+    """A zero-filled workspace, reused by back-to-back calls of different sizes and
+    modes, gives identical bytes each time, equal to the oracle's, and each call leaves
+    the workspace zero-filled again (its quantize launch clears the absmax slots that
+    its absmax launch filled)."""
     import torch
     import nvfp4_block_scaled_swiglu_amd as nv
     w = synth.TINY
     gate, up = w.activations()
     g_t, u_t = parity.to_device_bf16(gate, gpu), parity.to_device_bf16(up, gpu)
-    ws = torch.full((nv.nvfp4_quantize_workspace_bytes(),), 0xA5, dtype=torch.uint8, device=gpu)
-    outs = [nv.nvfp4_quantize_swiglu(g_t, u_t, workspace=ws) for _ in range(2)]
+    ws = torch.zeros((nv.nvfp4_quantize_workspace_bytes(),), dtype=torch.uint8, device=gpu)
+
+    def zero_after(out):
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, "workspace not left zero-filled"
+        return out
+
+    outs = [zero_after(nv.nvfp4_quantize_swiglu(g_t, u_t, workspace=ws)) for _ in range(2)]
     x_t = parity.to_device_bf16(w.weight(), gpu)
-    wq = nv.nvfp4_quantize(x_t, workspace=ws)
-    small = nv.nvfp4_quantize_swiglu(g_t[:20], u_t[:20], workspace=ws)
-    outs.append(nv.nvfp4_quantize_swiglu(g_t, u_t, workspace=ws))
-    torch.cuda.synchronize()
+    wq = zero_after(nv.nvfp4_quantize(x_t, workspace=ws))
+    small = zero_after(nv.nvfp4_quantize_swiglu(g_t[:20], u_t[:20], workspace=ws))
+    outs.append(zero_after(nv.nvfp4_quantize_swiglu(g_t, u_t, workspace=ws)))
     for o in outs[1:]:
         assert torch.equal(o.qdata, outs[0].qdata) and torch.equal(o.scales, outs[0].scales)
         assert torch.equal(o.global_scale, outs[0].global_scale)

@@ -64,6 +64,7 @@ constexpr int kSteps = 2;                   // steps of 2 rows per unit
 constexpr int kLanesPerRow = kUnitCols / 16;
 constexpr int kAbsWaves = 4;                // absmax workgroup: 4 waves, one unit each
 constexpr int kQuantWaves = 12;             // quantize workgroup: 12 waves, persistent
+constexpr int kGroupUnits = 4;              // units per queue take (one 64-byte scale line's rows)
 static_assert(kLanesPerRow * 2 == 64 && kSteps * 2 == kUnitRows, "unit geometry");
 
 struct ProducerArgs {
@@ -279,36 +280,42 @@ __device__ __forceinline__ void load_unit(const ProducerArgs& a, const LaneGeom&
   const int rt = uu / a.items_k, kt = uu - rt * a.items_k;
   const int64_t row0 = (int64_t)rt * kUnitRows;
   const int64_t col0 = (int64_t)kt * kUnitCols;
-  const char* bx = (const char*)a.x + (row0 * a.ldx + col0) * 2;
-  const char* bu = SWIGLU ? (const char*)a.u + (row0 * a.ldu + col0) * 2 : nullptr;
+  // Each load instruction reads one row's whole 1 KB segment of the unit, non-temporal:
+  // lane l takes bytes [32 (l mod 32) + 16 (l / 32), +16), the first or second half of
+  // the 16-element block l mod 32. One permlane32 swap per dword between the two rows
+  // of a step then hands every lane its whole block (lanes 0-31: the step's first row,
+  // 32-63: its second), the layout the rest of the unit works in.
+  const int64_t col = col0 + L.blk * 16 + L.r4 * 8;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  u32x4_t xr[kUnitRows], ur[kUnitRows];
   if (row0 + kUnitRows <= a.m && col0 + kUnitCols <= a.k) {  // the whole unit is inside (wave-uniform)
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const u32x4_t* px = (const u32x4_t*)(bx + s * L.step_x + L.lx);
-      gv[s][0] = px[0];
-      gv[s][1] = px[1];
-      if (SWIGLU) {
-        const u32x4_t* pu = (const u32x4_t*)(bu + s * L.step_u + L.lu);
-        uv[s][0] = pu[0];
-        uv[s][1] = pu[1];
-      }
+    for (int r = 0; r < kUnitRows; ++r) {
+      xr[r] = __builtin_nontemporal_load((const u32x4_t*)(a.x + (row0 + r) * a.ldx + col));
+      if (SWIGLU) ur[r] = __builtin_nontemporal_load((const u32x4_t*)(a.u + (row0 + r) * a.ldu + col));
     }
   } else {
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-    const bool cok = col0 + L.blk * 16 < a.k;
+    const bool cok = col < a.k;  // k % 64 == 0: both halves of a block are in or out together
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const bool ok = cok && row0 + 2 * s + L.r4 < a.m;
-      const u32x4_t* px = (const u32x4_t*)(bx + s * L.step_x + L.lx);
-      gv[s][0] = ok ? px[0] : z;
-      gv[s][1] = ok ? px[1] : z;
-      if (SWIGLU) {
-        const u32x4_t* pu = (const u32x4_t*)(bu + s * L.step_u + L.lu);
-        uv[s][0] = ok ? pu[0] : z;
-        uv[s][1] = ok ? pu[1] : z;
-      }
+    for (int r = 0; r < kUnitRows; ++r) {
+      const bool ok = cok && row0 + r < a.m;
+      xr[r] = ok ? __builtin_nontemporal_load((const u32x4_t*)(a.x + (row0 + r) * a.ldx + col)) : z;
+      if (SWIGLU) ur[r] = ok ? __builtin_nontemporal_load((const u32x4_t*)(a.u + (row0 + r) * a.ldu + col)) : z;
     }
   }
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const auto px = __builtin_amdgcn_permlane32_swap(xr[2 * s][d], xr[2 * s + 1][d], false, false);
+      gv[s][0][d] = px[0];
+      gv[s][1][d] = px[1];
+      if (SWIGLU) {
+        const auto pu = __builtin_amdgcn_permlane32_swap(ur[2 * s][d], ur[2 * s + 1][d], false, false);
+        uv[s][0][d] = pu[0];
+        uv[s][1][d] = pu[1];
+      }
+    }
 }
 
 // The modulation scale (mv[0]) and shift (mv[1]) of the lane's 16 columns of unit uu.
@@ -675,8 +682,11 @@ __device__ __forceinline__ void quantize_block(const ProducerArgs& a, const Quan
     if (clo1 ^ chi1) clo1 = fix_half(clo1, chi1, yb[4], yb[5], yb[6], yb[7], vS4, g, fma_ok, S);
   }
   if (store_q && cok) {
+    // non-temporal: QDATA is written once and read by the next stage (measured: about 2 %
+    // faster than plain stores); the scale bytes stay plain stores, which L2 merges into
+    // whole lines (non-temporal byte stores are far slower)
     const u32x2_t v = {clo0, clo1};
-    *(u32x2_t*)qdst = v;
+    __builtin_nontemporal_store(v, (u32x2_t*)qdst);
   }
   if (cok) *sdst = (uint8_t)S;
 }
@@ -705,6 +715,17 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
   const int j = (blockIdx.x * kQuantWaves + wave) % kProdQueueCounters;
   uint32_t* ctr = a.queue + j * kSlotStride;
 
+  // A take hands out a group of kGroupUnits units: rows r, r + 32, r + 64 and r + 96
+  // (r a multiple of 4) of one 128-row tile, 4 rows each, in one column segment. The 64-byte
+  // lines of the scale tiles hold exactly these 16 rows, so each line is written whole by
+  // one wave, and L2 merges its byte stores before the line goes to memory.
+  const int ngroups = a.nunits / kGroupUnits;
+  auto group_unit = [&](int grp, int jj) {  // unit index of member jj of group grp (reverse order)
+    const int gg = ngroups - 1 - grp;
+    const int kt = gg % a.items_k, rest = gg / a.items_k;
+    const int rt = (rest / 8) * 32 + (rest % 8) + 8 * jj;
+    return rt * a.items_k + kt;
+  };
   uint32_t t0 = 0, t1 = 0;
   if (lane == 0) {
     t0 = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -714,9 +735,9 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
   int un = (int)__builtin_amdgcn_readfirstlane(t1) * kProdQueueCounters + j;
   // the first unit's loads are in flight while the table is staged and amax reduced
   u32x4_t gv[kSteps][2], uv[kSteps][2], mv[2][2];
-  if (u < a.nunits) {
-    load_unit<MODE>(a, L, a.nunits - 1 - u, gv, uv);
-    if (MOD) load_modulation(a, L, a.nunits - 1 - u, mv);
+  if (u < ngroups) {
+    load_unit<MODE>(a, L, group_unit(u, 0), gv, uv);
+    if (MOD) load_modulation(a, L, group_unit(u, 0), mv);
   }
   uint32_t slot_max = 0;
   if (!GIVEN && tid < kAmaxSlots) slot_max = a.slots[tid * kSlotStride];
@@ -741,32 +762,45 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
   if (blockIdx.x == 0 && tid == 0) *a.gout = c.g;
 
   const int64_t qrow = a.k / 2;
-  while (u < a.nunits) {
+  auto process = [&](int uu, const u32x4_t (&xv)[kSteps][2], const u32x4_t (&yv)[kSteps][2],
+                     const u32x4_t (&zv)[2][2]) {
+    const int rt = uu / a.items_k, kt = uu - rt * a.items_k;
+    const int64_t row0 = (int64_t)rt * kUnitRows;
+    const bool cok = (int64_t)kt * kUnitCols + L.blk * 16 < a.k;
+    const bool store_q = row0 < a.m_pad;  // units are 4-row aligned, m_pad 16-row aligned
+    uint8_t* bq = a.qdata + row0 * qrow + kt * (kUnitCols / 2) + L.r4 * qrow + L.blk * 8;
+    // scale byte of (row, block column bc) in its 128 x 4 tile; a unit stays inside one
+    // 32-row group of one tile
+    const int64_t bc = (int64_t)kt * kLanesPerRow + L.blk;
+    uint8_t* bs = a.scales + ((row0 >> 7) * (a.cpad / 4) + (bc >> 2)) * 512 + (row0 & 31) * 16 +
+                  ((row0 >> 5) & 3) * 4 + L.r4 * 16 + (bc & 3);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      quantize_block<MODE>(a, c, xv[s], yv[s], zv, tab, row0 + 2 * s + L.r4, store_q, cok, bq + s * 2 * qrow,
+                           bs + s * 32);
+  };
+  // Double-buffered: the next unit's loads are issued before the current unit is
+  // quantized, so they are in flight during its arithmetic and stores.
+  u32x4_t gw[kSteps][2], uw[kSteps][2], mw[2][2];
+  while (u < ngroups) {
     uint32_t tr = 0;
     if (lane == 0) tr = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    {
-      const int uu = a.nunits - 1 - u;
-      const int rt = uu / a.items_k, kt = uu - rt * a.items_k;
-      const int64_t row0 = (int64_t)rt * kUnitRows;
-      const bool cok = (int64_t)kt * kUnitCols + L.blk * 16 < a.k;
-      const bool store_q = row0 < a.m_pad;  // units are 4-row aligned, m_pad 16-row aligned
-      uint8_t* bq = a.qdata + row0 * qrow + kt * (kUnitCols / 2) + L.r4 * qrow + L.blk * 8;
-      // scale byte of (row, block column bc) in its 128 x 4 tile; a unit stays inside one
-      // 32-row group of one tile
-      const int64_t bc = (int64_t)kt * kLanesPerRow + L.blk;
-      uint8_t* bs = a.scales + ((row0 >> 7) * (a.cpad / 4) + (bc >> 2)) * 512 + (row0 & 31) * 16 +
-                    ((row0 >> 5) & 3) * 4 + L.r4 * 16 + (bc & 3);
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s)
-        quantize_block<MODE>(a, c, gv[s], uv[s], mv, tab, row0 + 2 * s + L.r4, store_q, cok, bq + s * 2 * qrow,
-                             bs + s * 32);
+    for (int jj = 0; jj < kGroupUnits; jj += 2) {
+      const int n1 = group_unit(u, jj + 1);
+      load_unit<MODE>(a, L, n1, gw, uw);
+      if (MOD) load_modulation(a, L, n1, mw);
+      process(group_unit(u, jj), gv, uv, mv);
+      const bool more = jj + 2 < kGroupUnits || un < ngroups;
+      if (more) {
+        const int n2 = jj + 2 < kGroupUnits ? group_unit(u, jj + 2) : group_unit(un, 0);
+        load_unit<MODE>(a, L, n2, gv, uv);
+        if (MOD) load_modulation(a, L, n2, mv);
+      }
+      process(n1, gw, uw, mw);
     }
     u = un;
     un = (int)__builtin_amdgcn_readfirstlane(tr) * kProdQueueCounters + j;
-    if (u < a.nunits) {
-      load_unit<MODE>(a, L, a.nunits - 1 - u, gv, uv);
-      if (MOD) load_modulation(a, L, a.nunits - 1 - u, mv);
-    }
   }
   // Every take of this wave has returned (its last value was read above). The last wave
   // to count itself clears the counter set and, after a two-pass call, the slots: every

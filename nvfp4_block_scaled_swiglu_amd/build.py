@@ -20,10 +20,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-I", os.path.join(HERE, "..", "include")]
 
+# Per-source additions. The producer's work-queue takes are single-lane atomics whose
+# result is needed one group later; LLVM's atomic optimizer rewrites them into a form
+# that reads the result (and so waits for every load in flight) right after the atomic.
+EXTRA_FLAGS = {"producer.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

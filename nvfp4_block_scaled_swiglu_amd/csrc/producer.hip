@@ -21,8 +21,8 @@
 // each input row per step).
 //
 // Two ordinary launches on the caller's stream:
-//  - The absmax launch is a one-shot grid of small workgroups (4 waves, one unit
-//    each), dispatched in address order. It needs no table: for SwiGLU, every |y| is
+//  - The absmax launch is a one-shot grid of 8-wave workgroups (one unit per wave),
+//    dispatched in address order. It needs no table: for SwiGLU, every |y| is
 //    bounded by max(gate, 0.28125) * |up| (exact in fp32), and that bound is |y|
 //    itself up to the bf16 rounding when gate >= 8 (silu_bf16 is the identity
 //    there); only elements whose bound reaches the wave's exact maximum are looked up
@@ -62,7 +62,7 @@ constexpr int kUnitRows = 4;
 constexpr int kUnitCols = 512;
 constexpr int kSteps = 2;                   // steps of 2 rows per unit
 constexpr int kLanesPerRow = kUnitCols / 16;
-constexpr int kAbsWaves = 4;                // absmax workgroup: 4 waves, one unit each
+constexpr int kAbsWaves = 8;                // absmax workgroup: 8 waves, one unit each
 constexpr int kQuantWaves = 12;             // quantize workgroup: 12 waves, persistent
 constexpr int kGroupUnits = 4;              // units per queue take (one 64-byte scale line's rows)
 static_assert(kLanesPerRow * 2 == 64 && kSteps * 2 == kUnitRows, "unit geometry");
@@ -282,38 +282,58 @@ __device__ __forceinline__ void load_unit(const ProducerArgs& a, const LaneGeom&
   const int64_t col0 = (int64_t)kt * kUnitCols;
   // Each load instruction reads one row's whole 1 KB segment of the unit, non-temporal:
   // lane l takes bytes [32 (l mod 32) + 16 (l / 32), +16), the first or second half of
-  // the 16-element block l mod 32. One permlane32 swap per dword between the two rows
-  // of a step then hands every lane its whole block (lanes 0-31: the step's first row,
-  // 32-63: its second), the layout the rest of the unit works in.
-  const int64_t col = col0 + L.blk * 16 + L.r4 * 8;
-  const u32x4_t z = {0u, 0u, 0u, 0u};
-  u32x4_t xr[kUnitRows], ur[kUnitRows];
-  if (row0 + kUnitRows <= a.m && col0 + kUnitCols <= a.k) {  // the whole unit is inside (wave-uniform)
+  // the 16-element block l mod 32. Row r lands in gv[r / 2][r % 2] as loaded;
+  // arrange_unit later hands every lane its whole blocks.
+  // The eight loads have no condition: rows past the tensor read its last row and
+  // columns past it its last 8 columns (the caller zeroes such rows and stores nothing
+  // for such columns). With no branch around them, the compiler knows how many loads
+  // are in flight behind each one and waits for no more than it needs.
+  int64_t col = col0 + L.blk * 16 + L.r4 * 8;
+  col = col < a.k - 8 ? col : a.k - 8;
 #pragma unroll
-    for (int r = 0; r < kUnitRows; ++r) {
-      xr[r] = __builtin_nontemporal_load((const u32x4_t*)(a.x + (row0 + r) * a.ldx + col));
-      if (SWIGLU) ur[r] = __builtin_nontemporal_load((const u32x4_t*)(a.u + (row0 + r) * a.ldu + col));
-    }
-  } else {
-    const bool cok = col < a.k;  // k % 64 == 0: both halves of a block are in or out together
-#pragma unroll
-    for (int r = 0; r < kUnitRows; ++r) {
-      const bool ok = cok && row0 + r < a.m;
-      xr[r] = ok ? __builtin_nontemporal_load((const u32x4_t*)(a.x + (row0 + r) * a.ldx + col)) : z;
-      if (SWIGLU) ur[r] = ok ? __builtin_nontemporal_load((const u32x4_t*)(a.u + (row0 + r) * a.ldu + col)) : z;
-    }
+  for (int r = 0; r < kUnitRows; ++r) {
+    const int64_t row = row0 + r < a.m ? row0 + r : a.m - 1;  // wave-uniform
+    gv[r >> 1][r & 1] = __builtin_nontemporal_load((const u32x4_t*)(a.x + row * a.ldx + col));
+    if (SWIGLU) uv[r >> 1][r & 1] = __builtin_nontemporal_load((const u32x4_t*)(a.u + row * a.ldu + col));
   }
+}
+
+// One permlane32 swap per dword between the two rows of a step turns load_unit's rows
+// into blocks: afterwards gv[s][h] holds, in lanes 0-31, the step's first row and, in
+// lanes 32-63, its second, 16 whole elements per lane (h: first or second 8). Done when
+// the unit is about to be quantized, so that the wait for its loads comes as late as
+// possible.
+template <int MODE>
+__device__ __forceinline__ void arrange_unit(u32x4_t (&gv)[kSteps][2], u32x4_t (&uv)[kSteps][2]) {
 #pragma unroll
   for (int s = 0; s < kSteps; ++s)
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const auto px = __builtin_amdgcn_permlane32_swap(xr[2 * s][d], xr[2 * s + 1][d], false, false);
+      const auto px = __builtin_amdgcn_permlane32_swap(gv[s][0][d], gv[s][1][d], false, false);
       gv[s][0][d] = px[0];
       gv[s][1][d] = px[1];
-      if (SWIGLU) {
-        const auto pu = __builtin_amdgcn_permlane32_swap(ur[2 * s][d], ur[2 * s + 1][d], false, false);
+      if (MODE == kSwiglu) {
+        const auto pu = __builtin_amdgcn_permlane32_swap(uv[s][0][d], uv[s][1][d], false, false);
         uv[s][0][d] = pu[0];
         uv[s][1][d] = pu[1];
+      }
+    }
+}
+
+// Zero the arranged blocks of the rows at or past m (row0: the unit's first row; lanes
+// 32-63 hold the second row of each step).
+template <int MODE>
+__device__ __forceinline__ void zero_tail_rows(const ProducerArgs& a, int64_t row0, int lane,
+                                               u32x4_t (&gv)[kSteps][2], u32x4_t (&uv)[kSteps][2]) {
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+    if (row0 + 2 * s + (lane >> 5) >= a.m) {
+      gv[s][0] = z;
+      gv[s][1] = z;
+      if (MODE == kSwiglu) {
+        uv[s][0] = z;
+        uv[s][1] = z;
       }
     }
 }
@@ -322,15 +342,14 @@ __device__ __forceinline__ void load_unit(const ProducerArgs& a, const LaneGeom&
 __device__ __forceinline__ void load_modulation(const ProducerArgs& a, const LaneGeom& L, int uu,
                                                 u32x4_t (&mv)[2][2]) {
   const int kt = uu % a.items_k;
-  const int64_t col = (int64_t)kt * kUnitCols + L.blk * 16;
-  const u32x4_t z = {0u, 0u, 0u, 0u};
-  const bool cok = col < a.k;
+  int64_t col = (int64_t)kt * kUnitCols + L.blk * 16;
+  col = col < a.k - 16 ? col : a.k - 16;  // blocks past the columns are never stored
   const u32x4_t* ps = (const u32x4_t*)(a.mod_scale + col);
   const u32x4_t* pb = (const u32x4_t*)(a.mod_shift + col);
-  mv[0][0] = cok ? ps[0] : z;
-  mv[0][1] = cok ? ps[1] : z;
-  mv[1][0] = cok ? pb[0] : z;
-  mv[1][1] = cok ? pb[1] : z;
+  mv[0][0] = ps[0];
+  mv[0][1] = ps[1];
+  mv[1][0] = pb[0];
+  mv[1][1] = pb[1];
 }
 
 // ---- pass 1: the tensor absmax -----------------------------------------------------------
@@ -475,7 +494,7 @@ __device__ __forceinline__ void load_unit_rows(const ProducerArgs& a, int lane, 
   }
 }
 
-// One-shot grid: workgroup b covers units 4b .. 4b + 3 (more only when the grid is
+// One-shot grid: workgroup b covers units 8b .. 8b + 7 (more only when the grid is
 // capped), one per wave, in address order; its maximum goes to slot b % kAmaxSlots.
 template <int MODE>
 __global__ void __launch_bounds__(kAbsWaves * 64) producer_absmax_kernel(ProducerArgs a) {
@@ -617,23 +636,20 @@ __device__ __forceinline__ uint32_t fix_half(uint32_t c, uint32_t ch, uint32_t y
   return c;
 }
 
-// One step of a unit: the scale byte and the 16 codes of the lane's block of row `row`
-// (column `col`), stored at qdst / sdst. `store_q`: the row is below m_pad; `cok`: the
-// block is inside the columns.
+// The 16 values y of the lane's block of row `row` as 8 packed bf16 pairs, and the
+// largest magnitude among them (bf16 bits).
 template <int MODE>
-__device__ __forceinline__ void quantize_block(const ProducerArgs& a, const QuantCtx& c, const u32x4_t (&gv)[2],
-                                               const u32x4_t (&uv)[2], const u32x4_t (&mv)[2][2], const uint16_t* tab,
-                                               int64_t row, bool store_q, bool cok, uint8_t* qdst, uint8_t* sdst) {
+__device__ __forceinline__ void block_values(const ProducerArgs& a, const u32x4_t (&gv)[2], const u32x4_t (&uv)[2],
+                                             const u32x4_t (&mv)[2][2], const uint16_t* tab, int64_t row,
+                                             uint32_t (&yb)[8], uint32_t& mx) {
   constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
-  const float g = c.g;
-  uint32_t yb[8];
   block_y<MODE>(gv, uv, mv, tab, yb);
   if (MOD && row >= a.m) {
 #pragma unroll
     for (int w = 0; w < 8; ++w) yb[w] = 0u;  // padding rows are zero, not the shift
   }
   // block maximum of |y| (bf16 magnitudes compare as integers)
-  uint32_t mx, mn;
+  uint32_t mn;
   block_mag_range(yb, mx, mn);
   if (SWIGLU && mn <= 0x0080u) {
     // some |y| <= 2^-126 (or zero): its fp32 product may have been subnormal and
@@ -646,6 +662,14 @@ __device__ __forceinline__ void quantize_block(const ProducerArgs& a, const Quan
     for (int w = 0; w < 8; ++w) yb[w] = y.v[w];
     block_mag_range(yb, mx, mn);
   }
+}
+
+// The scale byte and the 16 codes of one block (values yb, largest magnitude mx), stored
+// at qdst / sdst. `store_q`: the row is below m_pad; `cok`: the block is inside the
+// columns.
+__device__ __forceinline__ void block_codes(const QuantCtx& c, const uint32_t (&yb)[8], uint32_t mx, bool store_q,
+                                            bool cok, uint8_t* qdst, uint8_t* sdst) {
+  const float g = c.g;
   const uint32_t S = (mx == 0) ? 0u : block_scale_byte(bf16_bits_to_float(mx), c.bscale, c.inv_f, c.g6);
 
   // E2M1 codes of the 16 elements
@@ -762,10 +786,11 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
   if (blockIdx.x == 0 && tid == 0) *a.gout = c.g;
 
   const int64_t qrow = a.k / 2;
-  auto process = [&](int uu, const u32x4_t (&xv)[kSteps][2], const u32x4_t (&yv)[kSteps][2],
-                     const u32x4_t (&zv)[2][2]) {
+  auto process = [&](int uu, u32x4_t (&xv)[kSteps][2], u32x4_t (&yv)[kSteps][2], const u32x4_t (&zv)[2][2]) {
+    arrange_unit<MODE>(xv, yv);
     const int rt = uu / a.items_k, kt = uu - rt * a.items_k;
     const int64_t row0 = (int64_t)rt * kUnitRows;
+    if (row0 + kUnitRows > a.m) zero_tail_rows<MODE>(a, row0, lane, xv, yv);
     const bool cok = (int64_t)kt * kUnitCols + L.blk * 16 < a.k;
     const bool store_q = row0 < a.m_pad;  // units are 4-row aligned, m_pad 16-row aligned
     uint8_t* bq = a.qdata + row0 * qrow + kt * (kUnitCols / 2) + L.r4 * qrow + L.blk * 8;
@@ -775,9 +800,11 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
     uint8_t* bs = a.scales + ((row0 >> 7) * (a.cpad / 4) + (bc >> 2)) * 512 + (row0 & 31) * 16 +
                   ((row0 >> 5) & 3) * 4 + L.r4 * 16 + (bc & 3);
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-      quantize_block<MODE>(a, c, xv[s], yv[s], zv, tab, row0 + 2 * s + L.r4, store_q, cok, bq + s * 2 * qrow,
-                           bs + s * 32);
+    for (int s = 0; s < kSteps; ++s) {
+      uint32_t yb[8], mx;
+      block_values<MODE>(a, xv[s], yv[s], zv, tab, row0 + 2 * s + L.r4, yb, mx);
+      block_codes(c, yb, mx, store_q, cok, bq + s * 2 * qrow, bs + s * 32);
+    }
   };
   // Double-buffered: the next unit's loads are issued before the current unit is
   // quantized, so they are in flight during its arithmetic and stores.
@@ -790,13 +817,17 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
       const int n1 = group_unit(u, jj + 1);
       load_unit<MODE>(a, L, n1, gw, uw);
       if (MOD) load_modulation(a, L, n1, mw);
+      // nothing of the unit below may move above the next unit's loads (the scheduler
+      // would otherwise start its lane swaps there and wait for those loads too)
+      __builtin_amdgcn_sched_barrier(0);
       process(group_unit(u, jj), gv, uv, mv);
+      // the next unit: the group's next member, or the next group's first (after the
+      // last group, an inactive load that is never used)
       const bool more = jj + 2 < kGroupUnits || un < ngroups;
-      if (more) {
-        const int n2 = jj + 2 < kGroupUnits ? group_unit(u, jj + 2) : group_unit(un, 0);
-        load_unit<MODE>(a, L, n2, gv, uv);
-        if (MOD) load_modulation(a, L, n2, mv);
-      }
+      const int n2 = jj + 2 < kGroupUnits ? group_unit(u, jj + 2) : (more ? group_unit(un, 0) : 0);
+      load_unit<MODE>(a, L, n2, gv, uv);
+      if (MOD) load_modulation(a, L, n2, mv);
+      __builtin_amdgcn_sched_barrier(0);
       process(n1, gw, uw, mw);
     }
     u = un;

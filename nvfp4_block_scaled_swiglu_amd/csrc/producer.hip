@@ -30,13 +30,14 @@
 //    workspace's 64 slots by atomic max.
 //  - The kernel boundary is the grid-wide synchronisation the global scale needs.
 //  - The quantize launch runs one persistent 12-wave workgroup per CU with the bf16
-//    silu table in LDS. Its waves take units from 32 interleaved run-time counters
-//    (each wave its own counter, takes issued two units ahead), in reverse address
-//    order, so that the rows the absmax launch read last, still in the memory-side
-//    cache, come first and the whole grid moves through memory together. It reduces
+//    silu table in LDS. Its waves work through groups of 4 units: two fixed ones
+//    each, then groups taken from 32 interleaved run-time counters (takes issued two
+//    groups ahead), in reverse address order, so that the rows the absmax launch read
+//    last, still in the memory-side cache, come first and the whole grid moves
+//    through memory together. It reduces
 //    the slots to amax, derives g, recomputes y, and stores QDATA rows (32 lanes
 //    store one 256-byte row segment) and each scale byte at its place in its tile.
-//    Its last wave clears the counters and the slots for the next call.
+//    Its last workgroup clears the counters and the slots for the next call.
 // With GIVEN (amax from the caller) only the quantize launch runs: every input byte
 // is read once.
 //
@@ -715,12 +716,14 @@ __device__ __forceinline__ void block_codes(const QuantCtx& c, const uint32_t (&
   if (cok) *sdst = (uint8_t)S;
 }
 
-// Persistent grid of kQuantWaves-wave workgroups. Wave w (global index) takes units
-// from counter w % kProdQueueCounters of the launch's set: the t-th take of counter j
-// is unit t * kProdQueueCounters + j, walked from the end of the tensor (uu = nunits -
-// 1 - unit). Takes are issued two units ahead of their use. GIVEN: the tensor amax
-// comes from the caller (a device float); otherwise it is the maximum of the
-// workspace's slots, which the last wave clears together with the counters.
+// Persistent grid of G kQuantWaves-wave workgroups, W waves in all. Groups of units are
+// numbered from the end of the tensor. Wave v of workgroup b is wave w = v G + b (so
+// that consecutive groups go to different CUs); it starts with groups w and W + w, then
+// takes groups from counter j = w % kProdQueueCounters of the launch's set, the t-th
+// take of counter j being group 2W + t * kProdQueueCounters + j. Takes are issued two
+// groups ahead of their use. GIVEN: the tensor amax comes from the caller (a device
+// float); otherwise it is the maximum of the workspace's slots, which the last
+// workgroup clears together with the counters.
 template <int MODE, bool GIVEN>
 __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs a) {
   constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
@@ -736,7 +739,9 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so unit arithmetic stays scalar
   const int lane = tid & 63;
   const LaneGeom L = lane_geom(a, lane);
-  const int j = (blockIdx.x * kQuantWaves + wave) % kProdQueueCounters;
+  const int nwaves = gridDim.x * kQuantWaves;
+  const int wg = wave * gridDim.x + blockIdx.x;  // global wave index, CU-minor
+  const int j = wg % kProdQueueCounters;
   uint32_t* ctr = a.queue + j * kSlotStride;
 
   // A take hands out a group of kGroupUnits units: rows r, r + 32, r + 64 and r + 96
@@ -750,13 +755,9 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
     const int rt = (rest / 8) * 32 + (rest % 8) + 8 * jj;
     return rt * a.items_k + kt;
   };
-  uint32_t t0 = 0, t1 = 0;
-  if (lane == 0) {
-    t0 = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    t1 = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  int u = (int)__builtin_amdgcn_readfirstlane(t0) * kProdQueueCounters + j;
-  int un = (int)__builtin_amdgcn_readfirstlane(t1) * kProdQueueCounters + j;
+  // the first two groups need no take: every wave starting with a take put 192 takes
+  // on each counter before any load could be issued
+  int u = wg, un = nwaves + wg;
   // the first unit's loads are in flight while the table is staged and amax reduced
   u32x4_t gv[kSteps][2], uv[kSteps][2], mv[2][2];
   if (u < ngroups) {
@@ -831,23 +832,30 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
       process(n1, gw, uw, mw);
     }
     u = un;
-    un = (int)__builtin_amdgcn_readfirstlane(tr) * kProdQueueCounters + j;
+    un = 2 * nwaves + (int)__builtin_amdgcn_readfirstlane(tr) * kProdQueueCounters + j;
   }
-  // Every take of this wave has returned (its last value was read above). The last wave
-  // to count itself clears the counter set and, after a two-pass call, the slots: every
-  // wave read the slots before its loop.
-  uint32_t done = 0;
-  if (lane == 0)
-    done = __hip_atomic_fetch_add(a.queue + kProdQueueCounters * kSlotStride, 1u, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-  done = __builtin_amdgcn_readfirstlane(done);
-  if (done == gridDim.x * kQuantWaves - 1) {
-    if (lane < kProdQueueCounters)
-      __hip_atomic_store(a.queue + lane * kSlotStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!GIVEN && lane < kAmaxSlots)
-      __hip_atomic_store(a.slots + lane * kSlotStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Every take of this wave has returned (its last value was read above). The waves of
+  // the workgroup meet, and one lane counts the workgroup as done: one atomic per
+  // workgroup, since one per wave (3,072 on one address, about 11 ns each) took some
+  // 35 us at the end of every call. The last workgroup to count itself clears the
+  // counter set and, after a two-pass call, the slots: every wave read the slots before
+  // its loop.
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t done = 0;
     if (lane == 0)
-      __hip_atomic_store(a.queue + kProdQueueCounters * kSlotStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      done = __hip_atomic_fetch_add(a.queue + kProdQueueCounters * kSlotStride, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    done = __builtin_amdgcn_readfirstlane(done);
+    if (done == gridDim.x - 1) {
+      if (lane < kProdQueueCounters)
+        __hip_atomic_store(a.queue + lane * kSlotStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!GIVEN && lane < kAmaxSlots)
+        __hip_atomic_store(a.slots + lane * kSlotStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0)
+        __hip_atomic_store(a.queue + kProdQueueCounters * kSlotStride, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 

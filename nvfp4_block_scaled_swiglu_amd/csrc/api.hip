@@ -198,7 +198,8 @@ int check_quant_args(const void* x, int64_t ldx, const void* u, int64_t ldu, boo
   if (ldx < k || (swiglu && ldu < k))
     return fail(NVFP4_ERR_INVALID_ARG, "row stride below k (ld=%lld, %lld, k=%lld)", (long long)ldx,
                 (long long)ldu, (long long)k);
-  // the kernels address a 128-row item with 32-bit offsets from its base
+  // a documented limit that keeps every per-row count (512-column segments, scale
+  // columns) far inside 32-bit integers
   if (k > ((int64_t)1 << 23) || ldx > ((int64_t)1 << 23) || (swiglu && ldu > ((int64_t)1 << 23)))
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k and row strides above 2^23 elements are not supported");
   if (ldx % 8 != 0 || (swiglu && ldu % 8 != 0))

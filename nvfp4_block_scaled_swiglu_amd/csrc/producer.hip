@@ -255,22 +255,16 @@ __device__ __forceinline__ void block_mag_range(const uint32_t (&yb)[8], uint32_
 
 // ---- unit loads ------------------------------------------------------------------------
 //
-// The lane's 16 bf16 values of each step of unit uu (zero outside the logical rows and
-// columns). Addresses are a per-unit base plus a per-lane offset.
+// Where a lane works in the quantize launch: after the lane swaps, lane l holds the
+// 16-element block l mod 32 of row l / 32 of each step.
 struct LaneGeom {
-  int r4, blk;          // row within a step, 16-column block of the unit
-  uint32_t lx, lu;      // byte offsets of the lane's first element in x / u
-  int64_t step_x, step_u;  // bytes between the steps (2 rows)
+  int r4, blk;  // row within a step (0, 1), 16-column block of the unit (0 .. 31)
 };
 
-__device__ __forceinline__ LaneGeom lane_geom(const ProducerArgs& a, int lane) {
+__device__ __forceinline__ LaneGeom lane_geom(int lane) {
   LaneGeom L;
   L.r4 = lane / kLanesPerRow;
   L.blk = lane % kLanesPerRow;
-  L.lx = (uint32_t)((L.r4 * a.ldx + L.blk * 16) * 2);
-  L.lu = (uint32_t)((L.r4 * a.ldu + L.blk * 16) * 2);
-  L.step_x = 2 * a.ldx * 2;
-  L.step_u = 2 * a.ldu * 2;
   return L;
 }
 
@@ -738,7 +732,7 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so unit arithmetic stays scalar
   const int lane = tid & 63;
-  const LaneGeom L = lane_geom(a, lane);
+  const LaneGeom L = lane_geom(lane);
   const int nwaves = gridDim.x * kQuantWaves;
   const int wg = wave * gridDim.x + blockIdx.x;  // global wave index, CU-minor
   const int j = wg % kProdQueueCounters;

@@ -180,6 +180,40 @@ def test_workspace_reuse_and_determinism(gpu):
     assert float(small.global_scale.item()) == rg
 
 
+def test_many_calls_two_streams(gpu):
+    """70 calls queued without waiting, more than the 64 counter sets the quantize
+    launches rotate through, alternating two streams (each with its own workspace) and
+    two shapes whose grids take few and many groups. Every result equals the oracle's,
+    and both workspaces end zero-filled."""
+    import torch
+    import nvfp4_block_scaled_swiglu_amd as nv
+    w = synth.MID
+    gate, up = w.activations()  # 4,096 x 14,336: 7,168 groups, past the 6,144 that need no take
+    small_g, small_u = gate[:40, :1024], up[:40, :1024]  # 20 groups
+    refs = [oracle.quantize(np.ascontiguousarray(gate), np.ascontiguousarray(up)),
+            oracle.quantize(np.ascontiguousarray(small_g), np.ascontiguousarray(small_u))]
+    ins = [(parity.to_device_bf16(gate, gpu), parity.to_device_bf16(up, gpu)),
+           (parity.to_device_bf16(small_g, gpu), parity.to_device_bf16(small_u, gpu))]
+    streams = [torch.cuda.Stream(device=gpu), torch.cuda.Stream(device=gpu)]
+    wss = [torch.zeros((nv.nvfp4_quantize_workspace_bytes(),), dtype=torch.uint8, device=gpu) for _ in streams]
+    torch.cuda.synchronize(gpu)
+    outs = []
+    for i in range(70):
+        sel = (i // 2) % 2  # shape: large, large, small, small, ...
+        s_i = i % 2         # stream
+        with torch.cuda.stream(streams[s_i]):
+            g_t, u_t = ins[sel]
+            outs.append((sel, nv.nvfp4_quantize_swiglu(g_t, u_t, workspace=wss[s_i], stream=streams[s_i])))
+    torch.cuda.synchronize(gpu)
+    _say(f"[producer] 70 queued calls on two streams done")
+    for ws in wss:
+        assert int(ws.count_nonzero()) == 0, "workspace not left zero-filled"
+    for i, (sel, o) in enumerate(outs):
+        rq, rs, rg = refs[sel]
+        assert (o.qdata.cpu().numpy() == rq).all() and (o.scales.cpu().numpy() == rs).all(), f"call {i}"
+        assert float(o.global_scale.item()) == rg, f"call {i}"
+
+
 def test_non_strict_failure_leaves_buffers(gpu):
     """A call that fails validation, made non-strict, returns None, counts a fallback
     and leaves the produced NVFP4 bytes and the output buffer as they were."""

@@ -22,11 +22,11 @@
 //
 // Two ordinary launches on the caller's stream:
 //  - The absmax launch is a one-shot grid of 8-wave workgroups (one unit per wave),
-//    dispatched in address order. It needs no table: for SwiGLU, every |y| is
-//    bounded by max(gate, 0.28125) * |up| (exact in fp32), and that bound is |y|
-//    itself up to the bf16 rounding when gate >= 8 (silu_bf16 is the identity
-//    there); only elements whose bound reaches the wave's exact maximum are looked up
-//    in the device silu table. Each workgroup folds its maximum into one of the
+//    dispatched in address order. It keeps no table in LDS: for SwiGLU, every |y| is
+//    bounded by max(gate, 0.28125) * |up|, and silu_bf16 is the identity for
+//    gate >= 8, so a log-domain screen on the bits leaves only the elements whose
+//    bound can reach the wave's exact maximum to be looked up in the device silu
+//    table in global memory. Each workgroup folds its maximum into one of the
 //    workspace's 64 slots by atomic max.
 //  - The kernel boundary is the grid-wide synchronisation the global scale needs.
 //  - The quantize launch runs one persistent 12-wave workgroup per CU with the bf16
@@ -34,10 +34,10 @@
 //    each, then groups taken from 32 interleaved run-time counters (takes issued two
 //    groups ahead), in reverse address order, so that the rows the absmax launch read
 //    last, still in the memory-side cache, come first and the whole grid moves
-//    through memory together. It reduces
-//    the slots to amax, derives g, recomputes y, and stores QDATA rows (32 lanes
-//    store one 256-byte row segment) and each scale byte at its place in its tile.
-//    Its last workgroup clears the counters and the slots for the next call.
+//    through memory together. It reduces the slots to amax, derives g, recomputes y,
+//    and stores QDATA rows (32 lanes store one 256-byte row segment) and each scale
+//    byte at its place in its tile. Its last workgroup clears the counters and the
+//    slots for the next call.
 // With GIVEN (amax from the caller) only the quantize launch runs: every input byte
 // is read once.
 //

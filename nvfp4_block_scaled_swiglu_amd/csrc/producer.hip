@@ -30,9 +30,9 @@
 //    workspace's 64 slots by atomic max.
 //  - The kernel boundary is the grid-wide synchronisation the global scale needs.
 //  - The quantize launch runs one persistent 12-wave workgroup per CU with the bf16
-//    silu table in LDS. Its waves work through groups of 4 units: two fixed ones
-//    each, then groups taken from 32 interleaved run-time counters (takes issued two
-//    groups ahead), in reverse address order, so that the rows the absmax launch read
+//    silu table in LDS. Its waves work through groups of 4 units: a fixed one each,
+//    then groups taken from 32 interleaved run-time counters (takes issued one group
+//    ahead), in reverse address order, so that the rows the absmax launch read
 //    last, still in the memory-side cache, come first and the whole grid moves
 //    through memory together. It reduces the slots to amax, derives g, recomputes y,
 //    and stores QDATA rows (32 lanes store one 256-byte row segment) and each scale
@@ -712,10 +712,10 @@ __device__ __forceinline__ void block_codes(const QuantCtx& c, const uint32_t (&
 
 // Persistent grid of G kQuantWaves-wave workgroups, W waves in all. Groups of units are
 // numbered from the end of the tensor. Wave v of workgroup b is wave w = v G + b (so
-// that consecutive groups go to different CUs); it starts with groups w and W + w, then
-// takes groups from counter j = w % kProdQueueCounters of the launch's set, the t-th
-// take of counter j being group 2W + t * kProdQueueCounters + j. Takes are issued two
-// groups ahead of their use. GIVEN: the tensor amax comes from the caller (a device
+// that consecutive groups go to different CUs); it starts with group w, then takes
+// groups from counter j = (w / 8) % kProdQueueCounters of the launch's set, the t-th
+// take of counter j being group W + t * kProdQueueCounters + j. Each take is issued one
+// group ahead of its use. GIVEN: the tensor amax comes from the caller (a device
 // float); otherwise it is the maximum of the workspace's slots, which the last
 // workgroup clears together with the counters.
 template <int MODE, bool GIVEN>
@@ -735,7 +735,10 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
   const LaneGeom L = lane_geom(lane);
   const int nwaves = gridDim.x * kQuantWaves;
   const int wg = wave * gridDim.x + blockIdx.x;  // global wave index, CU-minor
-  const int j = wg % kProdQueueCounters;
+  // Counter j serves the waves of 8 consecutive workgroups, which sit on the 8 different
+  // XCDs: counters serving a single XCD ran out at that XCD's pace, and the XCDs' clocks
+  // differ.
+  const int j = (wg >> 3) % kProdQueueCounters;
   uint32_t* ctr = a.queue + j * kSlotStride;
 
   // A take hands out a group of kGroupUnits units: rows r, r + 32, r + 64 and r + 96
@@ -749,14 +752,24 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
     const int rt = (rest / 8) * 32 + (rest % 8) + 8 * jj;
     return rt * a.items_k + kt;
   };
-  // the first two groups need no take: every wave starting with a take put 192 takes
-  // on each counter before any load could be issued
-  int u = wg, un = nwaves + wg;
+  // Work is handed out as pieces: whole groups, except that the last nsplit groups (the
+  // start of the tensor, reached last) go out as halves (units 0, 1 or 2, 3 of a group),
+  // so that when the counters run out no wave has more than half a group left to do.
+  // Piece p is group p (p < nfull), else half (p - nfull) % 2 of group
+  // nfull + (p - nfull) / 2.
+  const int nsplit = ngroups < nwaves / 2 ? ngroups : nwaves / 2;
+  const int nfull = ngroups - nsplit, npieces = nfull + 2 * nsplit;
+  auto piece_group = [&](int p) { return p < nfull ? p : nfull + ((p - nfull) >> 1); };
+  auto piece_half = [&](int p) { return p < nfull ? 0 : ((p - nfull) & 1); };        // first half
+  auto piece_end = [&](int p) { return p < nfull ? 2 : ((p - nfull) & 1) + 1; };     // past its last half
+  // the first piece needs no take: every wave starting with a take put 96 takes on
+  // each counter before any load could be issued
+  int p = wg, grp = piece_group(p), h = piece_half(p), hend = piece_end(p);
   // the first unit's loads are in flight while the table is staged and amax reduced
   u32x4_t gv[kSteps][2], uv[kSteps][2], mv[2][2];
-  if (u < ngroups) {
-    load_unit<MODE>(a, L, group_unit(u, 0), gv, uv);
-    if (MOD) load_modulation(a, L, group_unit(u, 0), mv);
+  if (p < npieces) {
+    load_unit<MODE>(a, L, group_unit(grp, 2 * h), gv, uv);
+    if (MOD) load_modulation(a, L, group_unit(grp, 2 * h), mv);
   }
   uint32_t slot_max = 0;
   if (!GIVEN && tid < kAmaxSlots) slot_max = a.slots[tid * kSlotStride];
@@ -804,29 +817,41 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
   // Double-buffered: the next unit's loads are issued before the current unit is
   // quantized, so they are in flight during its arithmetic and stores.
   u32x4_t gw[kSteps][2], uw[kSteps][2], mw[2][2];
-  while (u < ngroups) {
-    uint32_t tr = 0;
-    if (lane == 0) tr = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int jj = 0; jj < kGroupUnits; jj += 2) {
-      const int n1 = group_unit(u, jj + 1);
-      load_unit<MODE>(a, L, n1, gw, uw);
-      if (MOD) load_modulation(a, L, n1, mw);
-      // nothing of the unit below may move above the next unit's loads (the scheduler
-      // would otherwise start its lane swaps there and wait for those loads too)
-      __builtin_amdgcn_sched_barrier(0);
-      process(group_unit(u, jj), gv, uv, mv);
-      // the next unit: the group's next member, or the next group's first (after the
-      // last group, an inactive load that is never used)
-      const bool more = jj + 2 < kGroupUnits || un < ngroups;
-      const int n2 = jj + 2 < kGroupUnits ? group_unit(u, jj + 2) : (more ? group_unit(un, 0) : 0);
-      load_unit<MODE>(a, L, n2, gv, uv);
-      if (MOD) load_modulation(a, L, n2, mv);
-      __builtin_amdgcn_sched_barrier(0);
-      process(n1, gw, uw, mw);
+  // One iteration per half group. The take for the next piece is issued when a piece
+  // starts and read in its last half, just after that half's first loads are issued
+  // (before any store of the half, so that waiting for it waits for nothing newer):
+  // one piece ahead.
+  uint32_t tr = 0;
+  bool fresh = true;  // the current half starts its piece
+  while (p < npieces) {
+    if (fresh && lane == 0) tr = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int n1 = group_unit(grp, 2 * h + 1);
+    load_unit<MODE>(a, L, n1, gw, uw);
+    if (MOD) load_modulation(a, L, n1, mw);
+    // the next half: the piece's next one, or the next piece's first
+    int np = p, ngrp = grp, nh = h + 1, nhend = hend;
+    fresh = nh == hend;
+    if (fresh) {
+      np = nwaves + (int)__builtin_amdgcn_readfirstlane(tr) * kProdQueueCounters + j;
+      ngrp = piece_group(np);
+      nh = piece_half(np);
+      nhend = piece_end(np);
     }
-    u = un;
-    un = 2 * nwaves + (int)__builtin_amdgcn_readfirstlane(tr) * kProdQueueCounters + j;
+    // nothing of the unit below may move above the next unit's loads (the scheduler
+    // would otherwise start its lane swaps there and wait for those loads too)
+    __builtin_amdgcn_sched_barrier(0);
+    process(group_unit(grp, 2 * h), gv, uv, mv);
+    // (after the last piece, a load of unit 0 that is never used)
+    const bool more = np < npieces;
+    const int n2 = more ? group_unit(ngrp, 2 * nh) : 0;
+    load_unit<MODE>(a, L, n2, gv, uv);
+    if (MOD) load_modulation(a, L, n2, mv);
+    __builtin_amdgcn_sched_barrier(0);
+    process(n1, gw, uw, mw);
+    p = np;
+    grp = ngrp;
+    h = nh;
+    hend = nhend;
   }
   // Every take of this wave has returned (its last value was read above). The waves of
   // the workgroup meet, and one lane counts the workgroup as done: one atomic per

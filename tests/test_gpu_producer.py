@@ -49,10 +49,13 @@ def test_tiny_config(gpu):
     check_quant(w.weight(), None, gpu, "tiny weight")
 
 
-@pytest.mark.parametrize("m,k", [(1, 64), (15, 64), (16, 128), (17, 192), (130, 320), (255, 1024), (300, 576)])
+@pytest.mark.parametrize("m,k", [(1, 64), (15, 64), (16, 128), (17, 192), (130, 320), (255, 1024), (300, 576),
+                                 (1000, 14336), (3000, 5376)])
 def test_edge_shapes(gpu, m, k):
-    """Ragged rows (padding to 16 and to 128-row scale tiles) and widths that do not
-    fill a 256-column work item."""
+    """Ragged rows (padding to 16 and to 128-row scale tiles), widths that do not fill
+    a 512-column unit, and grids on both sides of the quantize launch's split into
+    whole groups and halves (1,000 x 14,336: 1,792 groups, 256 of them whole; 3,000 x
+    5,376: 2,112 groups with a half-filled last column segment)."""
     gate = synth.normal_bf16(m, k, seed=m, tag=1, sigma=1.0)
     up = synth.normal_bf16(m, k, seed=m, tag=2, sigma=1.0)
     check_quant(gate, up, gpu, f"swiglu m={m} k={k}")

@@ -709,10 +709,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
     const int64_t n_half = a.n >> 1, j0 = (col >> 4) << 3;
     // The amax only needs the largest |y|. The value already in *amax (the caller's
     // start, raised by tiles done so far) is a lower bound of the final one, and
-    // |y| <= max(|gate|, 0.28125) |up| (1 + 2^-8) bounds an element (|silu| <= |x| for
-    // x > 0 and <= 0.2785 for x < 0; one bf16 rounding of the product): elements
-    // whose bound is below the running maximum cannot raise it and skip the silu
-    // lookup. ymax is the running maximum as an fp32 value of a bf16.
+    // |y| <= max(gate, 0.28125) |up| (1 + 2^-8) bounds an element, gate signed
+    // (silu_bf16(x) <= x for x > 0, and |silu_bf16(x)| <= 0.2793 for x <= 0; one bf16
+    // rounding of the product): elements whose bound is below the running maximum
+    // cannot raise it and skip the silu lookup. With |gate| in place of the signed
+    // gate the bound is loose without limit for negative gates, which then all become
+    // candidates. ymax is the running maximum as an fp32 value of a bf16.
     float ymax = 0.0f;
     // Candidates are queued per wave in LDS (past the pipeline stages) as
     // gate | up << 16 and resolved together - their silu lookups in one batch - when
@@ -760,7 +762,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
     if (EPI == 2 && a.ep.amax)
       ymax = __uint_as_float(__hip_atomic_load((const uint32_t*)a.ep.amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     // Kind 2 first screens each 64-row half in registers, on the fp32 values before
-    // their bf16 rounding: for a gate g and up u of one channel, with G = max(|g|,
+    // their bf16 rounding: for a gate g and up u of one channel, with G = max(g,
     // 0.28125), s = G |u| + G 2^-130 (one multiply, one fused multiply-add) satisfies
     // |silu_bf16(RN(g)) RN(u)| <= (1 + 2^-6) s for ymax >= 2^-100: (1 + 2^-8) per bf16
     // rounding, the fp32 roundings, and the subnormal-u term covered by G 2^-130. A half
@@ -788,7 +790,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
         for (int e = 0; e < 4; ++e) {
           const uint32_t g16 = (gpk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
           const uint32_t u16 = (upk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          const float bnd = fmaxf(fabsf(bf16_bits_to_float(g16)), 0.28125f) * fabsf(bf16_bits_to_float(u16));
+          const float bnd = fmaxf(bf16_bits_to_float(g16), 0.28125f) * fabsf(bf16_bits_to_float(u16));
           if (ok && bnd > bbest) {
             bbest = bnd;
             best = g16 | (u16 << 16);
@@ -829,7 +831,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
         for (int e = 0; e < 4; ++e) {
           const uint32_t g16 = ((e >> 1) ? gpk[1] : gpk[0]) >> (16 * (e & 1)) & 0xFFFFu;
           const uint32_t u16 = ((e >> 1) ? upk[1] : upk[0]) >> (16 * (e & 1)) & 0xFFFFu;
-          const float gb = fmaxf(fabsf(bf16_bits_to_float(g16)), 0.28125f);
+          const float gb = fmaxf(bf16_bits_to_float(g16), 0.28125f);
           const float ub = fabsf(bf16_bits_to_float(u16));
           const bool cand = ok && gb * ub * (1.0f + 0x1p-7f) + 0x1p-140f >= ymax;  // margin covers fp32 rounding
           const uint64_t mask = __ballot(cand);
@@ -891,7 +893,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int64_t m0, int64_t 
             for (int pq = 0; pq < 4; pq += 2)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float G = fmaxf(fabsf(f[pq][e]), 0.28125f);
+                const float G = fmaxf(f[pq][e], 0.28125f);
                 smax_ii = fmaxf(smax_ii, __builtin_fmaf(G, 0x1p-130f, G * fabsf(f[pq + 1][e])));
               }
           }

@@ -30,10 +30,10 @@
 //    workspace's 64 slots by atomic max.
 //  - The kernel boundary is the grid-wide synchronisation the global scale needs.
 //  - The quantize launch runs one persistent 12-wave workgroup per CU with the bf16
-//    silu table in LDS. Its waves work through groups of 4 units: a fixed one each,
-//    then groups taken from 32 interleaved run-time counters (takes issued one group
-//    ahead), in reverse address order, so that the rows the absmax launch read
-//    last, still in the memory-side cache, come first and the whole grid moves
+//    silu table in LDS. Its waves work through pieces (groups of 4 units, or half
+//    groups near the end): a fixed one each, then pieces taken from 32 interleaved
+//    run-time counters (takes issued one piece ahead), in reverse address order, so
+//    that the rows the absmax launch read last come first and the whole grid moves
 //    through memory together. It reduces the slots to amax, derives g, recomputes y,
 //    and stores QDATA rows (32 lanes store one 256-byte row segment) and each scale
 //    byte at its place in its tile. Its last workgroup clears the counters and the
@@ -710,12 +710,13 @@ __device__ __forceinline__ void block_codes(const QuantCtx& c, const uint32_t (&
   if (cok) *sdst = (uint8_t)S;
 }
 
-// Persistent grid of G kQuantWaves-wave workgroups, W waves in all. Groups of units are
-// numbered from the end of the tensor. Wave v of workgroup b is wave w = v G + b (so
-// that consecutive groups go to different CUs); it starts with group w, then takes
-// groups from counter j = (w / 8) % kProdQueueCounters of the launch's set, the t-th
-// take of counter j being group W + t * kProdQueueCounters + j. Each take is issued one
-// group ahead of its use. GIVEN: the tensor amax comes from the caller (a device
+// Persistent grid of G kQuantWaves-wave workgroups, W waves in all. Pieces of work
+// (groups of units, and half groups at the end) are numbered from the end of the
+// tensor. Wave v of workgroup b is wave w = v G + b (so that consecutive pieces go to
+// different CUs); it starts with piece w, then takes pieces from counter
+// j = (w / 8) % kProdQueueCounters of the launch's set, the t-th take of counter j
+// being piece W + t * kProdQueueCounters + j. Each take is issued one piece ahead of
+// its use. GIVEN: the tensor amax comes from the caller (a device
 // float); otherwise it is the maximum of the workspace's slots, which the last
 // workgroup clears together with the counters.
 template <int MODE, bool GIVEN>

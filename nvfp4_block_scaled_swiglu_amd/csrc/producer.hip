@@ -714,11 +714,11 @@ __device__ __forceinline__ void block_codes(const QuantCtx& c, const uint32_t (&
 // (groups of units, and half groups at the end) are numbered from the end of the
 // tensor. Wave v of workgroup b is wave w = v G + b (so that consecutive pieces go to
 // different CUs); it starts with piece w, then takes pieces from counter
-// j = (w / 8) % kProdQueueCounters of the launch's set, the t-th take of counter j
-// being piece W + t * kProdQueueCounters + j. Each take is issued one piece ahead of
-// its use. GIVEN: the tensor amax comes from the caller (a device
-// float); otherwise it is the maximum of the workspace's slots, which the last
-// workgroup clears together with the counters.
+// j = (w / 8) % nq of the launch's set, the t-th take of counter j being piece
+// W + t nq + j, where nq is kProdQueueCounters, or fewer on a grid too small to give each
+// counter a wave. Each take is issued one piece ahead of its use. GIVEN: the tensor amax
+// comes from the caller (a device float); otherwise it is the maximum of the workspace's
+// slots, which the last workgroup clears together with the counters.
 template <int MODE, bool GIVEN>
 __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs a) {
   constexpr bool SWIGLU = MODE == kSwiglu, MOD = MODE == kModulate;
@@ -739,7 +739,10 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
   // Counter j serves the waves of 8 consecutive workgroups, which sit on the 8 different
   // XCDs: counters serving a single XCD ran out at that XCD's pace, and the XCDs' clocks
   // differ.
-  const int j = (wg >> 3) % kProdQueueCounters;
+  // (a grid of fewer than 8 * kProdQueueCounters waves uses as many counters as it has
+  // groups of 8 waves, so that every counter in use serves at least one wave)
+  const int nq = kProdQueueCounters < (nwaves + 7) / 8 ? kProdQueueCounters : (nwaves + 7) / 8;
+  const int j = (wg >> 3) % nq;
   uint32_t* ctr = a.queue + j * kSlotStride;
 
   // A take hands out a group of kGroupUnits units: rows r, r + 32, r + 64 and r + 96
@@ -833,7 +836,7 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
     int np = p, ngrp = grp, nh = h + 1, nhend = hend;
     fresh = nh == hend;
     if (fresh) {
-      np = nwaves + (int)__builtin_amdgcn_readfirstlane(tr) * kProdQueueCounters + j;
+      np = nwaves + (int)__builtin_amdgcn_readfirstlane(tr) * nq + j;
       ngrp = piece_group(np);
       nh = piece_half(np);
       nhend = piece_end(np);

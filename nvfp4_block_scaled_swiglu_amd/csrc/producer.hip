@@ -659,11 +659,11 @@ __device__ __forceinline__ void block_values(const ProducerArgs& a, const u32x4_
   }
 }
 
-// The scale byte and the 16 codes of one block (values yb, largest magnitude mx), stored
-// at qdst / sdst. `store_q`: the row is below m_pad; `cok`: the block is inside the
-// columns.
-__device__ __forceinline__ void block_codes(const QuantCtx& c, const uint32_t (&yb)[8], uint32_t mx, bool store_q,
-                                            bool cok, uint8_t* qdst, uint8_t* sdst) {
+// The scale byte and the 16 codes of one block (values yb, largest magnitude mx): the
+// codes are stored at qdst, the scale byte is returned. `store_q`: the row is below
+// m_pad; `cok`: the block is inside the columns.
+__device__ __forceinline__ uint32_t block_codes(const QuantCtx& c, const uint32_t (&yb)[8], uint32_t mx,
+                                                bool store_q, bool cok, uint8_t* qdst) {
   const float g = c.g;
   const uint32_t S = (mx == 0) ? 0u : block_scale_byte(bf16_bits_to_float(mx), c.bscale, c.inv_f, c.g6);
 
@@ -702,12 +702,32 @@ __device__ __forceinline__ void block_codes(const QuantCtx& c, const uint32_t (&
   }
   if (store_q && cok) {
     // non-temporal: QDATA is written once and read by the next stage (measured: about 2 %
-    // faster than plain stores); the scale bytes stay plain stores, which L2 merges into
-    // whole lines (non-temporal byte stores are far slower)
+    // faster than plain stores)
     const u32x2_t v = {clo0, clo1};
     __builtin_nontemporal_store(v, (u32x2_t*)qdst);
   }
-  if (cok) *sdst = (uint8_t)S;
+  return S;
+}
+
+// The scale bytes of a half group. Lane (r4, blk) holds, for one step, the bytes of the
+// half's two units (sa: unit 2h, sb: unit 2h + 1) for its row and block column. In a
+// 128 x 4 tile those bytes, for the tile's 4 block columns, are 8 consecutive bytes of
+// the row's 16: unit 2h's 4 columns, then unit 2h + 1's. The 4 lanes of a tile
+// (blk = 4t .. 4t + 3, one DPP quad) gather them, and the first writes them with one
+// 8-byte store (plain: the L2 merges the group's pieces into whole lines;
+// non-temporal stores of scale bytes were far slower). `cok` is the same for the 4
+// lanes (k is a multiple of 64). All lanes of the wave must be active.
+__device__ __forceinline__ void store_half_scales(uint32_t sa, uint32_t sb, int blk, bool cok, uint8_t* dst) {
+  const uint32_t x = sa | (sb << 8);                                              // a_c, b_c
+  const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // lane c ^ 1
+  const uint32_t pr = (blk & 1) ? (y | (x << 16)) : (x | (y << 16));             // a_e, b_e, a_o, b_o
+  const uint32_t z = (uint32_t)__builtin_amdgcn_mov_dpp((int)pr, 0x4E, 0xF, 0xF, false); // lane c ^ 2
+  if ((blk & 3) == 0 && cok) {
+    u32x2_t v;
+    v[0] = __builtin_amdgcn_perm(z, pr, 0x06040200u);  // a_0 a_1 a_2 a_3
+    v[1] = __builtin_amdgcn_perm(z, pr, 0x07050301u);  // b_0 b_1 b_2 b_3
+    *(u32x2_t*)dst = v;
+  }
 }
 
 // Persistent grid of G kQuantWaves-wave workgroups, W waves in all. Pieces of work
@@ -798,7 +818,9 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
   if (blockIdx.x == 0 && tid == 0) *a.gout = c.g;
 
   const int64_t qrow = a.k / 2;
-  auto process = [&](int uu, u32x4_t (&xv)[kSteps][2], u32x4_t (&yv)[kSteps][2], const u32x4_t (&zv)[2][2]) {
+  // quantizes unit uu; returns each step's scale byte in sc
+  auto process = [&](int uu, u32x4_t (&xv)[kSteps][2], u32x4_t (&yv)[kSteps][2], const u32x4_t (&zv)[2][2],
+                     uint32_t (&sc)[kSteps]) {
     arrange_unit<MODE>(xv, yv);
     const int rt = uu / a.items_k, kt = uu - rt * a.items_k;
     const int64_t row0 = (int64_t)rt * kUnitRows;
@@ -806,17 +828,25 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
     const bool cok = (int64_t)kt * kUnitCols + L.blk * 16 < a.k;
     const bool store_q = row0 < a.m_pad;  // units are 4-row aligned, m_pad 16-row aligned
     uint8_t* bq = a.qdata + row0 * qrow + kt * (kUnitCols / 2) + L.r4 * qrow + L.blk * 8;
-    // scale byte of (row, block column bc) in its 128 x 4 tile; a unit stays inside one
-    // 32-row group of one tile
-    const int64_t bc = (int64_t)kt * kLanesPerRow + L.blk;
-    uint8_t* bs = a.scales + ((row0 >> 7) * (a.cpad / 4) + (bc >> 2)) * 512 + (row0 & 31) * 16 +
-                  ((row0 >> 5) & 3) * 4 + L.r4 * 16 + (bc & 3);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       uint32_t yb[8], mx;
       block_values<MODE>(a, xv[s], yv[s], zv, tab, row0 + 2 * s + L.r4, yb, mx);
-      block_codes(c, yb, mx, store_q, cok, bq + s * 2 * qrow, bs + s * 32);
+      sc[s] = block_codes(c, yb, mx, store_q, cok, bq + s * 2 * qrow);
     }
+  };
+  // writes the scale bytes of the half group whose first unit is uu (sa) and second sb
+  auto store_scales = [&](int uu, const uint32_t (&sa)[kSteps], const uint32_t (&sb)[kSteps]) {
+    const int rt = uu / a.items_k, kt = uu - rt * a.items_k;
+    const int64_t row0 = (int64_t)rt * kUnitRows;
+    const bool cok = (int64_t)kt * kUnitCols + L.blk * 16 < a.k;
+    // the lane's row in its 128 x 4 tile (block column bc): row group (row0 & 31) + r4,
+    // 4-byte column group (row0 >> 5) & 3, which is 2h for the half's first unit
+    const int64_t bc = (int64_t)kt * kLanesPerRow + L.blk;
+    uint8_t* bs = a.scales + ((row0 >> 7) * (a.cpad / 4) + (bc >> 2)) * 512 + (row0 & 31) * 16 +
+                  ((row0 >> 5) & 3) * 4 + L.r4 * 16;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) store_half_scales(sa[s], sb[s], L.blk, cok, bs + s * 32);
   };
   // Double-buffered: the next unit's loads are issued before the current unit is
   // quantized, so they are in flight during its arithmetic and stores.
@@ -844,14 +874,17 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
     // nothing of the unit below may move above the next unit's loads (the scheduler
     // would otherwise start its lane swaps there and wait for those loads too)
     __builtin_amdgcn_sched_barrier(0);
-    process(group_unit(grp, 2 * h), gv, uv, mv);
+    const int u0 = group_unit(grp, 2 * h);
+    uint32_t sa[kSteps], sb[kSteps];
+    process(u0, gv, uv, mv, sa);
     // (after the last piece, a load of unit 0 that is never used)
     const bool more = np < npieces;
     const int n2 = more ? group_unit(ngrp, 2 * nh) : 0;
     load_unit<MODE>(a, L, n2, gv, uv);
     if (MOD) load_modulation(a, L, n2, mv);
     __builtin_amdgcn_sched_barrier(0);
-    process(n1, gw, uw, mw);
+    process(n1, gw, uw, mw, sb);
+    store_scales(u0, sa, sb);
     p = np;
     grp = ngrp;
     h = nh;

@@ -35,9 +35,10 @@
 //    run-time counters (takes issued one piece ahead), in reverse address order, so
 //    that the rows the absmax launch read last come first and the whole grid moves
 //    through memory together. It reduces the slots to amax, derives g, recomputes y,
-//    and stores QDATA rows (32 lanes store one 256-byte row segment) and each scale
-//    byte at its place in its tile. Its last workgroup clears the counters and the
-//    slots for the next call.
+//    and stores QDATA rows (32 lanes store one 256-byte row segment) and, per half
+//    group, each row's 8 scale bytes of each tile (gathered from the tile's 4 lanes)
+//    with one store. Its last workgroup clears the counters and the slots for the
+//    next call.
 // With GIVEN (amax from the caller) only the quantize launch runs: every input byte
 // is read once.
 //

@@ -47,7 +47,9 @@
  * dequantize-then-matmul and one-hot / all-ones reductions. O8: the tile
  * structure (each 128-row x 4-column tile is one contiguous 512-byte run, tiles
  * row-tile-major) and bijectivity are pinned; the order inside a tile is a
- * reading the pages do not fix - parity unpinned for that order.
+ * reading (the pages name the tiled layout but do not spell out the order), and
+ * the offsets here are pinned against an independent statement of that reading
+ * as reshapes and one transpose of an index grid.
  *
  * All floating-point decisions are taken exactly: every product compared below
  * has at most 31 significant bits and is exact in double.

@@ -35,10 +35,10 @@
 //    run-time counters (takes issued one piece ahead), in reverse address order, so
 //    that the rows the absmax launch read last come first and the whole grid moves
 //    through memory together. It reduces the slots to amax, derives g, recomputes y,
-//    and stores QDATA rows (32 lanes store one 256-byte row segment) and, per half
-//    group, each row's 8 scale bytes of each tile (gathered from the tile's 4 lanes)
-//    with one store. Its last workgroup clears the counters and the slots for the
-//    next call.
+//    and stores QDATA rows (32 lanes store one 256-byte row segment) and, per group,
+//    each row's 16 scale bytes of each tile (gathered from the tile's 4 lanes) with
+//    one store (8 bytes per half piece). Its last workgroup clears the counters and
+//    the slots for the next call.
 // With GIVEN (amax from the caller) only the quantize launch runs: every input byte
 // is read once.
 //
@@ -731,6 +731,28 @@ __device__ __forceinline__ void store_half_scales(uint32_t sa, uint32_t sb, int 
   }
 }
 
+// The scale bytes of a whole group: lane (r4, blk) holds in x, for one step, the bytes
+// of the group's units 0 .. 3 (byte q) for its row and block column. In a 128 x 4 tile
+// they are the row's 16 bytes (unit q's 4 columns at 4q). The 4 lanes of a tile
+// transpose them as a 4 x 4 byte matrix (two DPP quad moves each way), and the first
+// writes them with one 16-byte store. All lanes of the wave must be active.
+__device__ __forceinline__ void store_group_scales(uint32_t x, int blk, bool cok, uint8_t* dst) {
+  const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // lane c ^ 1
+  const uint32_t lo = (blk & 1) ? y : x, hi = (blk & 1) ? x : y;                 // even, odd column
+  const uint32_t pr = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // units 0, 1 of the lane pair
+  const uint32_t rr = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // units 2, 3
+  const uint32_t p2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)pr, 0x4E, 0xF, 0xF, false); // lane c ^ 2
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)rr, 0x4E, 0xF, 0xF, false);
+  if ((blk & 3) == 0 && cok) {
+    u32x4_t v;
+    v[0] = __builtin_amdgcn_perm(p2, pr, 0x05040100u);  // unit 0, columns 0 .. 3
+    v[1] = __builtin_amdgcn_perm(p2, pr, 0x07060302u);  // unit 1
+    v[2] = __builtin_amdgcn_perm(r2, rr, 0x05040100u);  // unit 2
+    v[3] = __builtin_amdgcn_perm(r2, rr, 0x07060302u);  // unit 3
+    *(u32x4_t*)dst = v;
+  }
+}
+
 // Persistent grid of G kQuantWaves-wave workgroups, W waves in all. Pieces of work
 // (groups of units, and half groups at the end) are numbered from the end of the
 // tensor. Wave v of workgroup b is wave w = v G + b (so that consecutive pieces go to
@@ -836,8 +858,10 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
       sc[s] = block_codes(c, yb, mx, store_q, cok, bq + s * 2 * qrow);
     }
   };
-  // writes the scale bytes of the half group whose first unit is uu (sa) and second sb
-  auto store_scales = [&](int uu, const uint32_t (&sa)[kSteps], const uint32_t (&sb)[kSteps]) {
+  // Writes the scale bytes of the half group whose first unit is uu (sa) and second sb:
+  // a half piece's at once, a whole group's first half kept in sx until its second.
+  uint32_t sx[kSteps] = {0u, 0u};
+  auto store_scales = [&](int uu, bool whole, int hh, const uint32_t (&sa)[kSteps], const uint32_t (&sb)[kSteps]) {
     const int rt = uu / a.items_k, kt = uu - rt * a.items_k;
     const int64_t row0 = (int64_t)rt * kUnitRows;
     const bool cok = (int64_t)kt * kUnitCols + L.blk * 16 < a.k;
@@ -846,8 +870,17 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
     const int64_t bc = (int64_t)kt * kLanesPerRow + L.blk;
     uint8_t* bs = a.scales + ((row0 >> 7) * (a.cpad / 4) + (bc >> 2)) * 512 + (row0 & 31) * 16 +
                   ((row0 >> 5) & 3) * 4 + L.r4 * 16;
+    if (!whole) {
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) store_half_scales(sa[s], sb[s], L.blk, cok, bs + s * 32);
+      for (int s = 0; s < kSteps; ++s) store_half_scales(sa[s], sb[s], L.blk, cok, bs + s * 32);
+    } else if (hh == 0) {
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) sx[s] = sa[s] | (sb[s] << 8);
+    } else {
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s)
+        store_group_scales(sx[s] | (sa[s] << 16) | (sb[s] << 24), L.blk, cok, bs - 8 + s * 32);
+    }
   };
   // Double-buffered: the next unit's loads are issued before the current unit is
   // quantized, so they are in flight during its arithmetic and stores.
@@ -885,7 +918,7 @@ __global__ void __launch_bounds__(kQuantWaves * 64) producer_kernel(ProducerArgs
     if (MOD) load_modulation(a, L, n2, mv);
     __builtin_amdgcn_sched_barrier(0);
     process(n1, gw, uw, mw, sb);
-    store_scales(u0, sa, sb);
+    store_scales(u0, p < nfull, h, sa, sb);
     p = np;
     grp = ngrp;
     h = nh;

@@ -89,8 +89,8 @@ def lib() -> ctypes.CDLL:
     with _lock:
         if _lib is None:
             if not os.path.exists(LIB_PATH):
-                raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
-                                  "g.build()'` or `python nvfp4_block_scaled_swiglu_amd/build.py`")
+                raise ImportError(f"{LIB_PATH} is missing: build it with "
+                                  "`python nvfp4_block_scaled_swiglu_amd/build.py`")
             l = ctypes.CDLL(LIB_PATH)
             for name, (res, args) in SIGNATURES.items():
                 fn = getattr(l, name)
